@@ -1,0 +1,326 @@
+// C ABI of libgsi (declared in include/gsi.h): argument validation, handles, and enqueueing of
+// the HIP kernels. Every argument check runs before the first HIP call, so an invalid call
+// enqueues nothing and never touches the device.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "gsi_internal.h"
+
+using namespace gsi;
+
+namespace {
+
+bool dtype_ok(int dtype) { return dtype == GSI_F32 || dtype == GSI_F16 || dtype == GSI_BF16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Shape rules shared by every entry point (see include/gsi.h).
+int check_shape(int dtype, int d_out, int d, int k) {
+  if (!dtype_ok(dtype)) return GSI_ERR_DTYPE;
+  if (d_out < 1 || d < 8 || d % 8 != 0 || d > 65536) return GSI_ERR_SHAPE;
+  if (k < 8 || k > 512 || k > d || !pow2(k)) return GSI_ERR_SHAPE;
+  // rows of M longer than one wave of 16-byte chunks are combined through a 256-entry buffer
+  const int cprk = (int)(k * dtype_size(dtype) / 16);
+  if (cprk > 64) {
+    const int segs = cprk / 64;
+    const int rpb_max = (d_out + (kMaxK / 4) - 1) / (kMaxK / 4);  // at least 128 blocks
+    if ((long long)rpb_max * segs > 256) return GSI_ERR_SHAPE;
+  }
+  return GSI_OK;
+}
+
+int check_eps(float eps) {
+  if (std::isnan(eps) || eps < 0.f) return GSI_ERR_EPS;
+  return GSI_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? GSI_OK : GSI_ERR_HIP; }
+
+size_t aux_bytes(int dtype, int d, int k) {
+  return align256((size_t)k * d * dtype_size(dtype)) + align256((size_t)k * k * 4);
+}
+
+size_t ws_bytes_for(int k, int T) { return align256(decode_ws_bytes()) + batched_ws_bytes(k, T < 1 ? 1 : T); }
+
+WsHeader* ws_header(void* ws) { return reinterpret_cast<WsHeader*>(ws); }
+
+void fill_decode_boxes(DecodeParams& p, void* ws) {
+  char* c = (char*)ws;
+  p.hdr = (WsHeader*)c;
+  c += sizeof(WsHeader);
+  p.box_g = (u64*)c;
+  c += (size_t)kReplicas * kMaxK * 8;
+  p.box_p = (u64*)c;
+  c += (size_t)kReplicas * kMaxBlocks * 8;
+  p.box_f = (u64*)c;
+}
+
+BatchedWs batched_part(void* ws, int k, int T) {
+  return batched_ws_carve((char*)ws + align256(decode_ws_bytes()), k, T);
+}
+
+// Batched path for one site over T tokens whose rows sit at X (+ row stride x_ld) and Y.
+int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps, void* Y,
+                long long y_ld, uint8_t* gate, int gate_ld, float* rho, void* ws, hipStream_t s) {
+  BatchedWs w = batched_part(ws, L.k, T);
+  int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
+  if (rc != GSI_OK) return rc;
+  // fast tokens: y = M g     [GSI §2.2]
+  rc = launch_gemm_nt(GSI_F32, dtype, dtype, w.G, L.k, w.fast_idx, L.M, L.k, Y, y_ld, w.fast_idx, T, L.d_out, L.k,
+                      w.counts + 0, 0, s);
+  if (rc != GSI_OK) return rc;
+  // slow tokens: y = W x     [GSI §2.2]
+  return launch_gemm_nt(dtype, dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, Y, y_ld, w.slow_idx, T, L.d_out, L.d,
+                        w.counts + 1, 0, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gsi_status_string(int code) {
+  switch (code) {
+    case GSI_OK: return "ok";
+    case GSI_ERR_NULL: return "null pointer argument";
+    case GSI_ERR_SHAPE: return "dimension out of range (d, k multiples of 8, k a power of two <= min(d, 512))";
+    case GSI_ERR_DTYPE: return "unknown or mismatched dtype";
+    case GSI_ERR_EPS: return "eps must be >= 0 and not NaN";
+    case GSI_ERR_WORKSPACE: return "workspace missing or too small";
+    case GSI_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case GSI_ERR_DEVICE: return "current device is not gfx950 or cannot co-schedule the persistent grid";
+    case GSI_ERR_HIP: return "HIP runtime error";
+    case GSI_ERR_TIMEOUT: return "an in-kernel wait exceeded its bound";
+  }
+  return "unknown status";
+}
+
+int gsi_device_check(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GSI_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GSI_ERR_DEVICE;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? GSI_OK : GSI_ERR_DEVICE;
+}
+
+size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k) {
+  if (check_shape(dtype, d_out, d, k) != GSI_OK) return 0;
+  return aux_bytes(dtype, d, k);
+}
+
+int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const void* W, const void* V, void* M,
+                     void* aux, size_t aux_nbytes, void* stream) {
+  if (!out) return GSI_ERR_NULL;
+  *out = nullptr;
+  int rc = check_shape(dtype, d_out, d, k);
+  if (rc != GSI_OK) return rc;
+  if (!W || !V || !M || !aux) return GSI_ERR_NULL;
+  if (!aligned16(W) || !aligned16(V) || !aligned16(M) || !aligned16(aux)) return GSI_ERR_ALIGN;
+  if (aux_nbytes < aux_bytes(dtype, d, k)) return GSI_ERR_WORKSPACE;
+  if ((rc = gsi_device_check()) != GSI_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  void* Vt = aux;
+  float* Dl = (float*)((char*)aux + align256((size_t)k * d * dtype_size(dtype)));
+  // V^T (k x d), then M = W V = W (V^T)^T, then V^T V - I   [GSI §2.1]
+  if ((rc = launch_transpose(dtype, V, Vt, d, k, s)) != GSI_OK) return rc;
+  if ((rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s)) != GSI_OK)
+    return rc;
+  if ((rc = launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s)) != GSI_OK)
+    return rc;
+  gsi_layer* L = new (std::nothrow) gsi_layer;
+  if (!L) return GSI_ERR_NULL;
+  L->dtype = dtype;
+  L->d_out = d_out;
+  L->d = d;
+  L->k = k;
+  L->desc.Vt = Vt;
+  L->desc.M = M;
+  L->desc.Dl = Dl;
+  L->desc.W = W;
+  L->desc.d = d;
+  L->desc.d_out = d_out;
+  L->desc.k = k;
+  L->desc.pad = 0;
+  L->desc.x_off = 0;
+  L->desc.y_off = 0;
+  *out = L;
+  return GSI_OK;
+}
+
+int gsi_layer_destroy(gsi_layer* L) {
+  delete L;
+  return GSI_OK;
+}
+
+size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max) {
+  if (check_shape(dtype, d_out, d, k) != GSI_OK || T_max < 0) return 0;
+  return ws_bytes_for(k, T_max);
+}
+
+int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, uint8_t* gate, float* rho, void* ws,
+                size_t ws_nbytes, void* stream) {
+  if (!L) return GSI_ERR_NULL;
+  if (T < 0) return GSI_ERR_SHAPE;
+  int rc = check_eps(eps);
+  if (rc != GSI_OK) return rc;
+  if (T == 0) return GSI_OK;
+  if (!x || !y || !gate || !ws) return GSI_ERR_NULL;
+  if (!aligned16(x) || !aligned16(ws)) return GSI_ERR_ALIGN;
+  if (ws_nbytes < ws_bytes_for(L->k, T)) return GSI_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (T < 16) {
+    DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.sites = nullptr;
+    p.one = L->desc;
+    p.n_sites = 1;
+    p.n_tokens = T;
+    p.X = x;
+    p.x_ld = L->d;
+    p.Y = y;
+    p.y_ld = L->d_out;
+    p.gates = gate;
+    p.rho = rho;
+    p.gate_ld = 1;
+    p.site0 = 0;
+    p.eps = eps;
+    p.k_max = L->k;
+    p.d_max = L->d;
+    fill_decode_boxes(p, ws);
+    return launch_decode(L->dtype, p, s);
+  }
+  return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, s);
+}
+
+int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
+  if (!out) return GSI_ERR_NULL;
+  *out = nullptr;
+  if (!sites) return GSI_ERR_NULL;
+  if (n_sites < 1) return GSI_ERR_SHAPE;
+  for (int i = 0; i < n_sites; ++i) {
+    if (!sites[i]) return GSI_ERR_NULL;
+    if (sites[i]->dtype != sites[0]->dtype) return GSI_ERR_DTYPE;
+  }
+  LayerDesc* table = (LayerDesc*)std::malloc(sizeof(LayerDesc) * n_sites);
+  gsi_layer** layers = (gsi_layer**)std::malloc(sizeof(gsi_layer*) * n_sites);
+  gsi_stack* S = new (std::nothrow) gsi_stack;
+  if (!table || !layers || !S) {
+    std::free(table);
+    std::free(layers);
+    delete S;
+    return GSI_ERR_NULL;
+  }
+  long long xo = 0, yo = 0;
+  int kmax = 0, dmax = 0, domax = 0;
+  for (int i = 0; i < n_sites; ++i) {
+    table[i] = sites[i]->desc;
+    table[i].x_off = xo;
+    table[i].y_off = yo;
+    xo += sites[i]->d;
+    yo += sites[i]->d_out;
+    kmax = sites[i]->k > kmax ? sites[i]->k : kmax;
+    dmax = sites[i]->d > dmax ? sites[i]->d : dmax;
+    domax = sites[i]->d_out > domax ? sites[i]->d_out : domax;
+    layers[i] = sites[i];
+  }
+  S->dtype = sites[0]->dtype;
+  S->n_sites = n_sites;
+  S->k_max = kmax;
+  S->d_max = dmax;
+  S->d_out_max = domax;
+  S->x_ld = xo;
+  S->y_ld = yo;
+  S->layers = layers;
+  S->h_table = table;
+  S->d_table = nullptr;
+  hipError_t e = hipMalloc((void**)&S->d_table, sizeof(LayerDesc) * n_sites);
+  if (e == hipSuccess) e = hipMemcpy(S->d_table, table, sizeof(LayerDesc) * n_sites, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (S->d_table) (void)hipFree(S->d_table);
+    std::free(table);
+    std::free(layers);
+    delete S;
+    return GSI_ERR_HIP;
+  }
+  *out = S;
+  return GSI_OK;
+}
+
+int gsi_stack_destroy(gsi_stack* S) {
+  if (!S) return GSI_OK;
+  int rc = GSI_OK;
+  if (S->d_table && hipFree(S->d_table) != hipSuccess) rc = GSI_ERR_HIP;
+  std::free(S->layers);
+  std::free(S->h_table);
+  delete S;
+  return rc;
+}
+
+size_t gsi_stack_workspace_bytes(const gsi_stack* S, int T_step) {
+  if (!S || T_step < 1) return 0;
+  return ws_bytes_for(S->k_max, T_step);
+}
+
+int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
+                     float* rho, void* ws, size_t ws_nbytes, void* stream) {
+  if (!S) return GSI_ERR_NULL;
+  if (n_steps < 0 || T_step < 1) return GSI_ERR_SHAPE;
+  int rc = check_eps(eps);
+  if (rc != GSI_OK) return rc;
+  if (n_steps == 0) return GSI_OK;
+  if (!X || !Y || !gates || !ws) return GSI_ERR_NULL;
+  if (!aligned16(X) || !aligned16(ws)) return GSI_ERR_ALIGN;
+  if (ws_nbytes < ws_bytes_for(S->k_max, T_step)) return GSI_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (T_step == 1) {
+    DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.sites = S->d_table;
+    p.n_sites = S->n_sites;
+    p.n_tokens = n_steps;
+    p.X = X;
+    p.x_ld = S->x_ld;
+    p.Y = Y;
+    p.y_ld = S->y_ld;
+    p.gates = gates;
+    p.rho = rho;
+    p.gate_ld = S->n_sites;
+    p.site0 = 0;
+    p.eps = eps;
+    p.k_max = S->k_max;
+    p.d_max = S->d_max;
+    fill_decode_boxes(p, ws);
+    return launch_decode(S->dtype, p, s);
+  }
+  const size_t es = dtype_size(S->dtype);
+  for (int st = 0; st < n_steps; ++st) {
+    const long long row0 = (long long)st * T_step;
+    for (int i = 0; i < S->n_sites; ++i) {
+      const LayerDesc& L = S->h_table[i];
+      const char* xs = (const char*)X + (size_t)(row0 * S->x_ld + L.x_off) * es;
+      char* ys = (char*)Y + (size_t)(row0 * S->y_ld + L.y_off) * es;
+      uint8_t* gs = gates + row0 * S->n_sites + i;
+      float* rs = rho ? rho + row0 * S->n_sites + i : nullptr;
+      rc = run_batched(S->dtype, L, xs, S->x_ld, T_step, eps, ys, S->y_ld, gs, S->n_sites, rs, ws, s);
+      if (rc != GSI_OK) return rc;
+    }
+  }
+  return GSI_OK;
+}
+
+int gsi_workspace_status(void* ws, size_t ws_nbytes, int* host_status, void* stream) {
+  if (!ws || !host_status) return GSI_ERR_NULL;
+  if (ws_nbytes < sizeof(WsHeader)) return GSI_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int rc = hip_rc(hipStreamSynchronize(s));
+  if (rc != GSI_OK) return rc;
+  int v = 0;
+  rc = hip_rc(hipMemcpy(&v, &ws_header(ws)->status, sizeof(int), hipMemcpyDeviceToHost));
+  if (rc != GSI_OK) return rc;
+  *host_status = v;
+  int zero = 0;
+  return hip_rc(hipMemcpy(&ws_header(ws)->status, &zero, sizeof(int), hipMemcpyHostToDevice));
+}
+
+}  // extern "C"

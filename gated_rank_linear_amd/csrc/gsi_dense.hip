@@ -1,0 +1,272 @@
+// Dense kernels of libgsi: the create-time precomputation (V^T, M = W V, V^T V - I) and the
+// batched (T >= 16) path: projection, device-side gate with fast/slow token compaction, and the
+// fast (M g) and slow (W x) products. Method: "Gated Subspace Inference for transformer
+// acceleration" technical summary (gist.science, arXiv 2605.03109), §2.1-§2.2.
+#include "gsi_internal.h"
+
+namespace gsi {
+
+template <typename T> __device__ __forceinline__ float ld_f32(const void* p, long long i) {
+  return to_f32(reinterpret_cast<const T*>(p)[i]);
+}
+template <typename T> __device__ __forceinline__ void st_from_f32(void* p, long long i, float v) {
+  reinterpret_cast<T*>(p)[i] = from_f32<T>(v);
+}
+
+// ---------------------------------------------------------------------------------------------
+// NT GEMM on the vector ALU, float32 accumulation: C[m, n] = sum_i A[ra(m), i] * B[n, i].
+// 64x64 output tile per 256-thread block, K staged through LDS in chunks of 32 (converted to
+// float32 once), 4x4 outputs per thread. Each output is one thread's fixed-order sum, so results
+// are reproducible run to run.
+// ---------------------------------------------------------------------------------------------
+constexpr int GBM = 64, GBN = 64, GBK = 32;
+
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const void* __restrict__ A, long long lda,
+                                                      const int* __restrict__ a_idx, const void* __restrict__ B,
+                                                      long long ldb, void* __restrict__ C, long long ldc,
+                                                      const int* __restrict__ c_idx, int m, int n, int kdim,
+                                                      const int* __restrict__ m_count, int sub_identity) {
+  __shared__ float As[GBK][GBM + 4];
+  __shared__ float Bs[GBK][GBN + 4];
+  const int mv = m_count ? min(m, *m_count) : m;
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  if (m0 >= mv) return;
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  // loader mapping: 64 rows x 32 k per tile = 2048 elements, 8 per thread (one row, 8 consecutive k)
+  const int lr = tid / 4, lk = (tid % 4) * 8;
+  const int am = m0 + lr;
+  const bool a_ok = am < mv;
+  const long long a_row = a_ok ? (long long)(a_idx ? a_idx[am] : am) : 0;
+  const int bn = n0 + lr;
+  const bool b_ok = bn < n;
+
+  for (int k0 = 0; k0 < kdim; k0 += GBK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kk = k0 + lk + e;
+      As[lk + e][lr] = (a_ok && kk < kdim) ? ld_f32<TA>(A, a_row * lda + kk) : 0.f;
+      Bs[lk + e][lr] = (b_ok && kk < kdim) ? ld_f32<TB>(B, (long long)bn * ldb + kk) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < GBK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mm = m0 + ty * 4 + i;
+    if (mm >= mv) continue;
+    const long long crow = c_idx ? c_idx[mm] : mm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nn = n0 + tx * 4 + j;
+      if (nn >= n) continue;
+      float v = acc[i][j];
+      if (sub_identity && mm == nn) v -= 1.0f;
+      st_from_f32<TC>(C, crow * ldc + nn, v);
+    }
+  }
+}
+
+template <typename TA, typename TB>
+static void* pick_c(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)gemm_nt_kernel<TA, TB, float>;
+    case GSI_F16: return (void*)gemm_nt_kernel<TA, TB, f16_t>;
+    case GSI_BF16: return (void*)gemm_nt_kernel<TA, TB, bf16_t>;
+  }
+  return nullptr;
+}
+template <typename TA>
+static void* pick_b(int b_type, int c_type) {
+  switch (b_type) {
+    case GSI_F32: return pick_c<TA, float>(c_type);
+    case GSI_F16: return pick_c<TA, f16_t>(c_type);
+    case GSI_BF16: return pick_c<TA, bf16_t>(c_type);
+  }
+  return nullptr;
+}
+
+int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
+                   const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n, int kdim,
+                   const int* m_count, int sub_identity, hipStream_t s) {
+  if (m <= 0 || n <= 0) return GSI_OK;
+  void* fn = nullptr;
+  switch (a_type) {
+    case GSI_F32: fn = pick_b<float>(b_type, c_type); break;
+    case GSI_F16: fn = pick_b<f16_t>(b_type, c_type); break;
+    case GSI_BF16: fn = pick_b<bf16_t>(b_type, c_type); break;
+  }
+  if (!fn) return GSI_ERR_DTYPE;
+  dim3 grid((n + GBN - 1) / GBN, (m + GBM - 1) / GBM);
+  void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+  return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dst[k, d] = transpose(src[d, k]), 32x32 tiles through LDS
+// ---------------------------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst, int d, int k) {
+  __shared__ E t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;  // src rows r (d), cols c (k)
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  for (int i = ty; i < 32; i += 8) {
+    int r = r0 + i, c = c0 + tx;
+    if (r < d && c < k) t[i][tx] = src[(long long)r * k + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    int c = c0 + i, r = r0 + tx;
+    if (r < d && c < k) dst[(long long)c * d + r] = t[tx][i];
+  }
+}
+
+int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s) {
+  dim3 grid((k + 31) / 32, (d + 31) / 32);
+  if (dtype == GSI_F32)
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, d, k);
+  else
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, d, k);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Batched gate: one block per token. nx2 = |x|^2, gg = |g|^2, q = g^T (V^T V - I) g, then
+// nr2 = nx2 - gg + q (= |x - V g|^2 exactly in real arithmetic) and the float32 comparison
+// nr2 < fl(fl(eps^2) * nx2) -> fast [GSI §2.2]. Fixed-order block reductions.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  // wave reduction (fixed butterfly order), then the 4 wave sums in index order
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x / 64;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gate_batched_kernel(const void* __restrict__ X, long long x_ld, int d, int k,
+                                                           const float* __restrict__ G, const float* __restrict__ H,
+                                                           float eps, uint8_t* __restrict__ gate, int gate_ld,
+                                                           float* __restrict__ rho, float* __restrict__ nx2_out) {
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  const T* x = reinterpret_cast<const T*>(X) + (long long)t * x_ld;
+  float sx = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float v = to_f32(x[i]);
+    sx = __builtin_fmaf(v, v, sx);
+  }
+  float sg = 0.f, sq = 0.f;
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const float gj = G[(long long)t * k + j];
+    sg = __builtin_fmaf(gj, gj, sg);
+    sq = __builtin_fmaf(gj, H[(long long)t * k + j], sq);
+  }
+  const float nx2 = block_sum_256(sx, red);
+  const float gg = block_sum_256(sg, red + 4);
+  __syncthreads();
+  const float q = block_sum_256(sq, red);
+  if (threadIdx.x == 0) {
+    const float nr2 = (nx2 - gg) + q;
+    const float thr = eps * eps;
+    const float rhs = thr * nx2;
+    const bool fast = nr2 < rhs;
+    gate[(long long)t * gate_ld] = fast ? 0 : 1;
+    if (rho) rho[(long long)t * gate_ld] = sqrtf(fmaxf(nr2, 0.f) / nx2);
+    nx2_out[t] = nx2;
+  }
+}
+
+// Token compaction in token order: fast_idx / slow_idx lists and counts[0] (fast), counts[1] (slow).
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ gate, int gate_ld, int T,
+                                                       int* __restrict__ fast_idx, int* __restrict__ slow_idx,
+                                                       int* __restrict__ counts) {
+  __shared__ int wsum[2][16];
+  __shared__ int base[2];
+  if (threadIdx.x == 0) base[0] = base[1] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x / 64;
+  for (int t0 = 0; t0 < T; t0 += 1024) {
+    const int t = t0 + threadIdx.x;
+    const bool valid = t < T;
+    const bool slow = valid && gate[(long long)t * gate_ld] != 0;
+    const bool fast = valid && !slow;
+    const u64 mf = __ballot(fast), ms = __ballot(slow);
+    const u64 below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int pf = __popcll(mf & below), ps = __popcll(ms & below);
+    if (lane == 0) { wsum[0][w] = __popcll(mf); wsum[1][w] = __popcll(ms); }
+    __syncthreads();
+    int of = base[0], os = base[1];
+    for (int i = 0; i < w; ++i) { of += wsum[0][i]; os += wsum[1][i]; }
+    if (fast) fast_idx[of + pf] = t;
+    if (slow) slow_idx[os + ps] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < 16; ++i) { base[0] += wsum[0][i]; base[1] += wsum[1][i]; }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) { counts[0] = base[0]; counts[1] = base[1]; }
+}
+
+size_t batched_ws_bytes(int k, int T) {
+  return 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4);
+}
+BatchedWs batched_ws_carve(void* base, int k, int T) {
+  char* p = (char*)base;
+  BatchedWs w;
+  w.G = (float*)p; p += align256((size_t)T * k * 4);
+  w.H = (float*)p; p += align256((size_t)T * k * 4);
+  w.nx2 = (float*)p; p += align256((size_t)T * 4);
+  w.fast_idx = (int*)p; p += align256((size_t)T * 4);
+  w.slow_idx = (int*)p; p += align256((size_t)T * 4);
+  w.counts = (int*)p;
+  return w;
+}
+
+int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
+                        const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s) {
+  // G = X V as X (V^T)^T: [T, k] float32
+  int rc = launch_gemm_nt(dtype, dtype, GSI_F32, X, x_ld, nullptr, L.Vt, L.d, w.G, L.k, nullptr, T, L.k, L.d,
+                          nullptr, 0, s);
+  if (rc != GSI_OK) return rc;
+  // H = G (V^T V - I)  (the matrix is symmetric, so its rows serve as the K-contiguous operand)
+  rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.G, L.k, nullptr, L.Dl, L.k, w.H, L.k, nullptr, T, L.k, L.k,
+                      nullptr, 0, s);
+  if (rc != GSI_OK) return rc;
+  if (dtype == GSI_F32)
+    gate_batched_kernel<float><<<T, 256, 0, s>>>(X, x_ld, L.d, L.k, w.G, w.H, eps, gate, gate_ld, rho, w.nx2);
+  else if (dtype == GSI_F16)
+    gate_batched_kernel<f16_t><<<T, 256, 0, s>>>(X, x_ld, L.d, L.k, w.G, w.H, eps, gate, gate_ld, rho, w.nx2);
+  else
+    gate_batched_kernel<bf16_t><<<T, 256, 0, s>>>(X, x_ld, L.d, L.k, w.G, w.H, eps, gate, gate_ld, rho, w.nx2);
+  if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+  compact_kernel<<<1, 1024, 0, s>>>(gate, gate_ld, T, w.fast_idx, w.slow_idx, w.counts);
+  if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+  return GSI_OK;
+}
+
+}  // namespace gsi

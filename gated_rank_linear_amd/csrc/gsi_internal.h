@@ -1,0 +1,168 @@
+// Internal declarations shared by the libgsi translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/gsi.h"
+
+namespace gsi {
+
+typedef unsigned long long u64;
+
+// ---------------------------------------------------------------------------------------------
+// Element types. Storage is raw bits; conversions are explicit so every rounding is visible.
+// ---------------------------------------------------------------------------------------------
+struct bf16_t { uint16_t b; };
+struct f16_t { uint16_t b; };
+
+__host__ __device__ __forceinline__ float to_f32(float v) { return v; }
+__host__ __device__ __forceinline__ float to_f32(bf16_t v) {
+  union { uint32_t u; float f; } c;
+  c.u = (uint32_t)v.b << 16;
+  return c.f;
+}
+__device__ __forceinline__ float to_f32(f16_t v) {
+  _Float16 h;
+  __builtin_memcpy(&h, &v.b, 2);
+  return (float)h;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+// round to nearest even; NaN stays NaN (quiet)
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
+  union { float f; uint32_t u; } c;
+  c.f = f;
+  uint32_t u = c.u;
+  bf16_t r;
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+    r.b = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.b = (uint16_t)(u >> 16);
+  }
+  return r;
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+  f16_t r;
+  __builtin_memcpy(&r.b, &h, 2);
+  return r;
+}
+
+template <typename T> struct elem_size { static constexpr int v = sizeof(T); };
+
+// 16-byte vector of elements and its conversion to floats
+template <typename T> struct vec16 {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& q, float* out) {
+  const T* e = reinterpret_cast<const T*>(&q);
+#pragma unroll
+  for (int i = 0; i < vec16<T>::N; ++i) out[i] = to_f32(e[i]);
+}
+
+inline size_t dtype_size(int dtype) { return dtype == GSI_F32 ? 4 : 2; }
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------------------------
+// Layer and stack handles
+// ---------------------------------------------------------------------------------------------
+struct LayerDesc {  // device-side description of one site (also used host-side)
+  const void* Vt;     // [k, d]
+  const void* M;      // [d_out, k]
+  const float* Dl;    // [k, k] = V^T V - I
+  const void* W;      // [d_out, d]
+  int d, d_out, k, pad;
+  long long x_off, y_off;  // column offsets into stacked X / Y rows
+};
+
+}  // namespace gsi
+
+struct gsi_layer {
+  int dtype, d_out, d, k;
+  gsi::LayerDesc desc;  // x_off = y_off = 0
+};
+
+struct gsi_stack {
+  int dtype, n_sites, k_max, d_max, d_out_max;
+  long long x_ld, y_ld;
+  gsi::LayerDesc* d_table;  // device copy
+  gsi::LayerDesc* h_table;  // host copy
+  gsi_layer** layers;       // host copy of the borrowed handles
+};
+
+namespace gsi {
+
+// Workspace header (start of every workspace)
+struct WsHeader {
+  unsigned epoch;  // exchange tag base, advanced by every persistent launch
+  int status;      // GSI_OK or GSI_ERR_TIMEOUT (sticky until read by gsi_workspace_status)
+  unsigned abort_tag;  // tag base + 1 of a launch that gave up waiting
+  unsigned pad[61];
+};
+
+// ---------------------------------------------------------------------------------------------
+// Persistent decode kernel (batch of n_tokens processed one token at a time through all sites)
+// ---------------------------------------------------------------------------------------------
+constexpr int kReplicas = 8;       // one mailbox copy per XCD
+constexpr int kMaxBlocks = 256;    // persistent blocks (one per CU)
+constexpr int kMaxK = 512;
+constexpr int kDataThreads = 256;  // 4 data waves
+constexpr int kSyncThreads = 64;   // 1 sync wave
+constexpr int kDecodeThreads = kDataThreads + kSyncThreads;
+
+struct DecodeParams {
+  const LayerDesc* sites;  // device table of n_sites descriptors, or NULL to use `one`
+  LayerDesc one;
+  int n_sites, n_tokens;
+  const void* X;
+  long long x_ld;
+  void* Y;
+  long long y_ld;
+  uint8_t* gates;  // [n_tokens, gate_ld]
+  float* rho;      // optional
+  int gate_ld, site0;  // column of site 0 in gates/rho
+  float eps;
+  int k_max, d_max;
+  WsHeader* hdr;
+  u64* box_g;  // [2][kReplicas][kMaxK]     parity by exchange index
+  u64* box_p;  // [2][kReplicas][kMaxBlocks]
+  u64* box_f;  // [2][kReplicas][kMaxBlocks]
+};
+
+size_t decode_ws_bytes();
+int launch_decode(int dtype, const DecodeParams& p, hipStream_t s);
+int decode_grid_blocks(int dtype);
+
+// ---------------------------------------------------------------------------------------------
+// Dense helpers (create time and the batched path)
+// ---------------------------------------------------------------------------------------------
+// C[m, n] = alpha-free sum_i A[a_row(m), i] * B[n, i]  (both operands K-contiguous, "NT")
+//   a_idx: optional row gather for A (device int32 list), c_idx: optional row scatter for C,
+//   m_count: optional device int32 giving the number of valid rows (else m).
+//   sub_identity: C[m][n] -= (m == n) (for V^T V - I).
+int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
+                   const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n, int kdim,
+                   const int* m_count, int sub_identity, hipStream_t s);
+// dst[k, d] = transpose(src[d, k])
+int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s);
+
+struct BatchedWs {
+  float* G;      // [T, k]  g = V^T x per token
+  float* H;      // [T, k]  (V^T V - I) g per token
+  float* nx2;    // [T]
+  int* fast_idx; // [T]
+  int* slow_idx; // [T]
+  int* counts;   // [2]
+};
+size_t batched_ws_bytes(int k, int T);
+BatchedWs batched_ws_carve(void* base, int k, int T);
+int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
+                        const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s);
+
+}  // namespace gsi

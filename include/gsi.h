@@ -1,0 +1,144 @@
+/*
+ * gsi.h - C ABI of libgsi: Gated Subspace Inference (GSI) linear layers on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method is the one described in the technical summary "Gated Subspace Inference for
+ * transformer acceleration" (gist.science, arXiv 2605.03109), cited as [GSI §n]:
+ *
+ *   For a linear layer y = W x, W in R^{d_out x d}, and an orthonormal basis V_k in R^{d x k}
+ *   of the activation subspace, the input decomposes exactly as x = V_k V_k^T x + r [GSI §2.1].
+ *   M = W V_k (d_out x k) is precomputed once and cached; g = V_k^T x. A per-token gate compares
+ *   the residual ratio rho = |r| / |x| with a threshold eps [GSI §2.2]:
+ *     rho <  eps  -> fast path, y = M g   (reads M instead of W)
+ *     rho >= eps  -> slow path, y = W x   (the exact product)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers (memory of the current HIP device) unless a
+ *    parameter says "host". The caller allocates and owns every device buffer; the library
+ *    only borrows them. W, V, M and aux must stay valid and unmodified for a layer's lifetime.
+ *  - Layouts are row-major and dense:
+ *      W    [d_out, d]   weight dtype          V   [d, k]   weight dtype
+ *      M    [d_out, k]   weight dtype          x   [T, d]   weight dtype (token-major)
+ *      y    [T, d_out]   weight dtype          gate[T] uint8, 1 = slow (residual passed through)
+ *      rho  [T] float32 (optional, may be NULL): sqrt(|r|^2 / |x|^2), NaN when x = 0.
+ *  - dtype is one of GSI_F32, GSI_F16, GSI_BF16 and applies to W, V, M, x and y alike. All
+ *    accumulation is float32. g is kept in float32.
+ *  - d and k must be multiples of 8; 1 <= k <= min(d, 512); d <= 65536; d_out >= 1.
+ *    Device pointers must be 16-byte aligned.
+ *  - The gate is evaluated in float32 as  nr2 < fl(fl(eps*eps) * nx2),  with nx2 = |x|^2 and
+ *    nr2 = |x - V g|^2 of the *stored* V (formed exactly through the identity
+ *    |x - Vg|^2 = |x|^2 - |g|^2 + g^T (V^T V - I) g with g = V^T x). Ties (rho = eps) go slow,
+ *    x = 0 goes slow with y = 0, and NaN/Inf in x go slow and propagate into y.
+ *  - `stream` is a hipStream_t passed as void*. Every call only enqueues work on it and returns;
+ *    nothing synchronises the host. Validation happens before anything is enqueued: a call that
+ *    returns an error code has enqueued nothing. Faults inside kernels surface at the caller's
+ *    next synchronisation; a wait inside a kernel that exceeds its time bound records
+ *    GSI_ERR_TIMEOUT in the workspace (see gsi_workspace_status).
+ *  - Calls on one workspace must not overlap (use one workspace per stream).
+ */
+#ifndef GSI_H
+#define GSI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gsi_dtype { GSI_F32 = 0, GSI_F16 = 1, GSI_BF16 = 2 };
+
+enum gsi_status {
+  GSI_OK = 0,
+  GSI_ERR_NULL = -1,       /* a required pointer is NULL */
+  GSI_ERR_SHAPE = -2,      /* a dimension is out of range (see conventions) */
+  GSI_ERR_DTYPE = -3,      /* unknown dtype, or mixed dtypes in one stack */
+  GSI_ERR_EPS = -4,        /* eps < 0 or NaN */
+  GSI_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */
+  GSI_ERR_ALIGN = -6,      /* a device pointer is not 16-byte aligned */
+  GSI_ERR_DEVICE = -7,     /* the current device is not gfx950, or too few co-resident blocks */
+  GSI_ERR_HIP = -8,        /* a HIP runtime call or launch failed */
+  GSI_ERR_TIMEOUT = -9     /* recorded in a workspace: an in-kernel wait exceeded its bound */
+};
+
+typedef struct gsi_layer gsi_layer;
+typedef struct gsi_stack gsi_stack;
+
+/* Static text for a status code; never NULL. */
+const char* gsi_status_string(int code);
+
+/* GSI_OK if the current HIP device is gfx950 (MI355X), GSI_ERR_DEVICE otherwise. */
+int gsi_device_check(void);
+
+/*
+ * Bytes of per-layer derived data ("aux") that gsi_layer_create fills: V^T [k, d] in the weight
+ * dtype, then V^T V - I [k, k] in float32, each 256-byte aligned. 0 for invalid arguments.
+ */
+size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k);
+
+/*
+ * Create a GSI layer [GSI §2.1]: enqueue on `stream` the precomputation of the cached low-rank
+ * weight image M = W V (written to the caller's buffer M, [d_out, k], weight dtype, float32
+ * accumulation, rounded to nearest even) and of aux (V^T and V^T V - I). Returns after enqueueing;
+ * *out receives a small host handle that borrows W, M and aux (V is not used after the
+ * precomputation has run). On error *out is left NULL.
+ */
+int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const void* W, const void* V,
+                     void* M, void* aux, size_t aux_bytes, void* stream);
+
+/* Free the host handle (device buffers remain the caller's). NULL is accepted. */
+int gsi_layer_destroy(gsi_layer* L);
+
+/* Workspace bytes gsi_forward needs for up to T_max tokens on a layer of this shape. */
+size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max);
+
+/*
+ * Run one GSI layer over T tokens [GSI §2.1-§2.2]: y[t] = M g_t if rho_t < eps else W x_t,
+ * gate[t] = 0 (fast) or 1 (slow), rho[t] if rho != NULL. T = 0 returns GSI_OK with nothing
+ * enqueued. T < 16 runs the per-token persistent path; T >= 16 the batched path (projection,
+ * device-side gate with fast/slow token compaction, then the two products), with no host
+ * synchronisation in either. The workspace must be zero-filled before its first use and is
+ * kept consistent by the library afterwards.
+ */
+int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, uint8_t* gate, float* rho,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A stack of layers ("sites") run in order, as every linear map of a transformer block
+ * (QKV, output, MLP in and out) and block after block [GSI §3]. `sites` is a HOST array of
+ * n_sites layer handles, all of one dtype; the stack borrows them. The library allocates a small
+ * device table for the stack (freed by gsi_stack_destroy).
+ */
+int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites);
+int gsi_stack_destroy(gsi_stack* S);
+
+/* Workspace bytes gsi_stack_decode needs for steps of T_step tokens. */
+size_t gsi_stack_workspace_bytes(const gsi_stack* S, int T_step);
+
+/*
+ * Decode n_steps steps of T_step tokens through the stack. Token-major stacked layouts:
+ *   X     [n_steps * T_step, sum_s d_s]      row n holds site 0's input, then site 1's, ...
+ *   Y     [n_steps * T_step, sum_s d_out_s]  same stacking for the outputs
+ *   gates [n_steps * T_step, n_sites] uint8  (1 = slow)
+ *   rho   [n_steps * T_step, n_sites] float32, optional (NULL)
+ * Sites run in order within a step and steps run in order; each site starts after the previous
+ * site's output and gate are complete. Site inputs are read from X (they are not chained from
+ * the previous site's output). T_step = 1 runs one persistent kernel for the whole decode
+ * (batch-1); T_step >= 2 runs the batched path per (step, site).
+ */
+int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
+                     float* rho, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Copy the workspace's status word to *host_status (host pointer) after synchronising `stream`:
+ * GSI_OK, or GSI_ERR_TIMEOUT if an in-kernel wait of an earlier call ran past its bound.
+ * Resets the word to GSI_OK.
+ */
+int gsi_workspace_status(void* ws, size_t ws_bytes, int* host_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSI_H */

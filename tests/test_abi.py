@@ -1,0 +1,84 @@
+"""The C ABI loads, exports every symbol include/gsi.h declares, and rejects invalid arguments
+before touching the device (these calls run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+g = pytest.importorskip("gated_rank_linear_amd")
+lib = g.lib
+vp = ctypes.c_void_p
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gsi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gsi_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 12
+    bound = {n for n, _, _ in g.SIGNATURES}
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+        assert n in bound, f"{n} has no binding"
+
+
+def test_status_strings():
+    for code in range(0, -10, -1):
+        s = lib.gsi_status_string(code)
+        assert s and len(s) > 1
+    assert lib.gsi_status_string(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("dtype,d_out,d,k,ok", [
+    (2, 12288, 4096, 256, True), (2, 4096, 16384, 256, True), (0, 768, 768, 64, True), (1, 2304, 768, 256, True),
+    (2, 4096, 4096, 512, True), (3, 16, 16, 8, False), (2, 0, 16, 8, False), (2, 16, 12, 8, False),
+    (2, 16, 16, 24, False), (2, 16, 16, 32, False), (2, 16, 4096, 1024, False), (2, 16, 16, 4, False),
+])
+def test_aux_and_workspace_sizes(dtype, d_out, d, k, ok):
+    a = lib.gsi_layer_aux_bytes(dtype, d_out, d, k)
+    w = lib.gsi_workspace_bytes(dtype, d_out, d, k, 64)
+    if ok:
+        es = 4 if dtype == 0 else 2
+        assert a >= k * d * es + k * k * 4
+        assert w >= 64 * k * 4
+    else:
+        assert a == 0 and w == 0
+
+
+def test_layer_create_validation_before_device():
+    h = vp()
+    p = vp(256)  # never dereferenced: validation fails first
+    assert lib.gsi_layer_create(None, 2, 16, 16, 8, p, p, p, p, 1 << 20, None) == -1
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, None, p, p, p, 1 << 20, None) == -1
+    assert h.value is None
+    assert lib.gsi_layer_create(ctypes.byref(h), 7, 16, 16, 8, p, p, p, p, 1 << 20, None) == -3
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 24, p, p, p, p, 1 << 20, None) == -2
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, vp(257), p, p, p, 1 << 20, None) == -6
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, p, p, p, p, 16, None) == -5
+
+
+def test_forward_and_stack_validation_before_device():
+    p = vp(256)
+    assert lib.gsi_forward(None, p, 1, ctypes.c_float(0.1), p, p, None, p, 1 << 20, None) == -1
+    assert lib.gsi_stack_create(None, None, 0) == -1
+    h = vp()
+    assert lib.gsi_stack_create(ctypes.byref(h), None, 1) == -1
+    arr = (vp * 1)(None)
+    assert lib.gsi_stack_create(ctypes.byref(h), arr, 1) == -1
+    assert lib.gsi_stack_create(ctypes.byref(h), arr, 0) == -2
+    assert lib.gsi_stack_decode(None, p, 1, 1, ctypes.c_float(0.1), p, p, None, p, 1 << 20, None) == -1
+    assert lib.gsi_stack_workspace_bytes(None, 1) == 0
+    assert lib.gsi_workspace_status(None, 0, None, None) == -1
+    assert lib.gsi_layer_destroy(None) == 0 and lib.gsi_stack_destroy(None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        g._binding._ptr(torch.zeros(4))
