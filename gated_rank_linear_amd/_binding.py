@@ -13,7 +13,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libgsi.so")
+LIB_PATH = os.environ.get("GSI_LIB") or os.path.join(_HERE, "_lib", "libgsi.so")
 
 GSI_F32, GSI_F16, GSI_BF16 = 0, 1, 2
 GSI_OK = 0

@@ -38,9 +38,11 @@ int check_eps(float eps) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? GSI_OK : GSI_ERR_HIP; }
 
-size_t aux_bytes(int dtype, int d, int k) {
-  return align256((size_t)k * d * dtype_size(dtype)) + align256((size_t)k * k * 4);
-}
+// aux = [V^T (k x d, weight dtype)] [V^T V - I (k x k, float32)] [device copy of the descriptor]
+size_t aux_vt_off(int, int, int) { return 0; }
+size_t aux_dl_off(int dtype, int d, int k) { return align256((size_t)k * d * dtype_size(dtype)); }
+size_t aux_desc_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
+size_t aux_bytes(int dtype, int d, int k) { return aux_desc_off(dtype, d, k) + align256(sizeof(LayerDesc)); }
 
 size_t ws_bytes_for(int k, int T) { return align256(decode_ws_bytes()) + batched_ws_bytes(k, T < 1 ? 1 : T); }
 
@@ -120,8 +122,9 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
   if (aux_nbytes < aux_bytes(dtype, d, k)) return GSI_ERR_WORKSPACE;
   if ((rc = gsi_device_check()) != GSI_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  void* Vt = aux;
-  float* Dl = (float*)((char*)aux + align256((size_t)k * d * dtype_size(dtype)));
+  void* Vt = (char*)aux + aux_vt_off(dtype, d, k);
+  float* Dl = (float*)((char*)aux + aux_dl_off(dtype, d, k));
+  LayerDesc* dev_desc = (LayerDesc*)((char*)aux + aux_desc_off(dtype, d, k));
   // V^T (k x d), then M = W V = W (V^T)^T, then V^T V - I   [GSI §2.1]
   if ((rc = launch_transpose(dtype, V, Vt, d, k, s)) != GSI_OK) return rc;
   if ((rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s)) != GSI_OK)
@@ -130,6 +133,7 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
     return rc;
   gsi_layer* L = new (std::nothrow) gsi_layer;
   if (!L) return GSI_ERR_NULL;
+  L->dev_desc = dev_desc;
   L->dtype = dtype;
   L->d_out = d_out;
   L->d = d;
@@ -144,6 +148,10 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
   L->desc.pad = 0;
   L->desc.x_off = 0;
   L->desc.y_off = 0;
+  if ((rc = launch_write_desc(L->desc, dev_desc, s)) != GSI_OK) {
+    delete L;
+    return rc;
+  }
   *out = L;
   return GSI_OK;
 }
@@ -172,8 +180,7 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
   if (T < 16) {
     DecodeParams p;
     std::memset(&p, 0, sizeof(p));
-    p.sites = nullptr;
-    p.one = L->desc;
+    p.sites = L->dev_desc;
     p.n_sites = 1;
     p.n_tokens = T;
     p.X = x;
@@ -188,7 +195,7 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
     p.k_max = L->k;
     p.d_max = L->d;
     fill_decode_boxes(p, ws);
-    return launch_decode(L->dtype, p, s);
+    return launch_decode(L->dtype, p, &L->desc, s);
   }
   return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, s);
 }
@@ -291,7 +298,7 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
     p.k_max = S->k_max;
     p.d_max = S->d_max;
     fill_decode_boxes(p, ws);
-    return launch_decode(S->dtype, p, s);
+    return launch_decode(S->dtype, p, S->h_table, s);
   }
   const size_t es = dtype_size(S->dtype);
   for (int st = 0; st < n_steps; ++st) {

@@ -141,6 +141,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ sr
   }
 }
 
+__global__ void write_desc_kernel(LayerDesc d, LayerDesc* dst) {
+  if (threadIdx.x == 0) *dst = d;
+}
+
+int launch_write_desc(const LayerDesc& d, LayerDesc* dst, hipStream_t s) {
+  write_desc_kernel<<<1, 64, 0, s>>>(d, dst);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s) {
   dim3 grid((k + 31) / 32, (d + 31) / 32);
   if (dtype == GSI_F32)

@@ -85,7 +85,8 @@ struct LayerDesc {  // device-side description of one site (also used host-side)
 
 struct gsi_layer {
   int dtype, d_out, d, k;
-  gsi::LayerDesc desc;  // x_off = y_off = 0
+  gsi::LayerDesc desc;       // x_off = y_off = 0
+  gsi::LayerDesc* dev_desc;  // device copy, stored in the layer's aux buffer
 };
 
 struct gsi_stack {
@@ -117,8 +118,7 @@ constexpr int kSyncThreads = 64;   // 1 sync wave
 constexpr int kDecodeThreads = kDataThreads + kSyncThreads;
 
 struct DecodeParams {
-  const LayerDesc* sites;  // device table of n_sites descriptors, or NULL to use `one`
-  LayerDesc one;
+  const LayerDesc* sites;  // device table of n_sites descriptors
   int n_sites, n_tokens;
   const void* X;
   long long x_ld;
@@ -130,14 +130,16 @@ struct DecodeParams {
   float eps;
   int k_max, d_max;
   WsHeader* hdr;
-  u64* box_g;  // [2][kReplicas][kMaxK]     parity by exchange index
-  u64* box_p;  // [2][kReplicas][kMaxBlocks]
-  u64* box_f;  // [2][kReplicas][kMaxBlocks]
+  u64* box_g;  // [kReplicas][kMaxK]       g values
+  u64* box_p;  // [kReplicas][kMaxBlocks]  per-block gate pieces
+  u64* box_f;  // [kReplicas][kMaxBlocks]  slow-path completion
 };
 
 size_t decode_ws_bytes();
-int launch_decode(int dtype, const DecodeParams& p, hipStream_t s);
-int decode_grid_blocks(int dtype);
+// host_sites: host copy of the n_sites descriptors (used to size the register windows)
+int launch_decode(int dtype, const DecodeParams& p, const LayerDesc* host_sites, hipStream_t s);
+// enqueue a copy of `d` (passed by value) into device memory `dst`
+int launch_write_desc(const LayerDesc& d, LayerDesc* dst, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Dense helpers (create time and the batched path)

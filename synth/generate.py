@@ -79,14 +79,23 @@ def _m(cfg: Config, d: int) -> int:
     return min(d - cfg.k, cfg.m_complement)
 
 
+def _fresh_basis(cid: int, block: int, site: int):
+    cfg = get(cid)
+    d, k = cfg.sites[site].d, cfg.k
+    m = _m(cfg, d)
+    q = orthonormal_columns(_rng(cid, block, site, _S_BASIS), d, k + m)
+    return q[:, :k].copy(), q[:, k:k + m].copy()
+
+
 @lru_cache(maxsize=None)
 def _chain_basis(cid: int, block: int, site: int):
+    """Depth-coherent chain (cached: block l needs block l-1)."""
     cfg = get(cid)
-    shp = cfg.sites[site]
-    d, k, m = shp.d, cfg.k, _m(cfg, shp.d)
-    if block == 0 or cfg.depth_rotation_deg is None:
-        q = orthonormal_columns(_rng(cid, block, site, _S_BASIS), d, k + m)
-        return q[:, :k].copy(), q[:, k:k + m].copy()
+    if block == 0:
+        return _fresh_basis(cid, block, site)
+    k = cfg.k
+    d = cfg.sites[site].d
+    m = _m(cfg, d)
     v_prev, _ = _chain_basis(cid, block - 1, site)
     th = math.radians(cfg.depth_rotation_deg)
     q = orthonormal_columns(_rng(cid, block, site, _S_ROT), d, 2 * k, lead=v_prev)
@@ -98,8 +107,9 @@ def _chain_basis(cid: int, block: int, site: int):
 
 def site_basis(cfg: Config, block: int, site: int):
     """(V_k, C) in float64: d x k orthonormal basis and d x m orthonormal complement block."""
-    v, c = _chain_basis(cfg.cid, block, site)
-    return v, c
+    if cfg.depth_rotation_deg is None:
+        return _fresh_basis(cfg.cid, block, site)
+    return _chain_basis(cfg.cid, block, site)
 
 
 def site_weight(cfg: Config, block: int, site: int) -> torch.Tensor:
@@ -203,3 +213,25 @@ def site_inputs(cfg: Config, block: int, site: int, n_steps: int | None = None) 
 def token_steps(cfg: Config) -> int:
     """Steps actually generated per site (pool size when the config cycles a pool)."""
     return cfg.token_pool_steps if cfg.token_pool_steps is not None else cfg.n_steps
+
+
+def config_inputs(cfg: Config, blocks=None, n_steps: int | None = None, threads: int | None = None):
+    """SiteInputs for every (block, site) of `blocks` (default: all), in decode order.
+
+    Sites are generated concurrently, each worker with a single BLAS thread; results do not depend
+    on the number of workers (every site has its own seeds). Depth-coherent chains are generated
+    block by block within a site, so they stay serial per site.
+    """
+    from threadpoolctl import threadpool_limits
+
+    blocks = list(range(cfg.n_blocks)) if blocks is None else list(blocks)
+    keys = [(b, s) for b in blocks for s in range(len(cfg.sites))]
+    if cfg.depth_rotation_deg is not None:
+        # warm the per-site chains in parallel over sites, serially over blocks
+        def chain(s):
+            for b in range(max(blocks) + 1):
+                site_basis(cfg, b, s)
+        with threadpool_limits(limits=1), ThreadPoolExecutor(min(len(cfg.sites), threads or _threads())) as ex:
+            list(ex.map(chain, range(len(cfg.sites))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads or _threads()) as ex:
+        return list(ex.map(lambda bs: site_inputs(cfg, bs[0], bs[1], n_steps), keys))

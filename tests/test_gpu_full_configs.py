@@ -1,0 +1,126 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Gate bits of every (token, site) are compared with the fp64 oracle (which needs only V and x);
+y is compared on sampled sites (all of their tokens) where the oracle also needs W.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gsi_oracle as orc
+from tests.gpu_util import TOL, Built, check_site, decode, rel_l2, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gated_rank_linear_amd as g
+    assert g.gsi_device_check() == 0
+    return g
+
+
+def _run_stack(cid, sample_sites, n_steps=None, T_step=1):
+    cfg = synth.get(cid)
+    say(f"case: config {cid} full stack ({cfg.n_blocks} blocks x {len(cfg.sites)} sites), T_step={T_step}")
+    built = Built(cfg, n_steps=n_steps, keep_w_for=sample_sites)
+    Y, gates, rho, _ = decode(built, cfg.eps, T_step=T_step)
+    Ys = built.split_outputs(Y)
+    n_slow = 0
+    worst = 0.0
+    for i, (b, s, si) in enumerate(built.sites):
+        e = check_site(built, i, Ys[i], gates[:, i], cfg.eps, with_y=(b, s) in sample_sites)
+        if e is not None:
+            worst = max(worst, e)
+    n_slow = int(gates.sum().item())
+    say(f"  gates exact on {gates.numel()} (token, site) pairs, {n_slow} slow; worst sampled y rel L2 {worst:.2e}")
+    return gates, worst
+
+
+def test_config3_gptj_stack_batch1(g):
+    cfg = synth.get(3)
+    sample = {(0, 0), (0, 1), (0, 2), (0, 3), (cfg.n_blocks - 1, 0), (cfg.n_blocks - 1, 3)}
+    gates, worst = _run_stack(3, sample)
+    assert gates.shape == (cfg.n_tokens, cfg.n_sites)
+    assert int(gates.sum()) == cfg.n_sites  # one slow token per site (99.8% fast)
+    assert worst <= TOL["bf16"]
+
+
+def test_config4_opt_stack_batch1(g):
+    cfg = synth.get(4)
+    sample = {(0, 0), (0, 2), (cfg.n_blocks - 1, 1), (cfg.n_blocks - 1, 3)}
+    gates, worst = _run_stack(4, sample)
+    frac = gates.float().mean().item()
+    assert 0.10 < frac < 0.20, frac
+    assert worst <= TOL["bf16"]
+
+
+def test_config5_gptj_batched_T64(g):
+    cfg = synth.get(5)
+    sample = {(0, 0), (0, 3), (cfg.n_blocks - 1, 2)}
+    gates, worst = _run_stack(5, sample, n_steps=4, T_step=cfg.t_step)
+    frac = gates.float().mean().item()
+    assert 0.1 < frac < 0.3, frac
+    assert worst <= TOL["bf16"]
+
+
+def _planned_tokens(rng, V, C, eps, n, slow_frac):
+    """Tokens with planned residual ratios (by construction from an orthonormal [V | C])."""
+    k, m = V.shape[1], C.shape[1]
+    slow = rng.random(n) < slow_frac
+    rho = np.where(slow, rng.uniform(eps + 5e-3, min(2 * eps, 0.95), n), rng.uniform(eps / 2, eps - 5e-3, n))
+    z = rng.standard_normal((n, k))
+    w = rng.standard_normal((n, m))
+    s = rho * np.linalg.norm(z, axis=1) / (np.linalg.norm(w, axis=1) * np.sqrt(1 - rho ** 2))
+    return z @ V.T + (s[:, None] * w) @ C.T
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(100, 40, 8), (257, 64, 32), (1000, 520, 64), (3, 24, 8), (700, 1032, 256)])
+def test_ragged_shapes(g, dtype, shape):
+    """Output rows not a multiple of the block split, d not a multiple of the lane tiles, k from 8
+    up, T = 1, 5, 17, 37 (persistent and batched paths, tails everywhere)."""
+    d_out, d, k = shape
+    rng = np.random.default_rng(d_out * 7 + d + k)
+    Q, R = np.linalg.qr(rng.standard_normal((d, min(d, k + 64))))
+    Q = Q * np.sign(np.diag(R))
+    V64, C64 = Q[:, :k], Q[:, k:]
+    W = torch.from_numpy(rng.standard_normal((d_out, d)) * 0.05).to(dtype)
+    V = torch.from_numpy(V64).to(dtype)
+    eps = 0.2
+    say(f"case: ragged {shape} {dtype}")
+    L = g.create_layer(W.cuda(), V.cuda())
+    for T in (1, 5, 17, 37):
+        X = torch.from_numpy(_planned_tokens(rng, V64, C64, eps, T, 0.3)).to(dtype)
+        ref_gate = orc.gate_only(V, X, eps)
+        keep = np.abs(ref_gate["rho"] - eps) > 1e-3   # rounding can move a token to the line
+        x = X.cuda().contiguous()
+        y = torch.zeros((T, d_out), dtype=dtype, device="cuda")
+        gate = torch.full((T,), 9, dtype=torch.uint8, device="cuda")
+        ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, d_out, d, k, T))
+        g.gsi_forward(L, x, eps, y, gate, None, ws)
+        torch.cuda.synchronize()
+        assert g.gsi_workspace_status(ws) == 0
+        gb = gate.cpu().numpy()
+        assert np.array_equal(gb[keep], ref_gate["gate"][keep]), f"T={T}"
+        ref = orc.forward(W, V, X, eps)
+        tol = TOL["f32"] if dtype == torch.float32 else TOL["bf16"]
+        # compare y only where the gate agrees (all tokens with a clear margin)
+        err = rel_l2(to_np(y)[keep], ref["y"][keep])
+        assert err <= tol, f"T={T}: y rel L2 {err}"
+
+
+def test_zero_tokens_is_a_no_op(g):
+    cfg = synth.get(1)
+    si = synth.site_inputs(cfg, 0, 0)
+    L = g.create_layer(synth.site_weight(cfg, 0, 0).cuda(), si.V.cuda())
+    x = torch.zeros((0, 768), device="cuda")
+    y = torch.full((1, 768), 7.0, device="cuda")
+    gate = torch.full((1,), 9, dtype=torch.uint8, device="cuda")
+    ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, 768, 768, 64, 1))
+    rc = g.lib.gsi_forward(L.handle, x.data_ptr() or 16, 0, 0.1, y.data_ptr(), gate.data_ptr(), None,
+                           ws.data_ptr(), ws.numel(), None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.all(y == 7.0) and int(gate.item()) == 9
