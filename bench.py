@@ -149,6 +149,8 @@ def main():
     achieved = bytes_total / t_gpu / 1e9
     tok_s = args.steps / t_gpu
 
+    traffic = measured_traffic(cfg, n_tok)
+
     # ---------------- CPU baseline: the fp64 oracle on a bounded sample ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -172,8 +174,8 @@ def main():
                                + f", k={cfg.k}, eps={cfg.eps}, batch 1, {n_tok} distinct tokens",
                    "batch": 1, "k": cfg.k, "eps": cfg.eps, "sites": n_sites},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gsi::decode_kernel<bf16_t>", "launches": n_launch,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "gsi::decode_kernel<bf16_t, 1, 8, 8>", "launches": n_launch,
                      "bytes_per_launch": bytes_total / n_launch, "launch_ms": round(t_gpu * 1e3 / n_launch, 4)},
         "cpu_baseline": cpu,
         "fast_fraction": round(fast_frac, 5),
@@ -183,6 +185,21 @@ def main():
                        "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS},
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(cfg, tokens_per_launch: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
+    each scaled by a 1 GiB copy), or None when the decode kernel's source changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_kernel_gptj_stack_bf16.traffic.json")
+    src = os.path.join(ROOT, "gated_rank_linear_amd", "csrc", "gsi_decode.hip")
+    if cfg.cid != 3 or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return round(rec["traffic_bytes_per_launch"] / rec["tokens_per_launch"] * tokens_per_launch)
 
 
 def cpu_baseline(cfg, sites, keep, seconds: float):
