@@ -175,7 +175,7 @@ def main():
                    "batch": 1, "k": cfg.k, "eps": cfg.eps, "sites": n_sites},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gsi::decode_kernel<bf16_t, 1, 8, 8>", "launches": n_launch,
+                     "kernel": decode_kernel_name(cfg), "launches": n_launch,
                      "bytes_per_launch": bytes_total / n_launch, "launch_ms": round(t_gpu * 1e3 / n_launch, 4)},
         "cpu_baseline": cpu,
         "fast_fraction": round(fast_frac, 5),
@@ -185,6 +185,15 @@ def main():
                        "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS},
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_kernel_name(cfg) -> str:
+    """The decode kernel instance the library launches for this stack: element type and input
+    window (2 chunks of 16 bytes per data thread when every input row fits in 512 chunks, else 8)."""
+    es = 4 if cfg.dtype == "f32" else 2
+    need = max((s.d * es // 16 + 255) // 256 for s in cfg.sites)
+    t = {"f32": "float", "f16": "gsi::f16_t", "bf16": "gsi::bf16_t"}[cfg.dtype]
+    return f"gsi::decode_kernel<{t}, {2 if need <= 2 else 8}>"
 
 
 def measured_traffic(cfg, tokens_per_launch: int):

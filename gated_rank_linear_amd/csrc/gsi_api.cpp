@@ -21,13 +21,9 @@ int check_shape(int dtype, int d_out, int d, int k) {
   if (!dtype_ok(dtype)) return GSI_ERR_DTYPE;
   if (d_out < 1 || d < 8 || d % 8 != 0 || d > 65536) return GSI_ERR_SHAPE;
   if (k < 8 || k > 512 || k > d || !pow2(k)) return GSI_ERR_SHAPE;
-  // rows of M longer than one wave of 16-byte chunks are combined through a 256-entry buffer
-  const int cprk = (int)(k * dtype_size(dtype) / 16);
-  if (cprk > 64) {
-    const int segs = cprk / 64;
-    const int rpb_max = (d_out + (kMaxK / 4) - 1) / (kMaxK / 4);  // at least 128 blocks
-    if ((long long)rpb_max * segs > 256) return GSI_ERR_SHAPE;
-  }
+  // a decode block holds its rows of y in LDS: at most kYPart rows for the largest row share,
+  // ceil(d_out / kMinBlocks)
+  if (((long long)d_out + kMinBlocks - 1) / kMinBlocks > kYPart) return GSI_ERR_SHAPE;
   return GSI_OK;
 }
 

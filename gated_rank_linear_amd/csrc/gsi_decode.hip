@@ -9,22 +9,28 @@
 // Design (one block per CU, all blocks co-resident via a cooperative launch):
 //  * Work split per site: block b owns the g columns j = b, b + P, ... (rows of V^T: each g_j is
 //    one complete d-long dot product inside one block) and a contiguous slice of output rows of
-//    M / W. Its slices of the next site (V^T rows, M rows, (V^T V - I) rows) and the next input
-//    row are loaded into registers while the current site waits on its exchanges, so the HBM
-//    stream overlaps synchronisation. Prefetch loads are unconditional (out-of-range slots read a
-//    valid dummy chunk) so the compiler keeps them in flight across barriers.
+//    M / W.
 //  * Two all-gather exchanges per site: (E1) every block needs all of g for its rows of M g;
-//    (E2) the gate needs the global sum of per-block pieces of g^T (V^T V - I) g, and its
-//    completion also means every block has written its rows of y. A slow token adds (E3), the
-//    completion of the W x rows.
+//    (E2) the gate needs the global sum of per-block pieces of g^T (V^T V - I) g. A block posts
+//    its E2 word only after its rows of y are stored, so E2 is also the completion of the site:
+//    no block starts the next site before every block has finished this one. A slow token adds
+//    (E3), the completion of the W x rows.
+//  * Weights stream into LDS ahead of use: two 64 KB site regions alternate with the site
+//    parity. Right after posting its E1 word, a block's data waves copy its slices of site s + 1
+//    (its V^T rows, its rows of V^T V - I and its rows of M) from HBM straight into the other
+//    region (global_load_lds, 16 bytes per lane, no registers); the copy drains while E1
+//    resolves and lands long before site s + 1 needs it. Nothing bulky is in flight on the CU
+//    while E2 resolves: only the next input row, read into registers after this block's rows of y
+//    are stored and used only after E2 has completed. Slices that do not fit a region are read
+//    from global memory when used.
 //  * Exchanges use tagged 64-bit mailbox words (tag << 32 | payload) with one copy per XCD, so
 //    a block polls the copy on its own XCD's side; stores and polls are device-scope. Tags grow
 //    monotonically across launches (base kept in the workspace header), so nothing is cleared.
 //    A slot is rewritten only after every reader consumed it (the other exchange always sits in
 //    between two uses of one mailbox).
-//  * One wave per block (the sync wave) does all polling; four data waves load and compute.
-//    Every wait is bounded: past the bound the launch is marked aborted and every block leaves,
-//    so a lost block cannot hang the device.
+//  * One wave per block (the sync wave) does all polling and posting; four data waves copy and
+//    compute. Every wait is bounded: past the bound the launch is marked aborted and every block
+//    leaves, so a lost block cannot hang the device.
 //  * Gate arithmetic is done identically (same data, same order) in every block, so all blocks
 //    take the same branch.
 #include <algorithm>
@@ -33,14 +39,19 @@
 
 namespace gsi {
 
-constexpr int kMaxJ = 4;   // g columns per block (k <= 512 with at least 128 blocks)
-constexpr int kSyncDRegs = 2;  // (V^T V - I) chunks per sync-wave lane held in registers
+constexpr int kMaxJ = 4;       // g columns per block (k <= 512 with at least 128 blocks)
 constexpr int kSlowBatch = 8;  // W / x chunk pairs per lane in flight on the slow path
 constexpr unsigned long long kWaitTicks = 200000000ull;  // 2 s at the 100 MHz wall clock
 
 // A 16-byte chunk as a built-in vector (address-space-qualified pointers to it copy cleanly).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1)))* g4p;  // global memory, read
+typedef __attribute__((address_space(3))) void lds_void;
+typedef u32x4 __attribute__((address_space(3))) lu32x4;  // a 16-byte chunk in LDS
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ldg(g4p p, long long i) { return p[i]; }
 
@@ -66,6 +77,19 @@ __device__ __forceinline__ u64 ld_dev(const u64* p) { return __hip_atomic_load(p
 __device__ __forceinline__ void st_dev(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u64 pack(unsigned tag, float v) { return ((u64)tag << 32) | (u64)__float_as_uint(v); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (expcnt and
+// lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS operations, not for its
+// outstanding global loads, so copies into LDS and mailbox stores stay in flight across it.
+// (Vector-memory data is always waited for explicitly before it is used.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <typename T>
 __device__ __forceinline__ void unpack(const u32x4& q, float* out) {
   const T* e = reinterpret_cast<const T*>(&q);
@@ -82,14 +106,34 @@ __device__ __forceinline__ float dot_chunk(const u32x4& a, const u32x4& b, float
   for (int i = 0; i < vec16<T>::N; ++i) acc = __builtin_fmaf(fa[i], fb[i], acc);
   return acc;
 }
+// Dot product of two 16-byte chunks of the same element type, accumulated in float32 (bf16 and
+// f16 pairs through v_dot2: the products are exact in float32). The 32-bit words are copied to
+// scalars before they are reinterpreted: reinterpreting a member of a vector held by reference
+// in place reads the vector's first word for every member with this compiler.
 template <typename T>
-__device__ __forceinline__ float sq_chunk(const u32x4& a, float acc) {
-  float fa[vec16<T>::N];
-  unpack<T>(a, fa);
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc);
+template <>
+__device__ __forceinline__ float dot16<bf16_t>(const u32x4& a, const u32x4& b, float acc) {
+  const unsigned aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int i = 0; i < vec16<T>::N; ++i) acc = __builtin_fmaf(fa[i], fa[i], acc);
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[i]), __builtin_bit_cast(bf16x2, bw[i]), acc,
+                                          false);
   return acc;
 }
+template <>
+__device__ __forceinline__ float dot16<f16_t>(const u32x4& a, const u32x4& b, float acc) {
+  const unsigned aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, aw[i]), __builtin_bit_cast(f16x2, bw[i]), acc, false);
+  return acc;
+}
+template <>
+__device__ __forceinline__ float dot16<float>(const u32x4& a, const u32x4& b, float acc) {
+  return dot_chunk<float>(a, b, acc);
+}
+
 template <typename T>
 __device__ __forceinline__ float dot_chunk_lds(const u32x4& a, const float* g, float acc) {
   float fa[vec16<T>::N];
@@ -133,15 +177,35 @@ __device__ __forceinline__ float wave_reduce(float v) {
   return v;
 }
 
+// Block b's share of one site and the layout of its LDS region (in 16-byte chunks). The region
+// holds [V^T rows | (V^T V - I) rows | M rows], each part starting on a 64-chunk boundary so that
+// every 1 KB copy instruction lies inside one part.
 struct SiteGeom {
   int nJ;        // g columns owned by this block
   int cprd;      // 16-byte chunks per V^T / W row (d / VW)
   int nx;        // x chunks per data thread (ceil(cprd / 256))
   int cprk;      // 16-byte chunks per M row (k / VW)
+  int cpk4;      // float4 chunks per (V^T V - I) row (k / 4)
   int r0, nrows; // output rows owned
   int nm;        // M chunks owned (nrows * cprk)
-  int nd;        // (V^T V - I) float4 chunks owned (nJ * k / 4)
+  int nd;        // (V^T V - I) chunks owned (nJ * cpk4)
+  int vj, v_n;   // V^T rows held in the region and their chunks (at offset 0)
+  int d_off, d_n;  // (V^T V - I) part: offset and chunks held (all or none)
+  int m_off, m_n;  // M part: offset and chunks held
+  int m_rows;    // rows of the M slice held in the region (the rest is read from HBM)
+  bool mf;       // matrix-core layout of the M part (bf16 with k >= 128): 16-row x 32-column
+                 // tiles, tile (rt, kt) being one 1 KB block whose lane l holds row 16 rt +
+                 // l mod 16, columns 32 kt + 8 (l / 16) .. + 7, i.e. the A operand of
+                 // v_mfma_f32_16x16x32_bf16; otherwise the rows are stored as they are, and the
+                 // part held is all of the slice or a multiple of 256 chunks so that one pass of
+                 // the data waves never mixes LDS and global reads
+  int n_inst;    // 1 KB copy instructions that fill the region
 };
+
+__device__ __forceinline__ int align64(int v) { return (v + 63) & ~63; }
+
+template <typename T> struct is_bf16 { static constexpr bool v = false; };
+template <> struct is_bf16<bf16_t> { static constexpr bool v = true; };
 
 template <typename T>
 __device__ __forceinline__ SiteGeom geom(const LayerDesc& L, int b, int P) {
@@ -151,86 +215,81 @@ __device__ __forceinline__ SiteGeom geom(const LayerDesc& L, int b, int P) {
   g.cprd = L.d / VW;
   g.nx = (g.cprd + kDataThreads - 1) / kDataThreads;
   g.cprk = L.k / VW;
+  g.cpk4 = L.k / 4;
   const int rpb = (L.d_out + P - 1) / P;
   g.r0 = min(L.d_out, b * rpb);
   g.nrows = min(L.d_out, g.r0 + rpb) - g.r0;
   g.nm = g.nrows * g.cprk;
-  g.nd = g.nJ * (L.k / 4);
+  g.nd = g.nJ * g.cpk4;
+  g.vj = min(g.nJ, kRegionChunks / g.cprd);
+  g.v_n = g.vj * g.cprd;
+  g.d_off = align64(g.v_n);
+  g.d_n = g.d_off + g.nd <= kRegionChunks ? g.nd : 0;
+  g.m_off = align64(g.d_off + g.d_n);
+  g.mf = is_bf16<T>::v && L.k >= 128;
+  if (g.mf) {
+    const int tile = 16 * g.cprk;  // chunks per 16-row tile
+    const int tiles = min((g.nrows + 15) / 16, max(0, (kRegionChunks - g.m_off) / tile));
+    g.m_n = tiles * tile;
+    g.m_rows = min(g.nrows, tiles * 16);
+  } else {
+    g.m_n = g.m_off + g.nm <= kRegionChunks ? g.nm : max(0, (kRegionChunks - g.m_off) / kDataThreads * kDataThreads);
+    g.m_rows = g.m_n / g.cprk;
+  }
+  g.n_inst = (g.m_off + g.m_n + 63) / 64;
   return g;
 }
 
-// Register windows: JR x XR chunks of V^T rows (column jl, x chunk tid + 256 u), XR chunks of the
-// input row, and MR chunks of M rows (chunk tid + 256 u of the block's slice).
-template <int JR, int XR, int MR>
-struct Window {
-  u32x4 v[JR][XR];
-  u32x4 x[XR];
-  u32x4 m[MR];
-};
-
-// Loads of one site's slices (and its input row) into the window, in two parts: the V^T rows and
-// the input row (consumed in phase A), then the M and (V^T V - I) rows (consumed in phase B). All
-// loads are unconditional: each reads through a pointer selected beforehand (the real chunk or a
-// valid dummy chunk), so exactly one load is issued per slot and it never leaves a valid buffer.
-template <typename T, int JR, int XR, int MR>
-__device__ __forceinline__ void prefetch_proj(const LayerDesc& L, const SiteGeom& g, const void* xrow, int b, int P,
-                                              int tid, const u32x4* dummy, Window<JR, XR, MR>& w) {
-  const g4p vt = (g4p)L.Vt;
-  const g4p dm = (g4p)dummy;
-#pragma unroll
-  for (int jl = 0; jl < JR; ++jl) {
-#pragma unroll
-    for (int u = 0; u < XR; ++u) {
-      const int cc = tid + u * kDataThreads;
-      const bool ok = jl < g.nJ && cc < g.cprd;
-      const long long j = b + (long long)jl * P;
-      const g4p src = ok ? vt + (j * g.cprd + cc) : dm;
-      w.v[jl][u] = src[0];
+// Copy instructions [i0, i1) of a site's region fill; instruction i (chunks 64 i .. 64 i + 63 of
+// the region) is issued by data wave i mod 4. Each lane reads one 16-byte chunk from global
+// memory straight into LDS at region + 16 (64 i + lane). Lanes past the end of a part read a
+// valid dummy chunk into the part's padding, so every lane issues exactly one load.
+template <typename T>
+__device__ __forceinline__ void fill_region(const LayerDesc& L, const SiteGeom& g, int b, int P, int wave, int lane,
+                                            int i0, int i1, lu32x4* region,
+                                            const u32x4* dummy) {
+  const char* vt = reinterpret_cast<const char*>(L.Vt);
+  const char* dl = reinterpret_cast<const char*>(L.Dl);
+  const char* mp = reinterpret_cast<const char*>(L.M) + (long long)g.r0 * g.cprk * 16;
+  for (int i = i0 + ((wave - i0) & 3); i < i1; i += 4) {
+    const int c = i * 64 + lane;
+    const char* src = reinterpret_cast<const char*>(dummy);
+    if (c < g.v_n) {
+      const int jl = c / g.cprd, cc = c - jl * g.cprd;
+      src = vt + ((long long)(b + jl * P) * g.cprd + cc) * 16;
+    } else if (c >= g.d_off && c < g.d_off + g.d_n) {
+      const int e = c - g.d_off;
+      const int jl = e / g.cpk4, cc = e - jl * g.cpk4;
+      src = dl + ((long long)(b + jl * P) * g.cpk4 + cc) * 16;
+    } else if (c >= g.m_off && c < g.m_off + g.m_n) {
+      if (g.mf) {  // tile (rt, kt) = instruction (i - m_off / 64) in row-tile-major order
+        const int kt = g.cprk / 4;
+        const int it = i - g.m_off / 64;
+        const int rt = it / kt, kk = it - rt * kt;
+        const int row = rt * 16 + (lane & 15);
+        if (row < g.nrows) src = mp + ((long long)row * g.cprk + kk * 4 + (lane >> 4)) * 16;
+      } else {
+        src = mp + (long long)(c - g.m_off) * 16;
+      }
     }
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(region + i * 64), 16, 0, 0);
   }
+}
+
+// The input row's chunks tid + 256 u (u < XR) into registers; slots past the row re-read chunk 0.
+template <typename T, int XR>
+__device__ __forceinline__ void load_x(const void* xrow, const SiteGeom& g, int tid, u32x4 (&xw)[XR]) {
   const g4p xp = (g4p)xrow;
 #pragma unroll
   for (int u = 0; u < XR; ++u) {
     const int cc = tid + u * kDataThreads;
-    w.x[u] = xp[cc < g.cprd ? cc : 0];
-  }
-}
-template <typename T, int JR, int XR, int MR>
-__device__ __forceinline__ void prefetch_image(const LayerDesc& L, const SiteGeom& g, int b, int P, int tid,
-                                               const u32x4* dummy, Window<JR, XR, MR>& w) {
-  const g4p dm = (g4p)dummy;
-  const g4p mp = (g4p)L.M + (long long)g.r0 * g.cprk;
-#pragma unroll
-  for (int u = 0; u < MR; ++u) {
-    const int c = tid + u * kDataThreads;
-    const g4p src = c < g.nm ? mp + c : dm;
-    w.m[u] = src[0];
-  }
-}
-
-// Sync wave: load this block's rows of V^T V - I for the next site (chunk c = lane + 64 u).
-__device__ __forceinline__ void prefetch_sync_delta(const LayerDesc& L, const SiteGeom& g, int b, int P, int lane,
-                                                    const u32x4* dummy, u32x4 (&sdl)[kSyncDRegs]) {
-  const g4p dm = (g4p)dummy;
-  const int cpk4 = L.k / 4;
-  const g4p dl = (g4p)L.Dl;
-#pragma unroll
-  for (int u = 0; u < kSyncDRegs; ++u) {
-    const int c = lane + 64 * u;
-    const bool ok = c < g.nd;
-    const int jl = ok ? c / cpk4 : 0, cc = ok ? c - jl * cpk4 : 0;
-    const long long j = b + (long long)jl * P;
-    const g4p src = ok ? dl + (j * cpk4 + cc) : dm;
-    sdl[u] = src[0];
+    xw[u] = xp[cc < g.cprd ? cc : 0];
   }
 }
 
 // A block whose wait runs past its bound marks this launch (tag base + 1) as aborted; every other
 // block polls that mark while it waits, so the whole grid leaves promptly. The mark of an older
 // launch never matches because every launch advances the tag base.
-__device__ __forceinline__ bool aborted(const DecodeParams& p, unsigned base) {
-  return __hip_atomic_load(&p.hdr->abort_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == base + 1u;
-}
 __device__ __forceinline__ void record_abort(const DecodeParams& p, unsigned base) {
   __hip_atomic_store(&p.hdr->abort_tag, base + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(&p.hdr->status, (int)GSI_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -266,12 +325,405 @@ __device__ __forceinline__ bool gather(const DecodeParams& p, unsigned base, con
   }
 }
 
-template <typename T, int JR, int XR, int MR>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+// LDS shared by the phases of one site (the two site regions are separate arrays so that the
+// compiler can tell a copy into one region from reads of the other).
+struct Shared {
+  float* gsh;    // [kMaxK] gathered g
+  lu32x4* gb;    // [kGbChunks] B operands of the matrix-core path (see mfma_rows)
+  float* ypart;  // [kYPart] this block's rows of y (float32) before rounding
+  float (*red)[kMaxJ + 2];  // [4][kMaxJ + 2] per-wave partial sums of phase A
+  float* s_nx2;
+  float* s_gg;
+  int* s_gate;
+  int* s_abort;
+};
+
+// Vector-ALU rows of y = M g. Each row is covered by Lr = cprk / CPL lanes of one wave, lane
+// (r, lc) holding chunks lc + Lr i (i < CPL) of row r, so a row's sum takes log2(Lr) DPP steps
+// and every thread reads its CPL slices of g once. Slots i >= CPL (rows shorter than 4 chunks)
+// read chunk 0 and g entries below 4 VW <= kMaxK, all in bounds, and are masked out of the sum.
+struct RowLanes {
+  int CPL, Lr, rpw, lr, lc;
+  int ch[4];
+};
+template <typename T>
+__device__ __forceinline__ RowLanes row_lanes(const SiteGeom& g, int lane) {
+  RowLanes q;
+  q.CPL = min(4, g.cprk);
+  q.Lr = g.cprk / q.CPL;  // lanes per row (a power of two <= 32)
+  q.rpw = 64 / q.Lr;      // rows per wave per pass
+  q.lr = lane / q.Lr;
+  q.lc = lane & (q.Lr - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q.ch[i] = i < q.CPL ? q.lc + q.Lr * i : 0;
+  return q;
+}
+template <typename T>
+__device__ __forceinline__ void g_slices(const Shared& sh, const RowLanes& q, float (&gl)[4][vec16<T>::N]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < vec16<T>::N; ++e) gl[i][e] = sh.gsh[(q.lc + q.Lr * i) * vec16<T>::N + e];
+}
+// rows [0, m_rows) from the region (stored as they are)
+template <typename T>
+__device__ __forceinline__ void row_sums_lds(const SiteGeom& g, const lu32x4* cur, const Shared& sh, int wave,
+                                             int lane) {
+  const RowLanes q = row_lanes<T>(g, lane);
+  float gl[4][vec16<T>::N];
+  g_slices<T>(sh, q, gl);
+  for (int rp = 0; rp < g.m_rows; rp += 4 * q.rpw) {
+    const int r = rp + wave * q.rpw + q.lr;
+    const bool ok = r < g.m_rows;
+    const int rb = g.m_off + (ok ? r : 0) * g.cprk;
+    u32x4 mv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mv[i] = cur[rb + q.ch[i]];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = dot_chunk_lds<T>(mv[i], gl[i], 0.f);
+      acc += i < q.CPL ? d : 0.f;
+    }
+    acc = group_reduce(ok ? acc : 0.f, q.Lr);
+    if (ok && q.lc == q.Lr - 1) sh.ypart[r] = acc;
+  }
+}
+// rows [m_rows, nrows) read from HBM (slices that do not fit the region)
+template <typename T>
+__device__ __forceinline__ void row_sums_hbm(const LayerDesc& L, const SiteGeom& g, const Shared& sh, int wave,
+                                             int lane) {
+  const RowLanes q = row_lanes<T>(g, lane);
+  float gl[4][vec16<T>::N];
+  g_slices<T>(sh, q, gl);
+  const g4p mrow = (g4p)L.M + (long long)g.r0 * g.cprk;
+  for (int rp = g.m_rows; rp < g.nrows; rp += 4 * q.rpw) {
+    const int r = rp + wave * q.rpw + q.lr;
+    const bool ok = r < g.nrows;
+    const long long rb = (long long)(ok ? r : 0) * g.cprk;
+    u32x4 mv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mv[i] = ldg(mrow, rb + q.ch[i]);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = dot_chunk_lds<T>(mv[i], gl[i], 0.f);
+      acc += i < q.CPL ? d : 0.f;
+    }
+    acc = group_reduce(ok ? acc : 0.f, q.Lr);
+    if (ok && q.lc == q.Lr - 1) sh.ypart[r] = acc;
+  }
+}
+
+// Matrix-core rows of y = M g (bf16, k = 32 KT). Wave w takes the 16-row tiles w, w + 4, ...
+// of the region's M part (stored as A operands of v_mfma_f32_16x16x32_bf16). B carries g as two
+// bf16 columns, column 0 its high part and column 1 the low part (g - high), every other column
+// zero; B for 32-column step s and lane group h = l / 16 is chunk 8 s + 2 h + column of sh.gb,
+// read once per site. Two accumulator chains (even and odd steps) are added at the end; then
+// D[r][0] + D[r][1] (lane l and lane l + 1 of each 16-lane row, a DPP shift) is row r of y.
+// Marks every chunk of `v` as needed here, so all of their loads are issued (and waited for once)
+// before any later use, instead of each load being issued just before its use.
+template <int N>
+__device__ __forceinline__ void hold(const u32x4 (&v)[N]) {
+  static_assert(N == 4 || N == 8, "operand group of 4 or 8 chunks");
+  if constexpr (N == 4) {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  } else {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  }
+}
+
+constexpr int kGbZero = kMaxK / 32 * 8;  // index of an all-zero chunk of sh.gb
+constexpr int kGbChunks = kGbZero + 1;
+template <int KT>
+__device__ __forceinline__ void mfma_rows(const SiteGeom& g, const lu32x4* cur, const Shared& sh, int wave, int lane) {
+  constexpr int KH = KT < 8 ? KT : 8;  // steps held in registers at a time
+  constexpr int NH = KT / KH;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tiles = (g.m_rows + 15) / 16;
+  u32x4 bv[KH];
+  auto load_b = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KH; ++i) bv[i] = sh.gb[col < 2 ? (k0 + i) * 8 + grp * 2 + col : kGbZero];
+    hold(bv);
+  };
+  if (NH == 1) load_b(0);
+  for (int rt = wave; rt < tiles; rt += 4) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      if (NH > 1) load_b(hh * KH);
+      u32x4 av[KH];
+#pragma unroll
+      for (int i = 0; i < KH; ++i) av[i] = cur[g.m_off + (rt * KT + hh * KH + i) * 64 + lane];
+      hold(av);
+#pragma unroll
+      for (int i = 0; i < KH; ++i) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av[i]);
+        const bf16x8 B = __builtin_bit_cast(bf16x8, bv[i]);
+        if (i & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, a1, 0, 0, 0);
+        else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, a0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = a0[r] + a1[r];
+      const float w = v + dpp_src<0x101, 0xF>(v);  // row_shl:1: lane l + 1's value
+      const int row = rt * 16 + 4 * grp + r;
+      if (col == 0 && row < g.m_rows) sh.ypart[row] = w;
+    }
+  }
+}
+
+// One (token, site) step. `cur` holds this site's slices (filled during the previous step);
+// `nxt` receives the next site's. Returns false when the launch was aborted.
+template <typename T, int XR>
+__device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, long long Q, unsigned base, int b, int P,
+                                          int tid, unsigned rep, const u32x4* dummy,
+                                          const lu32x4* cur, lu32x4* nxt, u32x4 (&xw)[XR],
+                                          const Shared& sh) {
   constexpr int VW = vec16<T>::N;
+  const bool is_sync = tid >= kDataThreads;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t = (int)(q / p.n_sites), s = (int)(q - (long long)t * p.n_sites);
+  const LayerDesc L = load_desc(p.sites, s);
+  const SiteGeom g = geom<T>(L, b, P);
+  const unsigned tag = base + (unsigned)(q * 4);
+  const unsigned tag_g = tag + 1, tag_p = tag + 2, tag_f = tag + 3;
+  const T* x = reinterpret_cast<const T*>(p.X) + (long long)t * p.x_ld + L.x_off;
+  const bool has_next = q + 1 < Q;
+  const long long qn = q + 1;
+  const int tn = (int)(qn / p.n_sites), sn = (int)(qn - (long long)tn * p.n_sites);
+  const LayerDesc Ln = load_desc(p.sites, has_next ? sn : s);
+  const SiteGeom gn = geom<T>(Ln, b, P);
+
+  // ---------------- phase A (data waves): g_j for owned columns and |x|^2 ----------------
+  if (!is_sync) {
+    float acc[kMaxJ];
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) acc[j] = 0.f;
+    float sx = 0.f;
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      if (u * kDataThreads < g.cprd) {  // uniform: slots past the input row are skipped
+        const float v = dot16<T>(xw[u], xw[u], 0.f);
+        sx += tid + u * kDataThreads < g.cprd ? v : 0.f;
+      }
+    }
+#pragma unroll
+    for (int jl = 0; jl < kMaxJ; ++jl) {
+      if (jl < g.vj) {  // uniform
+        const int rb = jl * g.cprd;
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < XR; ++u) {
+          if (u * kDataThreads < g.cprd) {  // uniform
+            const int cc = tid + u * kDataThreads;
+            const bool in = cc < g.cprd;
+            const u32x4 vv = cur[rb + (in ? cc : 0)];
+            const float part = dot16<T>(vv, xw[u], 0.f);
+            a += in ? part : 0.f;
+          }
+        }
+        acc[jl] = a;
+      }
+    }
+    // columns not held in the region, and inputs longer than the register window
+    if (g.vj < g.nJ || g.nx > XR) {
+      const g4p x4 = (g4p)x;
+      for (int cc = tid + XR * kDataThreads; cc < g.cprd; cc += kDataThreads) {
+        const u32x4 xv = ldg(x4, cc);
+        sx = dot16<T>(xv, xv, sx);
+      }
+      for (int jl = 0; jl < g.nJ; ++jl) {
+        const long long j = b + (long long)jl * P;
+        const g4p vr = (g4p)L.Vt + j * g.cprd;
+        float a = 0.f;
+        for (int cc = tid + (jl < g.vj ? XR : 0) * kDataThreads; cc < g.cprd; cc += kDataThreads)
+          a = dot16<T>(ldg(vr, cc), ldg(x4, cc), a);
+#pragma unroll
+        for (int jj = 0; jj < kMaxJ; ++jj) acc[jj] += (jj == jl) ? a : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (j < g.nJ) acc[j] = wave_reduce(acc[j]);  // uniform
+    sx = wave_reduce(sx);
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) sh.red[wave][j] = acc[j];
+      sh.red[wave][kMaxJ] = sx;
+    }
+  }
+  lds_barrier();
+  // ---------------- E1: post this block's g_j, then all-gather g ----------------
+  float gj_own[kMaxJ];
+  if (is_sync) {
+#pragma unroll
+    for (int jl = 0; jl < kMaxJ; ++jl)
+      gj_own[jl] = ((sh.red[0][jl] + sh.red[1][jl]) + sh.red[2][jl]) + sh.red[3][jl];
+    for (int jl = 0; jl < g.nJ; ++jl) {
+      const long long j = b + (long long)jl * P;
+      if (lane < kReplicas) st_dev(p.box_g + (long long)lane * kMaxK + j, pack(tag_g, gj_own[jl]));
+    }
+    if (lane == 0) *sh.s_nx2 = ((sh.red[0][kMaxJ] + sh.red[1][kMaxJ]) + sh.red[2][kMaxJ]) + sh.red[3][kMaxJ];
+  }
+  lds_barrier();  // the g words are issued ahead of the copy below
+  if (!is_sync) {
+    if (has_next) fill_region<T>(Ln, gn, b, P, wave, lane, 0, gn.n_inst, nxt, dummy);
+  } else {
+    float gv[kMaxK / 64];
+    const bool ok = gather(p, base, p.box_g + (long long)rep * kMaxK, L.k, tag_g, lane, gv);
+    if (!ok && lane == 0) *sh.s_abort = 1;
+    float gg = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxK / 64; ++i) {
+      const int j = lane + 64 * i;
+      if (j < L.k) {
+        sh.gsh[j] = gv[i];
+        if (g.mf) {  // g = hi + lo + O(2^-18 |g|), both parts bf16 (exact products with M)
+          const bf16_t hi = from_f32<bf16_t>(gv[i]);
+          const bf16_t lo = from_f32<bf16_t>(gv[i] - to_f32(hi));
+          auto* gb16 = reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(sh.gb);
+          const int c0 = ((j >> 5) * 4 + ((j >> 3) & 3)) * 2;  // chunk of (step j / 32, lane group)
+          gb16[c0 * 8 + (j & 7)] = hi.b;
+          gb16[(c0 + 1) * 8 + (j & 7)] = lo.b;
+        }
+      }
+      gg = __builtin_fmaf(gv[i], gv[i], gg);
+    }
+    gg = wave_reduce(gg);
+    if (lane == 63) *sh.s_gg = gg;
+  }
+  lds_barrier();
+  if (*sh.s_abort) return false;
+
+  // ------- phase B (data waves): this block's rows of y = M g; (sync wave) the gate piece -------
+  float pb = 0.f;
+  if (!is_sync) {
+    if (g.mf) {
+      switch (g.cprk / 4) {  // 32-column steps per row: k / 32
+        case 4: mfma_rows<4>(g, cur, sh, wave, lane); break;
+        case 8: mfma_rows<8>(g, cur, sh, wave, lane); break;
+        default: mfma_rows<16>(g, cur, sh, wave, lane); break;
+      }
+    } else {
+      row_sums_lds<T>(g, cur, sh, wave, lane);
+    }
+    if (g.m_rows < g.nrows) row_sums_hbm<T>(L, g, sh, wave, lane);
+  } else {
+    // p_b = sum_j g_j ((V^T V - I) g)_j over the owned columns; chunk c covers row c / cpk4,
+    // columns 4 (c mod cpk4) .. + 3
+    float pp = 0.f;
+    if (g.d_n > 0) {
+      for (int c = lane; c < g.nd; c += 64) {
+        const int jl = c / g.cpk4, cc = c & (g.cpk4 - 1);
+        float gjl = gj_own[0];
+#pragma unroll
+        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
+        const u32x4 dv = cur[g.d_off + c];
+        pp += dot_f32x4_lds(dv, sh.gsh + cc * 4, 0.f) * gjl;
+      }
+    } else {
+      for (int c = lane; c < g.nd; c += 64) {
+        const int jl = c / g.cpk4, cc = c & (g.cpk4 - 1);
+        float gjl = gj_own[0];
+#pragma unroll
+        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
+        const u32x4 dv = ldg((g4p)L.Dl, (long long)(b + (long long)jl * P) * g.cpk4 + cc);
+        pp += dot_f32x4_lds(dv, sh.gsh + cc * 4, 0.f) * gjl;
+      }
+    }
+    pp = wave_reduce(pp);
+    pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 63));
+  }
+  lds_barrier();
+  // ---- the sync wave stores this block's rows of y, then posts its E2 word (site done) ----
+  if (is_sync) {
+    T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off + g.r0;
+    for (int r = lane; r < g.nrows; r += 64) yrow[r] = from_f32<T>(sh.ypart[r]);
+    if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, pb));
+  }
+  lds_barrier();  // the y rows and the E2 word are issued ahead of the loads below
+  if (!is_sync) {
+    // the next input row streams in while E2 resolves
+    if (has_next) load_x<T, XR>(reinterpret_cast<const T*>(p.X) + (long long)tn * p.x_ld + Ln.x_off, gn, tid, xw);
+    wait_vmcnt<0>();  // the next region and input row are complete before the barrier below
+  } else {
+    // ---------------- E2: all-gather the pieces, resolve the gate ----------------
+    float pv[kMaxBlocks / 64];
+    const bool ok = gather(p, base, p.box_p + (long long)rep * kMaxBlocks, P, tag_p, lane, pv);
+    if (!ok && lane == 0) *sh.s_abort = 1;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks / 64; ++i) ps += pv[i];
+    ps = wave_reduce(ps);
+    if (lane == 63) {
+      const float nx2 = *sh.s_nx2;
+      const float nr2 = (nx2 - *sh.s_gg) + ps;
+      const float thr = p.eps * p.eps;
+      const float rhs = thr * nx2;
+      const int slow = (nr2 < rhs) ? 0 : 1;
+      *sh.s_gate = slow;
+      if (b == 0) {
+        const long long o = (long long)t * p.gate_ld + p.site0 + s;
+        p.gates[o] = (uint8_t)slow;
+        if (p.rho) p.rho[o] = sqrtf(fmaxf(nr2, 0.f) / nx2);
+      }
+    }
+    wait_vmcnt<0>();  // this block's fast-path rows of y are written before a slow path rewrites them
+  }
+  lds_barrier();
+  if (*sh.s_abort) return false;
+
+  // ---------------- slow path: y = W x for the owned rows, then E3 ----------------
+  if (*sh.s_gate) {
+    if (!is_sync) {
+      // one wave per row; each lane keeps kSlowBatch chunk pairs in flight per batch
+      const g4p x4 = (g4p)x;
+      T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off;
+      for (int r = g.r0 + wave; r < g.r0 + g.nrows; r += kDataThreads / 64) {
+        const g4p wr = (g4p)L.W + (long long)r * g.cprd;
+        float a = 0.f;
+        for (int c0 = 0; c0 < g.cprd; c0 += kSlowBatch * 64) {
+          u32x4 wv[kSlowBatch], xv[kSlowBatch];
+#pragma unroll
+          for (int i = 0; i < kSlowBatch; ++i) {
+            const int c = c0 + lane + 64 * i;
+            const int cc = c < g.cprd ? c : 0;
+            wv[i] = wr[cc];
+            xv[i] = x4[cc];
+          }
+#pragma unroll
+          for (int i = 0; i < kSlowBatch; ++i) {
+            const float v = dot16<T>(wv[i], xv[i], 0.f);
+            a += (c0 + lane + 64 * i < g.cprd) ? v : 0.f;
+          }
+        }
+        a = wave_reduce(a);
+        if (lane == 63) yrow[r] = from_f32<T>(a);
+      }
+    }
+    __syncthreads();
+    if (is_sync) {
+      if (lane < kReplicas) st_dev(p.box_f + (long long)lane * kMaxBlocks + b, pack(tag_f, 0.f));
+      float fv[kMaxBlocks / 64];
+      if (!gather(p, base, p.box_f + (long long)rep * kMaxBlocks, P, tag_f, lane, fv) && lane == 0) *sh.s_abort = 1;
+    }
+    __syncthreads();
+    if (*sh.s_abort) return false;
+  }
+  return true;
+}
+
+template <typename T, int XR>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+  __shared__ u32x4 region0[kRegionChunks];
+  __shared__ u32x4 region1[kRegionChunks];
   __shared__ float gsh[kMaxK];
+  __shared__ u32x4 gb[kGbChunks];
+  __shared__ float ypart[kYPart];
   __shared__ float red[kDecodeThreads / 64][kMaxJ + 2];
-  __shared__ float ypart[256];
   __shared__ float s_nx2, s_gg;
   __shared__ int s_gate, s_abort;
   __shared__ unsigned s_base;
@@ -281,257 +733,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
   const unsigned rep = xcc_id() % kReplicas;
-  const LayerDesc* tab = p.sites;
   const u32x4* dummy = reinterpret_cast<const u32x4*>(p.hdr);
+  const Shared sh{gsh, (lu32x4*)gb, ypart, red, &s_nx2, &s_gg, &s_gate, &s_abort};
+  lu32x4* const r0 = (lu32x4*)region0;
+  lu32x4* const r1 = (lu32x4*)region1;
 
   if (tid == 0) {
+    gb[kGbZero] = u32x4{0u, 0u, 0u, 0u};
     s_abort = 0;
     s_base = __hip_atomic_load(&p.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  const unsigned base = s_base;
   const long long Q = (long long)p.n_tokens * p.n_sites;
 
-  Window<JR, XR, MR> w;
-  u32x4 sdl[kSyncDRegs];
-  if (Q > 0) {
-    const LayerDesc L0 = load_desc(tab, 0);
+  u32x4 xw[XR];
+  if (Q > 0 && !is_sync) {  // site 0's region and input row
+    const LayerDesc L0 = load_desc(p.sites, 0);
     const SiteGeom g0 = geom<T>(L0, b, P);
-    if (!is_sync) {
-      prefetch_proj<T>(L0, g0, reinterpret_cast<const T*>(p.X) + L0.x_off, b, P, tid, dummy, w);
-      prefetch_image<T>(L0, g0, b, P, tid, dummy, w);
-    } else {
-      prefetch_sync_delta(L0, g0, b, P, lane, dummy, sdl);
-    }
+    load_x<T, XR>(reinterpret_cast<const T*>(p.X) + L0.x_off, g0, tid, xw);
+    fill_region<T>(L0, g0, b, P, wave, lane, 0, g0.n_inst, (lu32x4*)region0, dummy);
+    wait_vmcnt<0>();
   }
+  __syncthreads();
+  const unsigned base = s_base;
 
-  for (long long q = 0; q < Q; ++q) {
-    const int t = (int)(q / p.n_sites), s = (int)(q - (long long)t * p.n_sites);
-    const LayerDesc L = load_desc(tab, s);
-    const SiteGeom g = geom<T>(L, b, P);
-    const unsigned tag = base + (unsigned)(q * 4);
-    const unsigned tag_g = tag + 1, tag_p = tag + 2, tag_f = tag + 3;
-    const T* x = reinterpret_cast<const T*>(p.X) + (long long)t * p.x_ld + L.x_off;
-
-    // ---------------- phase A: g_j for owned columns and |x|^2, from the window ----------------
-    if (!is_sync) {
-      float acc[kMaxJ];
-#pragma unroll
-      for (int j = 0; j < kMaxJ; ++j) acc[j] = 0.f;
-#pragma unroll
-      for (int jl = 0; jl < JR; ++jl)
-#pragma unroll
-        for (int u = 0; u < XR; ++u) {
-          const int cc = tid + u * kDataThreads;
-          const float part = dot_chunk<T>(w.v[jl][u], w.x[u], 0.f);
-          acc[jl] += (jl < g.nJ && cc < g.cprd) ? part : 0.f;
-        }
-      float sx = 0.f;
-#pragma unroll
-      for (int u = 0; u < XR; ++u) {
-        const float v = sq_chunk<T>(w.x[u], 0.f);
-        sx += (tid + u * kDataThreads < g.cprd) ? v : 0.f;
-      }
-      // inputs longer than the window (d beyond XR * 256 chunks, or more columns than JR)
-      if (g.nx > XR || g.nJ > JR) {
-        const g4p x4 = (g4p)x;
-        for (int cc = tid + XR * kDataThreads; cc < g.cprd; cc += kDataThreads) sx = sq_chunk<T>(ldg(x4, cc), sx);
-        for (int jl = 0; jl < g.nJ; ++jl) {
-          const long long j = b + (long long)jl * P;
-          const g4p vr = (g4p)L.Vt + j * g.cprd;
-          float a = 0.f;
-          for (int cc = tid + (jl < JR ? XR : 0) * kDataThreads; cc < g.cprd; cc += kDataThreads)
-            a = dot_chunk<T>(ldg(vr, cc), ldg(x4, cc), a);
-#pragma unroll
-          for (int jj = 0; jj < kMaxJ; ++jj) acc[jj] += (jj == jl) ? a : 0.f;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxJ; ++j) acc[j] = wave_reduce(acc[j]);
-      sx = wave_reduce(sx);
-      if (lane == 63) {
-#pragma unroll
-        for (int j = 0; j < kMaxJ; ++j) red[wave][j] = acc[j];
-        red[wave][kMaxJ] = sx;
-      }
-    }
-    __syncthreads();
-    // ---- E1 (sync wave): publish this block's g_j, all-gather g, then the gate piece p_b ----
-    // The sync wave computes p_b = sum_j g_j ((V^T V - I) g)_j from its own prefetched rows of
-    // V^T V - I and publishes it before releasing the data waves, so E2 runs concurrently with
-    // phase B and the store is queued ahead of the data waves' next prefetch. Lane r < kReplicas
-    // writes mailbox copy r.
-    if (is_sync) {
-      const float nx2 = ((red[0][kMaxJ] + red[1][kMaxJ]) + red[2][kMaxJ]) + red[3][kMaxJ];
-      float gj_own[kMaxJ];
-#pragma unroll
-      for (int jl = 0; jl < kMaxJ; ++jl) gj_own[jl] = ((red[0][jl] + red[1][jl]) + red[2][jl]) + red[3][jl];
-      for (int jl = 0; jl < g.nJ; ++jl) {
-        const long long j = b + (long long)jl * P;
-        if (lane < kReplicas) st_dev(p.box_g + (long long)lane * kMaxK + j, pack(tag_g, gj_own[jl]));
-      }
-      if (lane == 0) s_nx2 = nx2;
-      float gv[kMaxK / 64];
-      const bool ok = gather(p, base, p.box_g + (long long)rep * kMaxK, L.k, tag_g, lane, gv);
-      if (!ok && lane == 0) s_abort = 1;
-      float gg = 0.f;
-#pragma unroll
-      for (int i = 0; i < kMaxK / 64; ++i) {
-        const int j = lane + 64 * i;
-        if (j < L.k) gsh[j] = gv[i];
-        gg = __builtin_fmaf(gv[i], gv[i], gg);
-      }
-      gg = wave_reduce(gg);
-      // p_b from the prefetched rows: chunk c = lane + 64 u covers row jl = c / (k/4), columns
-      // 4 (c mod k/4) .. + 3; g is read back from LDS (written above by this wave, in order)
-      const int cpk4 = L.k / 4;
-      float pp = 0.f;
-#pragma unroll
-      for (int u = 0; u < kSyncDRegs; ++u) {
-        const int c = lane + 64 * u;
-        const bool okc = c < g.nd;
-        const int jl = okc ? c / cpk4 : 0, cc = okc ? c - jl * cpk4 : 0;
-        float gjl = gj_own[0];
-#pragma unroll
-        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
-        const float v = dot_f32x4_lds(sdl[u], gsh + cc * 4, 0.f) * gjl;
-        pp += okc ? v : 0.f;
-      }
-      for (int c = lane + 64 * kSyncDRegs; c < g.nd; c += 64) {  // rows beyond the sync window
-        const int jl = c / cpk4, cc = c - jl * cpk4;
-        const long long j = b + (long long)jl * P;
-        float gjl = gj_own[0];
-#pragma unroll
-        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
-        pp += dot_f32x4_lds(ldg((g4p)L.Dl, j * cpk4 + cc), gsh + cc * 4, 0.f) * gjl;
-      }
-      pp = wave_reduce(pp);
-      const float pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 63));
-      if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, pb));
-      if (lane == 63) s_gg = gg;
-    }
-    __syncthreads();
-    if (s_abort) break;
-
-    const bool has_next = q + 1 < Q;
-    const long long qn = q + 1;
-    const int tn = (int)(qn / p.n_sites), sn = (int)(qn - (long long)tn * p.n_sites);
-    const LayerDesc Ln = load_desc(tab, has_next ? sn : s);
-    const SiteGeom gn = geom<T>(Ln, b, P);
-    if (!is_sync) {
-      // ------- phase B (data waves): y = M g for the owned rows, while E2 runs -------
-      // the next site's V^T rows and input row stream in now (phase A consumed those slots)
-      if (has_next)
-        prefetch_proj<T>(Ln, gn, reinterpret_cast<const T*>(p.X) + (long long)tn * p.x_ld + Ln.x_off, b, P, tid,
-                         dummy, w);
-      // The block's M slice is nrows * cprk contiguous chunks; chunk c = tid + 256 u belongs to
-      // row c / cprk. Rows are reduced inside lane groups of width min(cprk, 64) and, for
-      // cprk > 64, across groups through LDS in index order.
-      const int gw = min(g.cprk, 64);
-      const int segs = g.cprk / gw;
-      T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off + g.r0;
-#pragma unroll
-      for (int u = 0; u < MR; ++u) {
-        const int c = tid + u * kDataThreads;
-        if (u * kDataThreads < g.nm) {  // uniform across the block
-          const bool ok = c < g.nm;
-          const int cm = ok ? c : 0;
-          float v = dot_chunk_lds<T>(w.m[u], gsh + (cm % g.cprk) * VW, 0.f);
-          v = group_reduce(ok ? v : 0.f, gw);
-          if (ok && (c % gw) == gw - 1) {
-            if (segs == 1) yrow[c / g.cprk] = from_f32<T>(v);
-            else ypart[c / gw] = v;
-          }
-        }
-      }
-      for (int c0 = MR * kDataThreads; c0 < g.nm; c0 += kDataThreads) {  // slices beyond the window
-        const int c = tid + c0;
-        const bool ok = c < g.nm;
-        const int cm = ok ? c : 0;
-        float v = dot_chunk_lds<T>(ldg((g4p)L.M, (long long)g.r0 * g.cprk + cm), gsh + (cm % g.cprk) * VW, 0.f);
-        v = group_reduce(ok ? v : 0.f, gw);
-        if (ok && (c % gw) == gw - 1) {
-          if (segs == 1) yrow[c / g.cprk] = from_f32<T>(v);
-          else ypart[c / gw] = v;
-        }
-      }
-      // the next site's M rows stream in while the gate is being resolved
-      if (has_next) prefetch_image<T>(Ln, gn, b, P, tid, dummy, w);
-    } else {
-      // ---------------- E2 (sync wave): all-gather the pieces, resolve the gate ----------------
-      float pv[kMaxBlocks / 64];
-      const bool ok = gather(p, base, p.box_p + (long long)rep * kMaxBlocks, P, tag_p, lane, pv);
-      if (!ok && lane == 0) s_abort = 1;
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < kMaxBlocks / 64; ++i) ps += pv[i];
-      ps = wave_reduce(ps);
-      if (lane == 63) {
-        const float nx2 = s_nx2;
-        const float nr2 = (nx2 - s_gg) + ps;
-        const float thr = p.eps * p.eps;
-        const float rhs = thr * nx2;
-        const int slow = (nr2 < rhs) ? 0 : 1;
-        s_gate = slow;
-        if (b == 0) {
-          const long long o = (long long)t * p.gate_ld + p.site0 + s;
-          p.gates[o] = (uint8_t)slow;
-          if (p.rho) p.rho[o] = sqrtf(fmaxf(nr2, 0.f) / nx2);
-        }
-      }
-      // prefetch the next site's rows of V^T V - I for the next p_b
-      if (has_next) prefetch_sync_delta(Ln, gn, b, P, lane, dummy, sdl);
-    }
-    __syncthreads();
-    if (s_abort) break;
-    if (!is_sync && g.cprk / min(g.cprk, 64) > 1) {  // rows split over several lane groups
-      const int segs = g.cprk / min(g.cprk, 64);
-      T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off + g.r0;
-      for (int r = tid; r < g.nrows; r += kDataThreads) {
-        float v = 0.f;
-        for (int sg = 0; sg < segs; ++sg) v += ypart[r * segs + sg];
-        yrow[r] = from_f32<T>(v);
-      }
-    }
-
-    // ---------------- slow path: y = W x for the owned rows, then E3 ----------------
-    if (s_gate) {
-      if (!is_sync) {
-        // one wave per row; each lane keeps kSlowBatch chunk pairs in flight per batch
-        const g4p x4 = (g4p)x;
-        T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off;
-        for (int r = g.r0 + wave; r < g.r0 + g.nrows; r += kDataThreads / 64) {
-          const g4p wr = (g4p)L.W + (long long)r * g.cprd;
-          float a = 0.f;
-          for (int c0 = 0; c0 < g.cprd; c0 += kSlowBatch * 64) {
-            u32x4 wv[kSlowBatch], xv[kSlowBatch];
-#pragma unroll
-            for (int i = 0; i < kSlowBatch; ++i) {
-              const int c = c0 + lane + 64 * i;
-              const int cc = c < g.cprd ? c : 0;
-              wv[i] = wr[cc];
-              xv[i] = x4[cc];
-            }
-#pragma unroll
-            for (int i = 0; i < kSlowBatch; ++i) {
-              const float v = dot_chunk<T>(wv[i], xv[i], 0.f);
-              a += (c0 + lane + 64 * i < g.cprd) ? v : 0.f;
-            }
-          }
-          a = wave_reduce(a);
-          if (lane == 63) yrow[r] = from_f32<T>(a);
-        }
-      }
-      __syncthreads();
-      if (is_sync) {
-        if (lane < kReplicas) st_dev(p.box_f + (long long)lane * kMaxBlocks + b, pack(tag_f, 0.f));
-        float fv[kMaxBlocks / 64];
-        if (!gather(p, base, p.box_f + (long long)rep * kMaxBlocks, P, tag_f, lane, fv) && lane == 0) s_abort = 1;
-      }
-      __syncthreads();
-      if (s_abort) break;
-    }
+  for (long long q = 0; q < Q; q += 2) {
+    if (!site_step<T, XR>(p, q, Q, base, b, P, tid, rep, dummy, r0, r1, xw, sh)) break;
+    if (q + 1 < Q && !site_step<T, XR>(p, q + 1, Q, base, b, P, tid, rep, dummy, r1, r0, xw, sh)) break;
   }
+  if (!is_sync) wait_vmcnt<0>();  // no copy into LDS outlives the block
   // advance the tag base for the next launch (also after an abort, so its mark goes stale)
   if (b == 0 && tid == 0)
     __hip_atomic_store(&p.hdr->epoch, base + (unsigned)(Q * 4) + 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -541,24 +770,18 @@ size_t decode_ws_bytes() {
   return sizeof(WsHeader) + (size_t)kReplicas * kMaxK * 8 + 2 * (size_t)kReplicas * kMaxBlocks * 8;
 }
 
-// Instantiated register windows: JR columns, XR input chunks per thread (XR * 256 chunks of 16
-// bytes cover the input row), MR M chunks per thread. Larger sites fall back to streaming loops.
-template <typename T, int XR>
-static const void* pick_jm(int jr, int mr) {
-  if (jr <= 1 && mr <= 8) return (const void*)decode_kernel<T, 1, XR, 8>;
-  if (jr <= 2) return (const void*)decode_kernel<T, 2, XR, 16>;
-  return (const void*)decode_kernel<T, 4, XR, 16>;
-}
+// Instantiated input windows: XR chunks of 16 bytes per data thread (XR * 256 chunks cover the
+// input row); longer rows are finished by a streaming loop.
 template <typename T>
-static const void* pick(int jr, int xr, int mr) {
-  return xr <= 2 ? pick_jm<T, 2>(jr, mr) : pick_jm<T, 8>(jr, mr);
+static const void* pick(int xr) {
+  return xr <= 2 ? (const void*)decode_kernel<T, 2> : (const void*)decode_kernel<T, 8>;
 }
 
-static const void* decode_fn(int dtype, int jr, int xr, int mr) {
+static const void* decode_fn(int dtype, int xr) {
   switch (dtype) {
-    case GSI_F32: return pick<float>(jr, xr, mr);
-    case GSI_F16: return pick<f16_t>(jr, xr, mr);
-    case GSI_BF16: return pick<bf16_t>(jr, xr, mr);
+    case GSI_F32: return pick<float>(xr);
+    case GSI_F16: return pick<f16_t>(xr);
+    case GSI_BF16: return pick<bf16_t>(xr);
   }
   return nullptr;
 }
@@ -573,38 +796,18 @@ static int grid_blocks(const void* fn) {
 }
 
 int launch_decode(int dtype, const DecodeParams& prm, const LayerDesc* host_sites, hipStream_t s) {
-  // size the register windows for the largest site at the full grid
   const int es = dtype == GSI_F32 ? 4 : 2;
   int need_x = 1;
   for (int i = 0; i < prm.n_sites; ++i)
     need_x = std::max(need_x, (host_sites[i].d * es / 16 + kDataThreads - 1) / kDataThreads);
-  const int xr = need_x <= 2 ? 2 : 8;
-  int jr = 1, mr = 8;
-  for (int pass = 0; pass < 2; ++pass) {
-    const void* fn = decode_fn(dtype, jr, xr, mr);
-    if (!fn) return GSI_ERR_DTYPE;
-    const int P = grid_blocks(fn);
-    if (P < kMaxK / kMaxJ) return GSI_ERR_DEVICE;
-    int need_j = 1, need_m = 1;
-    for (int i = 0; i < prm.n_sites; ++i) {
-      const LayerDesc& L = host_sites[i];
-      need_j = std::max(need_j, (L.k + P - 1) / P);
-      const int rpb = (L.d_out + P - 1) / P;
-      const int cprk = L.k * es / 16;
-      need_m = std::max(need_m, (rpb * cprk + kDataThreads - 1) / kDataThreads);
-    }
-    const int jr2 = (need_j <= 1 && need_m <= 8) ? 1 : need_j <= 2 ? 2 : 4;
-    const int mr2 = jr2 == 1 ? 8 : 16;
-    if (jr2 == jr && mr2 == mr) {
-      DecodeParams p = prm;
-      void* args[] = {&p};
-      hipError_t e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(kDecodeThreads), args, 0, s);
-      return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
-    }
-    jr = jr2;
-    mr = mr2;
-  }
-  return GSI_ERR_DEVICE;
+  const void* fn = decode_fn(dtype, need_x);
+  if (!fn) return GSI_ERR_DTYPE;
+  const int P = grid_blocks(fn);
+  if (P < kMinBlocks) return GSI_ERR_DEVICE;
+  DecodeParams p = prm;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(kDecodeThreads), args, 0, s);
+  return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 }  // namespace gsi

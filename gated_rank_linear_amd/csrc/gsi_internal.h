@@ -116,6 +116,9 @@ constexpr int kMaxK = 512;
 constexpr int kDataThreads = 256;  // 4 data waves
 constexpr int kSyncThreads = 64;   // 1 sync wave
 constexpr int kDecodeThreads = kDataThreads + kSyncThreads;
+constexpr int kRegionChunks = 4096;  // 16-byte chunks per LDS site region (two regions, 64 KB each)
+constexpr int kYPart = 2048;         // rows of y per block held in LDS before they are stored
+constexpr int kMinBlocks = kMaxK / 4;  // the decode grid needs at least this many blocks
 
 struct DecodeParams {
   const LayerDesc* sites;  // device table of n_sites descriptors

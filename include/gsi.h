@@ -24,7 +24,8 @@
  *      rho  [T] float32 (optional, may be NULL): sqrt(|r|^2 / |x|^2), NaN when x = 0.
  *  - dtype is one of GSI_F32, GSI_F16, GSI_BF16 and applies to W, V, M, x and y alike. All
  *    accumulation is float32. g is kept in float32.
- *  - d and k must be multiples of 8; 1 <= k <= min(d, 512); d <= 65536; d_out >= 1.
+ *  - d must be a multiple of 8 with 8 <= d <= 65536; k must be a power of two with
+ *    8 <= k <= min(d, 512); 1 <= d_out <= 262144.
  *    Device pointers must be 16-byte aligned.
  *  - The gate is evaluated in float32 as  nr2 < fl(fl(eps*eps) * nx2),  with nx2 = |x|^2 and
  *    nr2 = |x - V g|^2 of the *stored* V (formed exactly through the identity

@@ -39,6 +39,7 @@ def test_status_strings():
     (2, 12288, 4096, 256, True), (2, 4096, 16384, 256, True), (0, 768, 768, 64, True), (1, 2304, 768, 256, True),
     (2, 4096, 4096, 512, True), (3, 16, 16, 8, False), (2, 0, 16, 8, False), (2, 16, 12, 8, False),
     (2, 16, 16, 24, False), (2, 16, 16, 32, False), (2, 16, 4096, 1024, False), (2, 16, 16, 4, False),
+    (2, 262144, 16, 8, True), (2, 262145, 16, 8, False), (0, 262144, 512, 512, True), (0, 262145, 512, 512, False),
 ])
 def test_aux_and_workspace_sizes(dtype, d_out, d, k, ok):
     a = lib.gsi_layer_aux_bytes(dtype, d_out, d, k)
