@@ -86,6 +86,152 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const void* __restrict__ A
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// NT GEMM on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}), float32 accumulation:
+// C[m, n] = sum_i A[ra(m), i] * B[n, i], both operands K-contiguous. 64x64 output tile per block
+// of 4 waves (2 x 2, 32x32 each: 2 x 2 tiles of 16x16). Per 32-column step, lane l of a wave
+// holds, for each of its 16-row tiles, 8 consecutive K elements of row l mod 16 starting at
+// 8 (l / 16) (the A operand layout), and the same for its B tiles; fragments are loaded straight
+// from global memory one step ahead of their use. Rows past m (or the device count) and K past
+// kdim read a valid location and are zeroed. A float32 A (with bf16 B) is split into bf16 high
+// and low parts, each multiplied exactly: |a - hi - lo| <= 2^-18 |a|.
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mf16x8 __attribute__((ext_vector_type(8)));
+typedef float mf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int mu32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct mfma_op;
+template <> struct mfma_op<bf16_t> {
+  static __device__ __forceinline__ mf32x4 run(mu32x4 a, mu32x4 b, mf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8, a), __builtin_bit_cast(mbf16x8, b), c, 0,
+                                                  0, 0);
+  }
+};
+template <> struct mfma_op<f16_t> {
+  static __device__ __forceinline__ mf32x4 run(mu32x4 a, mu32x4 b, mf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8, a), __builtin_bit_cast(mf16x8, b), c, 0,
+                                                 0, 0);
+  }
+};
+
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restrict__ A, long long lda,
+                                                           const int* __restrict__ a_idx, const void* __restrict__ B,
+                                                           long long ldb, void* __restrict__ C, long long ldc,
+                                                           const int* __restrict__ c_idx, int m, int n, int kdim,
+                                                           const int* __restrict__ m_count, int sub_identity) {
+  constexpr bool kSplit = sizeof(TA) == 4;  // float32 A against bf16 B
+  const int mv = m_count ? min(m, *m_count) : m;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (m0 >= mv) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, kq = lane >> 4;
+  // rows of A (through the gather list) and of B used by this lane; invalid ones read row 0
+  long long arow[2], brow[2];
+  bool aok[2], bok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int mm = m0 + wm * 32 + i * 16 + r16;
+    aok[i] = mm < mv;
+    arow[i] = aok[i] ? (long long)(a_idx ? a_idx[mm] : mm) * lda : 0;
+    const int nn = n0 + wn * 32 + i * 16 + r16;
+    bok[i] = nn < n;
+    brow[i] = bok[i] ? (long long)nn * ldb : 0;
+  }
+  mf32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_step = [&](int k0, mu32x4 (&ah)[2], mu32x4 (&al)[2], mu32x4 (&bv)[2]) {
+    const int kk = k0 + kq * 8;
+    const bool kin = kk < kdim;  // kdim is a multiple of 8, so a chunk is all in or all out
+    const int kc = kin ? kk : 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (kSplit) {
+        const float* pa = reinterpret_cast<const float*>(A) + arow[i] + kc;
+        const mf32x4 f0 = reinterpret_cast<const mf32x4*>(pa)[0];
+        const mf32x4 f1 = reinterpret_cast<const mf32x4*>(pa)[1];
+        const bool ok = aok[i] && kin;
+        float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        unsigned short h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = ok ? f[e] : 0.f;
+          const bf16_t hb = from_f32<bf16_t>(v);
+          const bf16_t lb = from_f32<bf16_t>(v - to_f32(hb));
+          h[e] = hb.b;
+          l[e] = lb.b;
+        }
+        ah[i] = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
+                       h[6] | ((unsigned)h[7] << 16)};
+        al[i] = mu32x4{l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16), l[4] | ((unsigned)l[5] << 16),
+                       l[6] | ((unsigned)l[7] << 16)};
+      } else {
+        const mu32x4 v = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TA*>(A) + arow[i] + kc)[0];
+        const bool ok = aok[i] && kin;
+        ah[i] = ok ? v : mu32x4{0u, 0u, 0u, 0u};
+        al[i] = mu32x4{0u, 0u, 0u, 0u};
+      }
+      const mu32x4 w = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TB*>(B) + brow[i] + kc)[0];
+      bv[i] = (bok[i] && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  mu32x4 ah[2], al[2], bv[2];
+  load_step(0, ah, al, bv);
+  const int k_last = (kdim - 1) / 32 * 32;
+  for (int k0 = 0; k0 < kdim; k0 += 32) {
+    // the next step's fragments (the last step reloads itself), loaded unconditionally
+    mu32x4 nah[2], nal[2], nbv[2];
+    load_step(min(k0 + 32, k_last), nah, nal, nbv);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma_op<TB>::run(ah[i], bv[j], acc[i][j]);
+        if constexpr (kSplit) acc[i][j] = mfma_op<TB>::run(al[i], bv[j], acc[i][j]);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ah[i] = nah[i];
+      al[i] = nal[i];
+      bv[i] = nbv[i];
+    }
+  }
+  // D of a 16x16 tile: lane l holds column l mod 16, rows 4 (l / 16) .. + 3
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m0 + wm * 32 + i * 16 + 4 * kq + r;
+      if (mm >= mv) continue;
+      const long long crow = c_idx ? c_idx[mm] : mm;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nn = n0 + wn * 32 + j * 16 + r16;
+        if (nn >= n) continue;
+        float v = acc[i][j][r];
+        if (sub_identity && mm == nn) v -= 1.0f;
+        st_from_f32<TC>(C, crow * ldc + nn, v);
+      }
+    }
+}
+
+template <typename TA, typename TB>
+static void* pick_mfma_c(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)gemm_nt_mfma_kernel<TA, TB, float>;
+    case GSI_F16: return (void*)gemm_nt_mfma_kernel<TA, TB, f16_t>;
+    case GSI_BF16: return (void*)gemm_nt_mfma_kernel<TA, TB, bf16_t>;
+  }
+  return nullptr;
+}
+
 template <typename TA, typename TB>
 static void* pick_c(int c_type) {
   switch (c_type) {
@@ -110,6 +256,18 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
                    const int* m_count, int sub_identity, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
   void* fn = nullptr;
+  // matrix cores for 16-bit operands of one type (float32 A with bf16 B through the bf16 split);
+  // the vector-ALU kernel for the rest. Operand rows must start on 16 bytes (d and k are
+  // multiples of 8 elements).
+  if (a_type == GSI_BF16 && b_type == GSI_BF16) fn = pick_mfma_c<bf16_t, bf16_t>(c_type);
+  else if (a_type == GSI_F16 && b_type == GSI_F16) fn = pick_mfma_c<f16_t, f16_t>(c_type);
+  else if (a_type == GSI_F32 && b_type == GSI_BF16) fn = pick_mfma_c<float, bf16_t>(c_type);
+  if (fn) {
+    dim3 grid((n + 63) / 64, (m + 63) / 64);
+    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   switch (a_type) {
     case GSI_F32: fn = pick_b<float>(b_type, c_type); break;
     case GSI_F16: fn = pick_b<f16_t>(b_type, c_type); break;
