@@ -210,31 +210,34 @@ template <> struct is_bf16<bf16_t> { static constexpr bool v = true; };
 template <typename T>
 __device__ __forceinline__ SiteGeom geom(const LayerDesc& L, int b, int P) {
   constexpr int VW = vec16<T>::N;
+  const int sh_P = __builtin_ctz(P);  // the grid is a power of two
   SiteGeom g;
-  g.nJ = b < L.k ? (L.k - 1 - b) / P + 1 : 0;
+  g.nJ = b < L.k ? ((L.k - 1 - b) >> sh_P) + 1 : 0;
   g.cprd = L.d / VW;
   g.nx = (g.cprd + kDataThreads - 1) / kDataThreads;
   g.cprk = L.k / VW;
   g.cpk4 = L.k / 4;
-  const int rpb = (L.d_out + P - 1) / P;
+  const int rpb = (L.d_out + P - 1) >> sh_P;
   g.r0 = min(L.d_out, b * rpb);
   g.nrows = min(L.d_out, g.r0 + rpb) - g.r0;
   g.nm = g.nrows * g.cprk;
   g.nd = g.nJ * g.cpk4;
-  g.vj = min(g.nJ, kRegionChunks / g.cprd);
+  g.vj = g.nJ;  // V^T rows that fit the region (at most kMaxJ: compares, no division)
+#pragma unroll
+  for (int r = kMaxJ; r >= 1; --r) g.vj = (g.vj >= r && r * g.cprd > kRegionChunks) ? r - 1 : g.vj;
   g.v_n = g.vj * g.cprd;
   g.d_off = align64(g.v_n);
   g.d_n = g.d_off + g.nd <= kRegionChunks ? g.nd : 0;
   g.m_off = align64(g.d_off + g.d_n);
   g.mf = is_bf16<T>::v && L.k >= 128;
+  const int sh_cprk = __builtin_ctz(g.cprk);  // k / VW is a power of two
   if (g.mf) {
-    const int tile = 16 * g.cprk;  // chunks per 16-row tile
-    const int tiles = min((g.nrows + 15) / 16, max(0, (kRegionChunks - g.m_off) / tile));
-    g.m_n = tiles * tile;
+    const int tiles = min((g.nrows + 15) / 16, max(0, kRegionChunks - g.m_off) >> (sh_cprk + 4));  // 16 cprk a tile
+    g.m_n = tiles << (sh_cprk + 4);
     g.m_rows = min(g.nrows, tiles * 16);
   } else {
     g.m_n = g.m_off + g.nm <= kRegionChunks ? g.nm : max(0, (kRegionChunks - g.m_off) / kDataThreads * kDataThreads);
-    g.m_rows = g.m_n / g.cprk;
+    g.m_rows = g.m_n >> sh_cprk;
   }
   g.n_inst = (g.m_off + g.m_n + 63) / 64;
   return g;
@@ -251,28 +254,34 @@ __device__ __forceinline__ void fill_region(const LayerDesc& L, const SiteGeom& 
   const char* vt = reinterpret_cast<const char*>(L.Vt);
   const char* dl = reinterpret_cast<const char*>(L.Dl);
   const char* mp = reinterpret_cast<const char*>(L.M) + (long long)g.r0 * g.cprk * 16;
+  // k, k / 4, k / 32 and k / VW are powers of two: shifts instead of divisions
+  const int sh_cpk4 = __builtin_ctz(g.cpk4);
+  const int sh_kt = g.mf ? __builtin_ctz(g.cprk / 4) : 0;
   for (int i = i0 + ((wave - i0) & 3); i < i1; i += 4) {
     const int c = i * 64 + lane;
     const char* src = reinterpret_cast<const char*>(dummy);
-    if (c < g.v_n) {
-      const int jl = c / g.cprd, cc = c - jl * g.cprd;
+    if (c < g.v_n) {  // V^T row jl = c / cprd (at most kMaxJ rows: compares, no division)
+      int jl = 0;
+#pragma unroll
+      for (int r = 1; r < kMaxJ; ++r) jl += c >= r * g.cprd ? 1 : 0;
+      const int cc = c - jl * g.cprd;
       src = vt + ((long long)(b + jl * P) * g.cprd + cc) * 16;
     } else if (c >= g.d_off && c < g.d_off + g.d_n) {
       const int e = c - g.d_off;
-      const int jl = e / g.cpk4, cc = e - jl * g.cpk4;
+      const int jl = e >> sh_cpk4, cc = e & (g.cpk4 - 1);
       src = dl + ((long long)(b + jl * P) * g.cpk4 + cc) * 16;
     } else if (c >= g.m_off && c < g.m_off + g.m_n) {
-      if (g.mf) {  // tile (rt, kt) = instruction (i - m_off / 64) in row-tile-major order
-        const int kt = g.cprk / 4;
+      if (g.mf) {  // tile (rt, kk) = instruction (i - m_off / 64) in row-tile-major order
         const int it = i - g.m_off / 64;
-        const int rt = it / kt, kk = it - rt * kt;
+        const int rt = it >> sh_kt, kk = it & ((1 << sh_kt) - 1);
         const int row = rt * 16 + (lane & 15);
         if (row < g.nrows) src = mp + ((long long)row * g.cprk + kk * 4 + (lane >> 4)) * 16;
       } else {
         src = mp + (long long)(c - g.m_off) * 16;
       }
     }
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(region + i * 64), 16, 0, 0);
+    // streamed once per token: non-temporal, so the copy does not displace cached lines
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(region + i * 64), 16, 0, 2 /* nt */);
   }
 }
 
@@ -350,9 +359,9 @@ template <typename T>
 __device__ __forceinline__ RowLanes row_lanes(const SiteGeom& g, int lane) {
   RowLanes q;
   q.CPL = min(4, g.cprk);
-  q.Lr = g.cprk / q.CPL;  // lanes per row (a power of two <= 32)
+  q.Lr = g.cprk >> __builtin_ctz(q.CPL);  // lanes per row (a power of two <= 32)
   q.rpw = 64 / q.Lr;      // rows per wave per pass
-  q.lr = lane / q.Lr;
+  q.lr = lane >> __builtin_ctz(q.Lr);
   q.lc = lane & (q.Lr - 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) q.ch[i] = i < q.CPL ? q.lc + q.Lr * i : 0;
@@ -478,22 +487,21 @@ __device__ __forceinline__ void mfma_rows(const SiteGeom& g, const lu32x4* cur, 
 // One (token, site) step. `cur` holds this site's slices (filled during the previous step);
 // `nxt` receives the next site's. Returns false when the launch was aborted.
 template <typename T, int XR>
-__device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, long long Q, unsigned base, int b, int P,
+__device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, int t, int s, long long Q, unsigned base,
+                                          int b, int P,
                                           int tid, unsigned rep, const u32x4* dummy,
                                           const lu32x4* cur, lu32x4* nxt, u32x4 (&xw)[XR],
                                           const Shared& sh) {
   constexpr int VW = vec16<T>::N;
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
-  const int t = (int)(q / p.n_sites), s = (int)(q - (long long)t * p.n_sites);
   const LayerDesc L = load_desc(p.sites, s);
   const SiteGeom g = geom<T>(L, b, P);
   const unsigned tag = base + (unsigned)(q * 4);
   const unsigned tag_g = tag + 1, tag_p = tag + 2, tag_f = tag + 3;
   const T* x = reinterpret_cast<const T*>(p.X) + (long long)t * p.x_ld + L.x_off;
   const bool has_next = q + 1 < Q;
-  const long long qn = q + 1;
-  const int tn = (int)(qn / p.n_sites), sn = (int)(qn - (long long)tn * p.n_sites);
+  const int sn = s + 1 < p.n_sites ? s + 1 : 0, tn = s + 1 < p.n_sites ? t : t + 1;
   const LayerDesc Ln = load_desc(p.sites, has_next ? sn : s);
   const SiteGeom gn = geom<T>(Ln, b, P);
 
@@ -617,7 +625,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, lo
     float pp = 0.f;
     if (g.d_n > 0) {
       for (int c = lane; c < g.nd; c += 64) {
-        const int jl = c / g.cpk4, cc = c & (g.cpk4 - 1);
+        const int jl = c >> __builtin_ctz(g.cpk4), cc = c & (g.cpk4 - 1);
         float gjl = gj_own[0];
 #pragma unroll
         for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
@@ -626,7 +634,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, lo
       }
     } else {
       for (int c = lane; c < g.nd; c += 64) {
-        const int jl = c / g.cpk4, cc = c & (g.cpk4 - 1);
+        const int jl = c >> __builtin_ctz(g.cpk4), cc = c & (g.cpk4 - 1);
         float gjl = gj_own[0];
 #pragma unroll
         for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
@@ -756,9 +764,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   __syncthreads();
   const unsigned base = s_base;
 
+  int t = 0, s = 0;  // token and site of step q
+  auto advance = [&]() {
+    if (++s == p.n_sites) {
+      s = 0;
+      ++t;
+    }
+  };
   for (long long q = 0; q < Q; q += 2) {
-    if (!site_step<T, XR>(p, q, Q, base, b, P, tid, rep, dummy, r0, r1, xw, sh)) break;
-    if (q + 1 < Q && !site_step<T, XR>(p, q + 1, Q, base, b, P, tid, rep, dummy, r1, r0, xw, sh)) break;
+    if (!site_step<T, XR>(p, q, t, s, Q, base, b, P, tid, rep, dummy, r0, r1, xw, sh)) break;
+    advance();
+    if (q + 1 < Q && !site_step<T, XR>(p, q + 1, t, s, Q, base, b, P, tid, rep, dummy, r1, r0, xw, sh)) break;
+    advance();
   }
   if (!is_sync) wait_vmcnt<0>();  // no copy into LDS outlives the block
   // advance the tag base for the next launch (also after an abort, so its mark goes stale)
@@ -802,7 +819,8 @@ int launch_decode(int dtype, const DecodeParams& prm, const LayerDesc* host_site
     need_x = std::max(need_x, (host_sites[i].d * es / 16 + kDataThreads - 1) / kDataThreads);
   const void* fn = decode_fn(dtype, need_x);
   if (!fn) return GSI_ERR_DTYPE;
-  const int P = grid_blocks(fn);
+  int P = grid_blocks(fn);
+  while (P & (P - 1)) P &= P - 1;  // a power of two: the kernel splits work with shifts
   if (P < kMinBlocks) return GSI_ERR_DEVICE;
   DecodeParams p = prm;
   void* args[] = {&p};
