@@ -50,7 +50,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+    cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,--no-undefined", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libgsi failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -222,6 +222,127 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Matrix-core NT GEMM for 16-bit A and B with K a multiple of 32, staged through LDS: 128x128
+// output tile per block of 4 waves (2 x 2, 64x64 each = 4 x 4 tiles of 16x16). Each 32-column
+// K step is 16 operand blocks of 1 KB (8 of A, 8 of B), copied from global memory straight into
+// LDS (global_load_lds_dwordx4, 4 per wave) in the operand order of v_mfma_f32_16x16x32_*, so a
+// fragment is one conflict-free 16-byte LDS read per lane. Three stages in flight; the stage
+// buffers are separate LDS arrays and the K loop is unrolled by three, so reads of one stage
+// never wait for copies into another. Rows past m (or the device count) and columns past n read
+// row 0 and are not stored.
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void dlds_void;
+typedef mu32x4 __attribute__((address_space(3))) dlu32x4;
+
+template <int N>
+__device__ __forceinline__ void dwait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void dlds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, typename TC>
+__global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __restrict__ A, long long lda,
+                                                               const int* __restrict__ a_idx,
+                                                               const void* __restrict__ B, long long ldb,
+                                                               void* __restrict__ C, long long ldc,
+                                                               const int* __restrict__ c_idx, int m, int n, int kdim,
+                                                               const int* __restrict__ m_count, int sub_identity) {
+  __shared__ mu32x4 st0[16 * 64], st1[16 * 64], st2[16 * 64];  // 3 stages x 16 operand blocks
+  const int mv = m_count ? min(m, *m_count) : m;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  if (m0 >= mv) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // the 4 operand blocks this wave copies per step: blocks wave + 4 u; block q < 8 is A rows
+  // m0 + 16 q .., block q >= 8 is B rows n0 + 16 (q - 8) ..; lane l reads row + (l mod 16),
+  // elements 8 (l / 16) .. + 7 of the step
+  const T* src[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = wave + 4 * u;
+    if (q < 8) {
+      const int mm = m0 + 16 * q + (lane & 15);
+      const long long row = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) : 0;
+      src[u] = reinterpret_cast<const T*>(A) + row * lda + 8 * (lane >> 4);
+    } else {
+      const int nn = n0 + 16 * (q - 8) + (lane & 15);
+      const long long row = nn < n ? nn : 0;
+      src[u] = reinterpret_cast<const T*>(B) + row * ldb + 8 * (lane >> 4);
+    }
+  }
+  mf32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+// the stage arrays are named directly in every copy and read, so the compiler can tell them apart
+#define GSI_ISSUE(STAGE, K0)                                                                           \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) __builtin_amdgcn_global_load_lds(                    \
+        (const void*)(src[u] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + (wave + 4 * u) * 64), 16, 0, 0);              \
+  } while (0)
+#define GSI_COMPUTE(STAGE)                                                                             \
+  do {                                                                                                 \
+    mu32x4 af[4], bf[4];                                                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = ((const dlu32x4*)(STAGE))[(wm * 4 + i) * 64 + lane]; \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[j] = ((const dlu32x4*)(STAGE))[(8 + wn * 4 + j) * 64 + lane]; \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
+  } while (0)
+// every step issues exactly 4 copies per wave (past the last stage they re-read the last K step
+// into a stage nobody reads again), so at step s the copies still outstanding are stage s and
+// stage s + 1, and waiting until at most 4 remain always completes stage s
+#define GSI_STEP(CUR, FUT, ST)                                                                          \
+  do {                                                                                                 \
+    dwait_vmcnt<4>();                                                                                  \
+    dlds_barrier();                                                                                    \
+    GSI_ISSUE(FUT, min((ST) + 2, nk - 1) * 32);                                                        \
+    GSI_COMPUTE(CUR);                                                                                  \
+  } while (0)
+  const int nk = kdim / 32;
+  GSI_ISSUE(st0, 0);
+  GSI_ISSUE(st1, min(1, nk - 1) * 32);
+  int s0 = 0;
+  for (; s0 + 3 <= nk; s0 += 3) {
+    GSI_STEP(st0, st2, s0);
+    GSI_STEP(st1, st0, s0 + 1);
+    GSI_STEP(st2, st1, s0 + 2);
+  }
+  if (s0 < nk) GSI_STEP(st0, st2, s0);
+  if (s0 + 1 < nk) GSI_STEP(st1, st0, s0 + 1);
+  dwait_vmcnt<0>();  // no copy may land in LDS after the block ends
+#undef GSI_STEP
+#undef GSI_COMPUTE
+#undef GSI_ISSUE
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+      if (mm >= mv) continue;
+      const long long crow = c_idx ? c_idx[mm] : mm;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nn = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (nn >= n) continue;
+        float v = acc[i][j][r];
+        if (sub_identity && mm == nn) v -= 1.0f;
+        st_from_f32<TC>(C, crow * ldc + nn, v);
+      }
+    }
+}
+
+template <typename T>
+static void* pick_mfma_lds_c(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)gemm_nt_mfma_lds_kernel<T, float>;
+    case GSI_F16: return (void*)gemm_nt_mfma_lds_kernel<T, f16_t>;
+    case GSI_BF16: return (void*)gemm_nt_mfma_lds_kernel<T, bf16_t>;
+  }
+  return nullptr;
+}
+
 template <typename TA, typename TB>
 static void* pick_mfma_c(int c_type) {
   switch (c_type) {
@@ -256,6 +377,16 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
                    const int* m_count, int sub_identity, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
   void* fn = nullptr;
+  // LDS-staged matrix cores: one 16-bit type for A and B, K in whole 32-column steps, and enough
+  // rows to fill 128-row tiles (the small-m products of the batched path use the direct kernel)
+  if (kdim % 32 == 0 && m >= 128 && a_type == b_type && (a_type == GSI_BF16 || a_type == GSI_F16)) {
+    fn = a_type == GSI_BF16 ? pick_mfma_lds_c<bf16_t>(c_type) : pick_mfma_lds_c<f16_t>(c_type);
+    if (!fn) return GSI_ERR_DTYPE;
+    dim3 grid((n + 127) / 128, (m + 127) / 128);
+    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   // matrix cores for 16-bit operands of one type (float32 A with bf16 B through the bf16 split);
   // the vector-ALU kernel for the rest. Operand rows must start on 16 bytes (d and k are
   // multiples of 8 elements).
