@@ -82,9 +82,13 @@ def main():
     for si in sites:
         W = synth.site_weight(cfg, si.block, si.site).cuda()
         V = si.V.cuda()
+        # M and aux are allocated before the timed region: it holds the precompute kernels only
+        nb = g.gsi_layer_aux_bytes(g.dtype_code(W.dtype), si.d_out, si.d, cfg.k)
+        M = torch.empty((si.d_out, cfg.k), dtype=W.dtype, device=W.device)
+        aux = torch.empty(nb, dtype=torch.uint8, device=W.device)
         torch.cuda.synchronize()
         ev0.record()
-        L = g.create_layer(W, V)
+        L = g.gsi_layer_create(W, V, M, aux)
         ev1.record()
         torch.cuda.synchronize()
         pre_ms += ev0.elapsed_time(ev1)
@@ -93,6 +97,7 @@ def main():
         keep.append((W, V))
     log(f"[bench] uploaded weights and ran the M = W V precompute in {time.time() - t0:.1f}s "
         f"(precompute kernels {pre_ms:.1f} ms)")
+    pre512 = precompute_rank512(g, torch, cfg, sites, keep) if cfg.dtype != "f32" and cfg.k == 256 else None
     stack = g.gsi_stack_create(layers)
     n_sites = len(layers)
     X = torch.cat([si.X for si in sites], dim=1).contiguous().cuda()
@@ -127,6 +132,7 @@ def main():
         times.append((ev0.elapsed_time(ev1) / 1e3, t_wall))
     if g.gsi_workspace_status(ws) != 0:
         raise SystemExit("decode kernel reported a wait timeout")
+    stream_gbps = stream_read_gbps(torch)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b2 = torch.empty_like(a)
@@ -180,11 +186,68 @@ def main():
         "cpu_baseline": cpu,
         "fast_fraction": round(fast_frac, 5),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
+        "stream_read_gbps": round(stream_gbps, 1),
+        "frac_of_stream_read": round(achieved / stream_gbps, 4),
         "precompute": {"ms": round(pre_ms, 2), "tflop": round(pre_flop / 1e12, 4),
                        "tflops": round(pre_flop / (pre_ms / 1e3) / 1e12, 2) if pre_ms > 0 else None,
                        "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS},
+        "precompute_k512": pre512,
     }
     print(json.dumps(out), flush=True)
+
+
+def precompute_rank512(g, torch, cfg, sites, keep):
+    """The create-time precompute (V^T, M = W V, V^T V - I) at rank k = 512 over the same weights:
+    the shapes of the T = 64 GPT-J-shaped workload, whose precompute is the one matrix-core bound
+    step of the method. V is a seeded Gaussian matrix scaled by 1/sqrt(d) (orthonormality does not
+    change the work). Only the kernels are timed."""
+    k = 512
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5120)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms, flop = 0.0, 0.0
+    for si, (W, _) in zip(sites, keep):
+        V = (torch.randn((si.d, k), generator=gen, device="cuda") / si.d ** 0.5).to(W.dtype)
+        nb = g.gsi_layer_aux_bytes(g.dtype_code(W.dtype), si.d_out, si.d, k)
+        M = torch.empty((si.d_out, k), dtype=W.dtype, device="cuda")
+        aux = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        ev0.record()
+        L = g.gsi_layer_create(W, V, M, aux)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms += ev0.elapsed_time(ev1)
+        flop += 2.0 * si.d_out * si.d * k + 2.0 * k * k * si.d
+        del L, M, aux, V
+    return {"k": k, "ms": round(ms, 2), "tflop": round(flop / 1e12, 4),
+            "tflops": round(flop / (ms / 1e3) / 1e12, 2), "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+            "frac": round(flop / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+
+def stream_read_gbps(torch) -> float:
+    """Read bandwidth of the in-repo streaming-read kernel (libgsi_bench.so, one pass over 4 GiB
+    with 16-byte non-temporal loads) on the same GPU: a practical ceiling to set the decode
+    kernel's bandwidth against, beside the 8 TB/s peak. Best of 5 passes, HIP events."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_rank_linear_amd", "_lib", "libgsi_bench.so"))
+    lib.gsi_bench_stream_read.restype = ctypes.c_int
+    lib.gsi_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    x = torch.ones(1 << 32, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        ev0.record(stream)
+        rc = lib.gsi_bench_stream_read(x.data_ptr(), x.numel() // 16, sink.data_ptr(), stream.cuda_stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise SystemExit(f"stream-read kernel failed ({rc})")
+        best = max(best, x.numel() / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    del x, sink
+    return best
 
 
 def decode_kernel_name(cfg) -> str:

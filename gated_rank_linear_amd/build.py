@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libgsi.so")
+BENCH_LIB = os.path.join(OUT_DIR, "libgsi_bench.so")
 SOURCES = ["gsi_api.cpp", "gsi_dense.hip", "gsi_decode.hip"]
 
 HIP_FLAGS = [
@@ -57,6 +58,13 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
+    # the benchmark's streaming-read reference kernel, a library of its own (not libgsi's interface)
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [cc, *HIP_FLAGS, "-x", "hip", "-shared", "-Wl,--no-undefined", os.path.join(CSRC, "bench_stream.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the stream-read kernel failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 

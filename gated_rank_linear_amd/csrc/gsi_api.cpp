@@ -1,6 +1,7 @@
 // C ABI of libgsi (declared in include/gsi.h): argument validation, handles, and enqueueing of
 // the HIP kernels. Every argument check runs before the first HIP call, so an invalid call
 // enqueues nothing and never touches the device.
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -95,11 +96,20 @@ const char* gsi_status_string(int code) {
 }
 
 int gsi_device_check(void) {
+  // the answer per device is cached: reading the device properties costs about a millisecond
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSI_ERR_DEVICE;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int k = known[dev].load(std::memory_order_relaxed);
+    if (k != 0) return k == 1 ? GSI_OK : GSI_ERR_DEVICE;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GSI_ERR_DEVICE;
-  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? GSI_OK : GSI_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < kMaxDevices) known[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? GSI_OK : GSI_ERR_DEVICE;
 }
 
 size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k) {

@@ -333,6 +333,175 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __res
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): 64x256
+// output tile per block of 4 waves, so A (the weight, d_out x d) streams from memory once per
+// 256 columns. Wave w owns columns 64 w .. 64 w + 63 (4 x 4 tiles of 16x16). A 64-column K step
+// is 40 operand blocks of 1 KB (A: 2 sub-steps x 4 row tiles; B: 2 x 16 column tiles), copied
+// straight into LDS in MFMA operand order (10 per wave), three stages in flight (120 KB).
+// ---------------------------------------------------------------------------------------------
+template <typename T, typename TC>
+__global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restrict__ A, long long lda,
+                                                           const int* __restrict__ a_idx,
+                                                           const void* __restrict__ B, long long ldb,
+                                                           void* __restrict__ C, long long ldc,
+                                                           const int* __restrict__ c_idx, int m, int n, int kdim,
+                                                           const int* __restrict__ m_count, int sub_identity) {
+  __shared__ mu32x4 st0[40 * 64], st1[40 * 64], st2[40 * 64];
+  const int mv = m_count ? min(m, *m_count) : m;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 256;
+  if (m0 >= mv) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // operand block q = wave + 4 t: q < 8 is A sub-step q / 4, row tile q mod 4; q >= 8 is B
+  // sub-step (q - 8) / 16, column tile (q - 8) mod 16. Lane l reads row + (l mod 16), elements
+  // 8 (l / 16) .. + 7 of the sub-step.
+  const T* src[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) {
+    const int q = wave + 4 * t;
+    const int ko = 8 * (lane >> 4);
+    if (q < 8) {
+      const int mm = m0 + 16 * (q & 3) + (lane & 15);
+      const long long row = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) : 0;
+      src[t] = reinterpret_cast<const T*>(A) + row * lda + 32 * (q >> 2) + ko;
+    } else {
+      const int qb = q - 8;
+      const long long row = n0 + 16 * (qb & 15) + (lane & 15);
+      src[t] = reinterpret_cast<const T*>(B) + row * ldb + 32 * (qb >> 4) + ko;
+    }
+  }
+  mf32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+#define GSI_WISSUE(STAGE, K0)                                                                          \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < 10; ++t) __builtin_amdgcn_global_load_lds(                   \
+        (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + (wave + 4 * t) * 64), 16, 0, 0); \
+  } while (0)
+#define GSI_WCOMPUTE(STAGE)                                                                            \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
+      mu32x4 af[4], bf[4];                                                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = ((const dlu32x4*)(STAGE))[(u * 4 + i) * 64 + lane]; \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
+        bf[j] = ((const dlu32x4*)(STAGE))[(8 + u * 16 + wave * 4 + j) * 64 + lane];                   \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
+    }                                                                                                  \
+  } while (0)
+// every step issues exactly 10 copies per wave (past the last stage they re-read the last K step
+// into a stage nobody reads again), so waiting until at most 10 remain completes the current stage
+#define GSI_WSTEP(CUR, FUT, ST)                                                                         \
+  do {                                                                                                 \
+    dwait_vmcnt<10>();                                                                                 \
+    dlds_barrier();                                                                                    \
+    GSI_WISSUE(FUT, min((ST) + 2, nk - 1) * 64);                                                       \
+    GSI_WCOMPUTE(CUR);                                                                                 \
+  } while (0)
+  const int nk = kdim / 64;
+  GSI_WISSUE(st0, 0);
+  GSI_WISSUE(st1, min(1, nk - 1) * 64);
+  int s0 = 0;
+  for (; s0 + 3 <= nk; s0 += 3) {
+    GSI_WSTEP(st0, st2, s0);
+    GSI_WSTEP(st1, st0, s0 + 1);
+    GSI_WSTEP(st2, st1, s0 + 2);
+  }
+  if (s0 < nk) GSI_WSTEP(st0, st2, s0);
+  if (s0 + 1 < nk) GSI_WSTEP(st1, st0, s0 + 1);
+  dwait_vmcnt<0>();  // no copy may land in LDS after the block ends
+#undef GSI_WSTEP
+#undef GSI_WCOMPUTE
+#undef GSI_WISSUE
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m0 + i * 16 + 4 * (lane >> 4) + r;
+      if (mm >= mv) continue;
+      const long long crow = c_idx ? c_idx[mm] : mm;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nn = n0 + wave * 64 + j * 16 + (lane & 15);
+        float v = acc[i][j][r];
+        if (sub_identity && mm == nn) v -= 1.0f;
+        st_from_f32<TC>(C, crow * ldc + nn, v);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core NT GEMM for a small output with a long K (V^T V - I, the batched projection
+// X V): one 16x16 output tile per block; wave w accumulates the 32-column K steps w, w + 4, ...
+// from global memory (8 steps of loads in flight), and the four partial tiles are added in a
+// fixed order through LDS, so results are reproducible run to run.
+// ---------------------------------------------------------------------------------------------
+template <typename T, typename TC>
+__global__ __launch_bounds__(256) void gemm_nt_kslice_kernel(const void* __restrict__ A, long long lda,
+                                                             const void* __restrict__ B, long long ldb,
+                                                             void* __restrict__ C, long long ldc, int m, int n,
+                                                             int kdim, int sub_identity) {
+  __shared__ mf32x4 part[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tm = blockIdx.y * 16, tn = blockIdx.x * 16;
+  const int ra = min(tm + (lane & 15), m - 1), rb = min(tn + (lane & 15), n - 1);
+  const mu32x4* pa = reinterpret_cast<const mu32x4*>(reinterpret_cast<const T*>(A) + (long long)ra * lda) + (lane >> 4);
+  const mu32x4* pb = reinterpret_cast<const mu32x4*>(reinterpret_cast<const T*>(B) + (long long)rb * ldb) + (lane >> 4);
+  const int nk = kdim / 32;  // a K step is 4 chunks of 16 bytes per row
+  mf32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  int s = wave;
+  for (; s + 28 < nk; s += 32) {
+    mu32x4 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = pa[(s + 4 * u) * 4];
+      b[u] = pb[(s + 4 * u) * 4];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      acc0 = mfma_op<T>::run(a[u], b[u], acc0);
+      acc1 = mfma_op<T>::run(a[u + 1], b[u + 1], acc1);
+    }
+  }
+  for (; s < nk; s += 4) acc0 = mfma_op<T>::run(pa[s * 4], pb[s * 4], acc0);
+  mf32x4 acc = acc0 + acc1;
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    acc = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = tm + 4 * (lane >> 4) + r, nn = tn + (lane & 15);
+      if (mm >= m || nn >= n) continue;
+      float v = acc[r];
+      if (sub_identity && mm == nn) v -= 1.0f;
+      st_from_f32<TC>(C, (long long)mm * ldc + nn, v);
+    }
+  }
+}
+
+template <typename T>
+static void* pick_wide_c(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)gemm_nt_wide_kernel<T, float>;
+    case GSI_F16: return (void*)gemm_nt_wide_kernel<T, f16_t>;
+    case GSI_BF16: return (void*)gemm_nt_wide_kernel<T, bf16_t>;
+  }
+  return nullptr;
+}
+
+template <typename T>
+static void* pick_kslice_c(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)gemm_nt_kslice_kernel<T, float>;
+    case GSI_F16: return (void*)gemm_nt_kslice_kernel<T, f16_t>;
+    case GSI_BF16: return (void*)gemm_nt_kslice_kernel<T, bf16_t>;
+  }
+  return nullptr;
+}
+
 template <typename T>
 static void* pick_mfma_lds_c(int c_type) {
   switch (c_type) {
@@ -377,6 +546,25 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
                    const int* m_count, int sub_identity, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
   void* fn = nullptr;
+  const bool same16 = a_type == b_type && (a_type == GSI_BF16 || a_type == GSI_F16);
+  // a small output with a long K and no row lists: one 16x16 tile per block, K split over 4 waves
+  if (same16 && kdim % 32 == 0 && kdim >= 1024 && !a_idx && !c_idx && !m_count && m <= 1024 && n <= 1024) {
+    fn = a_type == GSI_BF16 ? pick_kslice_c<bf16_t>(c_type) : pick_kslice_c<f16_t>(c_type);
+    if (!fn) return GSI_ERR_DTYPE;
+    dim3 grid((n + 15) / 16, (m + 15) / 16);
+    void* args[] = {&A, &lda, &B, &ldb, &C, &ldc, &m, &n, &kdim, &sub_identity};
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
+  // a tall A against a short, wide B (M = W V with k a multiple of 256): A streams once
+  if (same16 && kdim % 64 == 0 && n % 256 == 0 && m >= 256) {
+    fn = a_type == GSI_BF16 ? pick_wide_c<bf16_t>(c_type) : pick_wide_c<f16_t>(c_type);
+    if (!fn) return GSI_ERR_DTYPE;
+    dim3 grid((m + 63) / 64, n / 256);
+    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   // LDS-staged matrix cores: one 16-bit type for A and B, K in whole 32-column steps, and enough
   // rows to fill 128-row tiles (the small-m products of the batched path use the direct kernel)
   if (kdim % 32 == 0 && m >= 128 && a_type == b_type && (a_type == GSI_BF16 || a_type == GSI_F16)) {
