@@ -334,68 +334,74 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __res
 }
 
 // ---------------------------------------------------------------------------------------------
-// Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): 64x256
-// output tile per block of 4 waves, so A (the weight, d_out x d) streams from memory once per
-// 256 columns. Wave w owns columns 64 w .. 64 w + 63 (4 x 4 tiles of 16x16). A 64-column K step
-// is 40 operand blocks of 1 KB (A: 2 sub-steps x 4 row tiles; B: 2 x 16 column tiles), copied
-// straight into LDS in MFMA operand order (10 per wave), three stages in flight (120 KB).
+// Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): MT x 256
+// output tile per block of 4 waves (MT = 16, 32 or 64 rows, chosen so the grid fills the chip),
+// so A (the weight, d_out x d) streams from memory once per 256 columns. Wave w owns columns
+// 64 w .. 64 w + 63. A 64-column K step is NB operand blocks of 1 KB (A: 2 sub-steps x MT / 16
+// row tiles; B: 2 x 16 column tiles), copied straight into LDS in MFMA operand order, three
+// stages in flight. Every wave issues the same number of copies per step: when NB is not a
+// multiple of 4 the spare copies repeat the first blocks (same data to the same place).
 // ---------------------------------------------------------------------------------------------
-template <typename T, typename TC>
+template <typename T, typename TC, int MT>
 __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restrict__ A, long long lda,
                                                            const int* __restrict__ a_idx,
                                                            const void* __restrict__ B, long long ldb,
                                                            void* __restrict__ C, long long ldc,
                                                            const int* __restrict__ c_idx, int m, int n, int kdim,
                                                            const int* __restrict__ m_count, int sub_identity) {
-  __shared__ mu32x4 st0[40 * 64], st1[40 * 64], st2[40 * 64];
+  constexpr int RT = MT / 16, NA = 2 * RT, NB = NA + 32, CPW = (NB + 3) / 4;
+  __shared__ mu32x4 st0[NB * 64], st1[NB * 64], st2[NB * 64];
   const int mv = m_count ? min(m, *m_count) : m;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 256;
+  const int m0 = blockIdx.x * MT, n0 = blockIdx.y * 256;
   if (m0 >= mv) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // operand block q = wave + 4 t: q < 8 is A sub-step q / 4, row tile q mod 4; q >= 8 is B
-  // sub-step (q - 8) / 16, column tile (q - 8) mod 16. Lane l reads row + (l mod 16), elements
-  // 8 (l / 16) .. + 7 of the sub-step.
-  const T* src[10];
+  // copy t of this wave fills operand block qd = (wave + 4 t) mod NB: qd < NA is A sub-step
+  // qd / RT, row tile qd mod RT; qd >= NA is B sub-step (qd - NA) / 16, column tile
+  // (qd - NA) mod 16. Lane l reads row + (l mod 16), elements 8 (l / 16) .. + 7 of the sub-step.
+  const T* src[CPW];
+  int dst[CPW];
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
+  for (int t = 0; t < CPW; ++t) {
     const int q = wave + 4 * t;
+    const int qd = q < NB ? q : q - NB;
     const int ko = 8 * (lane >> 4);
-    if (q < 8) {
-      const int mm = m0 + 16 * (q & 3) + (lane & 15);
+    dst[t] = qd * 64;
+    if (qd < NA) {
+      const int mm = m0 + 16 * (qd % RT) + (lane & 15);
       const long long row = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) : 0;
-      src[t] = reinterpret_cast<const T*>(A) + row * lda + 32 * (q >> 2) + ko;
+      src[t] = reinterpret_cast<const T*>(A) + row * lda + 32 * (qd / RT) + ko;
     } else {
-      const int qb = q - 8;
+      const int qb = qd - NA;
       const long long row = n0 + 16 * (qb & 15) + (lane & 15);
       src[t] = reinterpret_cast<const T*>(B) + row * ldb + 32 * (qb >> 4) + ko;
     }
   }
-  mf32x4 acc[4][4];
+  mf32x4 acc[RT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
 #define GSI_WISSUE(STAGE, K0)                                                                          \
   do {                                                                                                 \
-    _Pragma("unroll") for (int t = 0; t < 10; ++t) __builtin_amdgcn_global_load_lds(                   \
-        (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + (wave + 4 * t) * 64), 16, 0, 0); \
+    _Pragma("unroll") for (int t = 0; t < CPW; ++t) __builtin_amdgcn_global_load_lds(                  \
+        (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + dst[t]), 16, 0, 0);             \
   } while (0)
 #define GSI_WCOMPUTE(STAGE)                                                                            \
   do {                                                                                                 \
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
-      mu32x4 af[4], bf[4];                                                                             \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = ((const dlu32x4*)(STAGE))[(u * 4 + i) * 64 + lane]; \
+      mu32x4 af[RT], bf[4];                                                                            \
+      _Pragma("unroll") for (int i = 0; i < RT; ++i) af[i] = ((const dlu32x4*)(STAGE))[(u * RT + i) * 64 + lane]; \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-        bf[j] = ((const dlu32x4*)(STAGE))[(8 + u * 16 + wave * 4 + j) * 64 + lane];                   \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+        bf[j] = ((const dlu32x4*)(STAGE))[(NA + u * 16 + wave * 4 + j) * 64 + lane];                  \
+      _Pragma("unroll") for (int i = 0; i < RT; ++i)                                                   \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
     }                                                                                                  \
   } while (0)
-// every step issues exactly 10 copies per wave (past the last stage they re-read the last K step
-// into a stage nobody reads again), so waiting until at most 10 remain completes the current stage
+// every step issues exactly CPW copies per wave (past the last stage they re-read the last K step
+// into a stage nobody reads again), so waiting until at most CPW remain completes the current one
 #define GSI_WSTEP(CUR, FUT, ST)                                                                         \
   do {                                                                                                 \
-    dwait_vmcnt<10>();                                                                                 \
+    dwait_vmcnt<CPW>();                                                                                \
     dlds_barrier();                                                                                    \
     GSI_WISSUE(FUT, min((ST) + 2, nk - 1) * 64);                                                       \
     GSI_WCOMPUTE(CUR);                                                                                 \
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
 #undef GSI_WCOMPUTE
 #undef GSI_WISSUE
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = m0 + i * 16 + 4 * (lane >> 4) + r;
@@ -482,14 +488,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kslice_kernel(const void* __restr
   }
 }
 
-template <typename T>
+template <typename T, int MT>
 static void* pick_wide_c(int c_type) {
   switch (c_type) {
-    case GSI_F32: return (void*)gemm_nt_wide_kernel<T, float>;
-    case GSI_F16: return (void*)gemm_nt_wide_kernel<T, f16_t>;
-    case GSI_BF16: return (void*)gemm_nt_wide_kernel<T, bf16_t>;
+    case GSI_F32: return (void*)gemm_nt_wide_kernel<T, float, MT>;
+    case GSI_F16: return (void*)gemm_nt_wide_kernel<T, f16_t, MT>;
+    case GSI_BF16: return (void*)gemm_nt_wide_kernel<T, bf16_t, MT>;
   }
   return nullptr;
+}
+
+template <typename T>
+static void* pick_wide(int mt, int c_type) {
+  return mt == 64 ? pick_wide_c<T, 64>(c_type) : mt == 32 ? pick_wide_c<T, 32>(c_type) : pick_wide_c<T, 16>(c_type);
 }
 
 template <typename T>
@@ -558,9 +569,13 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
   }
   // a tall A against a short, wide B (M = W V with k a multiple of 256): A streams once
   if (same16 && kdim % 64 == 0 && n % 256 == 0 && m >= 256) {
-    fn = a_type == GSI_BF16 ? pick_wide_c<bf16_t>(c_type) : pick_wide_c<f16_t>(c_type);
+    // rows per tile: the most that still gives about one block per CU (a block's time is set by
+    // its copies in flight, so more blocks, not bigger ones, raise the rate)
+    const long long cols = n / 256;
+    const int mt = (m + 63) / 64 * cols >= 192 ? 64 : (m + 31) / 32 * cols >= 192 ? 32 : 16;
+    fn = a_type == GSI_BF16 ? pick_wide<bf16_t>(mt, c_type) : pick_wide<f16_t>(mt, c_type);
     if (!fn) return GSI_ERR_DTYPE;
-    dim3 grid((m + 63) / 64, n / 256);
+    dim3 grid((m + mt - 1) / mt, n / 256);
     void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
     hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
