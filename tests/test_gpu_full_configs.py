@@ -124,3 +124,42 @@ def test_zero_tokens_is_a_no_op(g):
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.all(y == 7.0) and int(gate.item()) == 9
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(12300, 1024, 256), (6150, 1024, 256), (1000, 2048, 256), (3000, 1024, 512),
+                                   (300, 4096, 512)])
+def test_precompute_tile_paths(g, dtype, shape):
+    """The precompute M = W V on the matrix-core tile paths: 64-, 32- and 16-row tiles of the wide
+    kernel (chosen by d_out), two 256-column tiles (k = 512), ragged last row tiles, and the
+    K-split kernel of V^T V - I (d >= 1024), whose effect is checked through rho of single
+    tokens (persistent path) against the oracle's residual norms."""
+    d_out, d, k = shape
+    rng = np.random.default_rng(d_out + 3 * d + k)
+    Q, R = np.linalg.qr(rng.standard_normal((d, k + 32)))
+    Q = Q * np.sign(np.diag(R))
+    V64, C64 = Q[:, :k], Q[:, k:]
+    W = torch.from_numpy(rng.standard_normal((d_out, d)) * 0.03).to(dtype)
+    V = torch.from_numpy(V64).to(dtype)
+    say(f"case: precompute tiles {shape} {dtype}")
+    L = g.create_layer(W.cuda(), V.cuda())
+    torch.cuda.synchronize()
+    M = to_np(g.layer_image(L))
+    ref = orc.precompute_image(W, V)
+    # one rounding to the 16-bit type on top of float32 accumulation
+    assert rel_l2(M, ref) <= 4e-3, rel_l2(M, ref)
+    eps = 0.2
+    X = torch.from_numpy(_planned_tokens(rng, V64, C64, eps, 3, 0.5)).to(dtype)
+    x = X.cuda().contiguous()
+    y = torch.zeros((3, d_out), dtype=dtype, device="cuda")
+    gate = torch.full((3,), 9, dtype=torch.uint8, device="cuda")
+    rho = torch.zeros(3, dtype=torch.float32, device="cuda")
+    ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, d_out, d, k, 3))
+    g.gsi_forward(L, x, eps, y, gate, rho, ws)
+    torch.cuda.synchronize()
+    assert g.gsi_workspace_status(ws) == 0
+    ref_rho = np.sqrt(orc.residual_norms(V, X) / orc.squared_norms(X))
+    np.testing.assert_allclose(rho.cpu().numpy(), ref_rho, rtol=1e-4, atol=1e-6)
+    ref_g = orc.gate_only(V, X, eps)
+    keep = np.abs(ref_g["rho"] - eps) > 1e-3
+    assert np.array_equal(gate.cpu().numpy()[keep], ref_g["gate"][keep])
