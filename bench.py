@@ -67,7 +67,8 @@ def main():
         raise SystemExit("not a gfx950 device")
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
-        raise SystemExit("bench.py times batch-1 decode configs (t_step = 1)")
+        batched(args, cfg, g, torch, np)
+        return
     es = 2 if cfg.dtype != "f32" else 4
 
     # ---------------- inputs: generate on the host, upload, precompute M on the GPU ----------------
@@ -194,6 +195,97 @@ def main():
         "precompute_k512": pre512,
     }
     print(json.dumps(out), flush=True)
+
+
+def batched(args, cfg, g, torch, np):
+    """A T-token-per-step workload (the GPT-J-shaped stack at T = 64, k = 512): every site runs
+    the batched path (projection, device-side gate and compaction, M g for the fast tokens and W x
+    for the slow ones on the matrix cores) once per step. Inputs: a pool of generated steps,
+    cycled (the workload's own recipe); --steps counts steps of T tokens. Bytes per (step, site)
+    from the realised gates: V_k, plus M if any token is fast, plus W if any token is slow."""
+    from synth.generate import config_inputs, token_steps
+
+    es = 2 if cfg.dtype != "f32" else 4
+    pool = token_steps(cfg)
+    t0 = time.time()
+    sites = []
+    for b0 in range(0, cfg.n_blocks, 4):
+        sites += config_inputs(cfg, blocks=range(b0, min(cfg.n_blocks, b0 + 4)), n_steps=pool)
+        log(f"[bench] generated blocks {b0}..{min(cfg.n_blocks, b0 + 4) - 1} ({time.time() - t0:.0f}s)")
+    log(f"[bench] generated bases and {pool} steps of {cfg.t_step} tokens for {len(sites)} sites in {time.time() - t0:.1f}s")
+    layers, keep = [], []
+    for si in sites:
+        W = synth_weight(cfg, si)
+        L = g.create_layer(W, si.V.cuda())
+        layers.append(L)
+        keep.append(W)
+    torch.cuda.synchronize()
+    stack = g.gsi_stack_create(layers)
+    n_sites = len(layers)
+    X = torch.cat([si.X for si in sites], dim=1).contiguous().cuda()
+    n_tok = X.shape[0]
+    y_ld = sum(si.d_out for si in sites)
+    Y = torch.zeros((n_tok, y_ld), dtype=X.dtype, device="cuda")
+    gates = torch.zeros((n_tok, n_sites), dtype=torch.uint8, device="cuda")
+    ws = g.new_workspace(g.gsi_stack_workspace_bytes(stack, cfg.t_step))
+    stream = torch.cuda.current_stream()
+    slow_steps = []
+
+    def run(steps: int, record: bool):
+        done = 0
+        while done < steps:
+            n = min(pool, steps - done)
+            g.gsi_stack_decode(stack, X, n, cfg.t_step, cfg.eps, Y, gates, None, ws, stream)
+            if record:
+                slow_steps.append(gates[: n * cfg.t_step].view(n, cfg.t_step, n_sites).clone())
+            done += n
+
+    run(args.warmup, False)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(max(1, args.reps)):
+        slow_steps.clear()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        run(args.steps, True)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / 1e3)
+    if g.gsi_workspace_status(ws) != 0:
+        raise SystemExit("batched path reported a wait timeout")
+    times.sort()
+    t_gpu = times[len(times) // 2]
+    gs = torch.cat(slow_steps).cpu().numpy().astype(bool)          # [steps, T, sites]
+    any_slow = gs.any(axis=1)
+    any_fast = (~gs).any(axis=1)
+    v_b = np.array([si.d * cfg.k * es for si in sites], dtype=np.float64)
+    m_b = np.array([si.d_out * cfg.k * es for si in sites], dtype=np.float64)
+    w_b = np.array([si.d_out * si.d * es for si in sites], dtype=np.float64)
+    bytes_total = float(np.sum(v_b[None, :] + any_fast * m_b[None, :] + any_slow * w_b[None, :]))
+    tok_s = args.steps * cfg.t_step / t_gpu
+    achieved = bytes_total / t_gpu / 1e9
+    out = {
+        "metric": "GSI batched decode tokens/s + achieved HBM GB/s vs peak",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_gpu * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_blocks} blocks x {len(cfg.sites)} sites, k={cfg.k}, eps={cfg.eps}, "
+                               f"T={cfg.t_step} per step, pool of {pool} steps cycled", "batch": cfg.t_step, "k": cfg.k,
+                   "eps": cfg.eps, "sites": n_sites},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "batched path, all kernels of a step", "bytes_per_step": bytes_total / args.steps},
+        "slow_fraction": round(float(gs.mean()), 4),
+        "sites_with_slow_tokens": round(float(any_slow.mean()), 4),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def synth_weight(cfg, si):
+    import synth
+    return synth.site_weight(cfg, si.block, si.site).cuda()
 
 
 def precompute_rank512(g, torch, cfg, sites, keep):

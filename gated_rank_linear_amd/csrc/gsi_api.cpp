@@ -41,7 +41,9 @@ size_t aux_dl_off(int dtype, int d, int k) { return align256((size_t)k * d * dty
 size_t aux_desc_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
 size_t aux_bytes(int dtype, int d, int k) { return aux_desc_off(dtype, d, k) + align256(sizeof(LayerDesc)); }
 
-size_t ws_bytes_for(int k, int T) { return align256(decode_ws_bytes()) + batched_ws_bytes(k, T < 1 ? 1 : T); }
+size_t ws_bytes_for(int k, int d_out, int T) {
+  return align256(decode_ws_bytes()) + batched_ws_bytes(k, T < 1 ? 1 : T, d_out);
+}
 
 WsHeader* ws_header(void* ws) { return reinterpret_cast<WsHeader*>(ws); }
 
@@ -56,23 +58,24 @@ void fill_decode_boxes(DecodeParams& p, void* ws) {
   p.box_f = (u64*)c;
 }
 
-BatchedWs batched_part(void* ws, int k, int T) {
-  return batched_ws_carve((char*)ws + align256(decode_ws_bytes()), k, T);
+BatchedWs batched_part(void* ws, int k, int T, int d_out) {
+  return batched_ws_carve((char*)ws + align256(decode_ws_bytes()), k, T, d_out);
 }
 
 // Batched path for one site over T tokens whose rows sit at X (+ row stride x_ld) and Y.
+// d_out_ws: the d_out the workspace was sized for (the largest of a stack)
 int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps, void* Y,
-                long long y_ld, uint8_t* gate, int gate_ld, float* rho, void* ws, hipStream_t s) {
-  BatchedWs w = batched_part(ws, L.k, T);
+                long long y_ld, uint8_t* gate, int gate_ld, float* rho, void* ws, int d_out_ws, hipStream_t s) {
+  BatchedWs w = batched_part(ws, L.k, T, d_out_ws);
   int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
   if (rc != GSI_OK) return rc;
   // fast tokens: y = M g     [GSI §2.2]
-  rc = launch_gemm_nt(GSI_F32, dtype, dtype, w.G, L.k, w.fast_idx, L.M, L.k, Y, y_ld, w.fast_idx, T, L.d_out, L.k,
-                      w.counts + 0, 0, s);
+  rc = launch_gemm_nt_split(GSI_F32, dtype, dtype, w.G, L.k, w.fast_idx, L.M, L.k, Y, y_ld, w.fast_idx, T, L.d_out,
+                            L.k, w.counts + 0, w.part, w.part_elems, s);
   if (rc != GSI_OK) return rc;
   // slow tokens: y = W x     [GSI §2.2]
-  return launch_gemm_nt(dtype, dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, Y, y_ld, w.slow_idx, T, L.d_out, L.d,
-                        w.counts + 1, 0, s);
+  return launch_gemm_nt_split(dtype, dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, Y, y_ld, w.slow_idx, T, L.d_out,
+                              L.d, w.counts + 1, w.part, w.part_elems, s);
 }
 
 }  // namespace
@@ -169,7 +172,7 @@ int gsi_layer_destroy(gsi_layer* L) {
 
 size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max) {
   if (check_shape(dtype, d_out, d, k) != GSI_OK || T_max < 0) return 0;
-  return ws_bytes_for(k, T_max);
+  return ws_bytes_for(k, d_out, T_max);
 }
 
 int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, uint8_t* gate, float* rho, void* ws,
@@ -181,7 +184,7 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
   if (T == 0) return GSI_OK;
   if (!x || !y || !gate || !ws) return GSI_ERR_NULL;
   if (!aligned16(x) || !aligned16(ws)) return GSI_ERR_ALIGN;
-  if (ws_nbytes < ws_bytes_for(L->k, T)) return GSI_ERR_WORKSPACE;
+  if (ws_nbytes < ws_bytes_for(L->k, L->d_out, T)) return GSI_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (T < 16) {
     DecodeParams p;
@@ -203,7 +206,7 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
     fill_decode_boxes(p, ws);
     return launch_decode(L->dtype, p, &L->desc, s);
   }
-  return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, s);
+  return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, L->d_out, s);
 }
 
 int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
@@ -272,7 +275,7 @@ int gsi_stack_destroy(gsi_stack* S) {
 
 size_t gsi_stack_workspace_bytes(const gsi_stack* S, int T_step) {
   if (!S || T_step < 1) return 0;
-  return ws_bytes_for(S->k_max, T_step);
+  return ws_bytes_for(S->k_max, S->d_out_max, T_step);
 }
 
 int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
@@ -284,7 +287,7 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
   if (n_steps == 0) return GSI_OK;
   if (!X || !Y || !gates || !ws) return GSI_ERR_NULL;
   if (!aligned16(X) || !aligned16(ws)) return GSI_ERR_ALIGN;
-  if (ws_nbytes < ws_bytes_for(S->k_max, T_step)) return GSI_ERR_WORKSPACE;
+  if (ws_nbytes < ws_bytes_for(S->k_max, S->d_out_max, T_step)) return GSI_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (T_step == 1) {
     DecodeParams p;
@@ -315,7 +318,7 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
       char* ys = (char*)Y + (size_t)(row0 * S->y_ld + L.y_off) * es;
       uint8_t* gs = gates + row0 * S->n_sites + i;
       float* rs = rho ? rho + row0 * S->n_sites + i : nullptr;
-      rc = run_batched(S->dtype, L, xs, S->x_ld, T_step, eps, ys, S->y_ld, gs, S->n_sites, rs, ws, s);
+      rc = run_batched(S->dtype, L, xs, S->x_ld, T_step, eps, ys, S->y_ld, gs, S->n_sites, rs, ws, S->d_out_max, s);
       if (rc != GSI_OK) return rc;
     }
   }

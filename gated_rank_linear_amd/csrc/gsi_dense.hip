@@ -4,6 +4,8 @@
 // acceleration" technical summary (gist.science, arXiv 2605.03109), §2.1-§2.2.
 #include "gsi_internal.h"
 
+#include <algorithm>
+
 namespace gsi {
 
 template <typename T> __device__ __forceinline__ float ld_f32(const void* p, long long i) {
@@ -120,11 +122,15 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
                                                            const int* __restrict__ a_idx, const void* __restrict__ B,
                                                            long long ldb, void* __restrict__ C, long long ldc,
                                                            const int* __restrict__ c_idx, int m, int n, int kdim,
-                                                           const int* __restrict__ m_count, int sub_identity) {
+                                                           const int* __restrict__ m_count, int sub_identity,
+                                                           int k_chunk, float* __restrict__ part) {
   constexpr bool kSplit = sizeof(TA) == 4;  // float32 A against bf16 B
+  constexpr int kGroup = 4;                 // K steps of 32 whose loads are issued together
   const int mv = m_count ? min(m, *m_count) : m;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   if (m0 >= mv) return;
+  // split K: block z takes columns [kb, ke) and, when part is given, writes its raw sums there
+  const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -146,62 +152,90 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_step = [&](int k0, mu32x4 (&ah)[2], mu32x4 (&al)[2], mu32x4 (&bv)[2]) {
+  // raw 16-byte chunks of one K step (A as loaded; the bf16 split of a float32 A happens at use)
+  struct Frag {
+    mu32x4 a[2][kSplit ? 2 : 1];
+    mu32x4 b[2];
+  };
+  auto load_step = [&](int k0, Frag& f) {
     const int kk = k0 + kq * 8;
-    const bool kin = kk < kdim;  // kdim is a multiple of 8, so a chunk is all in or all out
-    const int kc = kin ? kk : 0;
+    const bool kin = kk < ke;  // kdim and the chunk bounds are multiples of 8: a chunk is all in or out
+    const int kc = kin ? kk : kb;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const bool ok = aok[i] && kin;
       if constexpr (kSplit) {
-        const float* pa = reinterpret_cast<const float*>(A) + arow[i] + kc;
-        const mf32x4 f0 = reinterpret_cast<const mf32x4*>(pa)[0];
-        const mf32x4 f1 = reinterpret_cast<const mf32x4*>(pa)[1];
-        const bool ok = aok[i] && kin;
-        float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        const mu32x4* pa = reinterpret_cast<const mu32x4*>(reinterpret_cast<const float*>(A) + arow[i] + kc);
+        f.a[i][0] = ok ? pa[0] : mu32x4{0u, 0u, 0u, 0u};
+        f.a[i][1] = ok ? pa[1] : mu32x4{0u, 0u, 0u, 0u};
+      } else {
+        const mu32x4 v = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TA*>(A) + arow[i] + kc)[0];
+        f.a[i][0] = ok ? v : mu32x4{0u, 0u, 0u, 0u};
+      }
+      const mu32x4 w = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TB*>(B) + brow[i] + kc)[0];
+      f.b[i] = (bok[i] && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto compute_step = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      mu32x4 ah, al = mu32x4{0u, 0u, 0u, 0u};
+      if constexpr (kSplit) {
+        const mu32x4 r0 = f.a[i][0], r1 = f.a[i][1];
+        const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
         unsigned short h[8], l[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float v = ok ? f[e] : 0.f;
+          const float v = __uint_as_float(raw[e]);
           const bf16_t hb = from_f32<bf16_t>(v);
           const bf16_t lb = from_f32<bf16_t>(v - to_f32(hb));
           h[e] = hb.b;
           l[e] = lb.b;
         }
-        ah[i] = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
-                       h[6] | ((unsigned)h[7] << 16)};
-        al[i] = mu32x4{l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16), l[4] | ((unsigned)l[5] << 16),
-                       l[6] | ((unsigned)l[7] << 16)};
+        ah = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
+                    h[6] | ((unsigned)h[7] << 16)};
+        al = mu32x4{l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16), l[4] | ((unsigned)l[5] << 16),
+                    l[6] | ((unsigned)l[7] << 16)};
       } else {
-        const mu32x4 v = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TA*>(A) + arow[i] + kc)[0];
-        const bool ok = aok[i] && kin;
-        ah[i] = ok ? v : mu32x4{0u, 0u, 0u, 0u};
-        al[i] = mu32x4{0u, 0u, 0u, 0u};
+        ah = f.a[i][0];
       }
-      const mu32x4 w = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TB*>(B) + brow[i] + kc)[0];
-      bv[i] = (bok[i] && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma_op<TB>::run(ah, f.b[j], acc[i][j]);
+        if constexpr (kSplit) acc[i][j] = mfma_op<TB>::run(al, f.b[j], acc[i][j]);
+      }
     }
   };
 
-  mu32x4 ah[2], al[2], bv[2];
-  load_step(0, ah, al, bv);
-  const int k_last = (kdim - 1) / 32 * 32;
-  for (int k0 = 0; k0 < kdim; k0 += 32) {
-    // the next step's fragments (the last step reloads itself), loaded unconditionally
-    mu32x4 nah[2], nal[2], nbv[2];
-    load_step(min(k0 + 32, k_last), nah, nal, nbv);
+  // groups of kGroup steps, double-buffered: the next group's loads are all issued before this
+  // group's products, so up to 2 kGroup steps of loads are in flight (steps past the chunk load
+  // zeros)
+  Frag cur[kGroup], nxt[kGroup];
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) load_step(kb + 32 * u, cur[u]);
+  for (int k0 = kb; k0 < ke; k0 += 32 * kGroup) {
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) load_step(k0 + 32 * (kGroup + u), nxt[u]);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) compute_step(cur[u]);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) cur[u] = nxt[u];
+  }
+  if (part) {  // raw partial sums of this K chunk: part[z][mm][nn]
+    float* pz = part + (long long)blockIdx.z * m * n;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma_op<TB>::run(ah[i], bv[j], acc[i][j]);
-        if constexpr (kSplit) acc[i][j] = mfma_op<TB>::run(al[i], bv[j], acc[i][j]);
-      }
+      for (int r = 0; r < 4; ++r) {
+        const int mm = m0 + wm * 32 + i * 16 + 4 * kq + r;
+        if (mm >= mv) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ah[i] = nah[i];
-      al[i] = nal[i];
-      bv[i] = nbv[i];
-    }
+        for (int j = 0; j < 2; ++j) {
+          const int nn = n0 + wn * 32 + j * 16 + r16;
+          if (nn < n) pz[(long long)mm * n + nn] = acc[i][j][r];
+        }
+      }
+    return;
   }
   // D of a 16x16 tile: lane l holds column l mod 16, rows 4 (l / 16) .. + 3
 #pragma unroll
@@ -220,6 +254,23 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
         st_from_f32<TC>(C, crow * ldc + nn, v);
       }
     }
+}
+
+// Sum of split-K partials in chunk order, C[c_row(mm)][nn] = sum_z part[z][mm][nn] for the
+// mv = min(m, *m_count) valid rows.
+template <typename TC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int m, int n,
+                                                            const int* __restrict__ m_count, void* __restrict__ C,
+                                                            long long ldc, const int* __restrict__ c_idx) {
+  const int mm = blockIdx.y;
+  const int mv = m_count ? min(m, *m_count) : m;
+  if (mm >= mv) return;
+  const long long crow = c_idx ? c_idx[mm] : mm;
+  for (int nn = blockIdx.x * 256 + threadIdx.x; nn < n; nn += gridDim.x * 256) {
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += part[((long long)z * m + mm) * n + nn];
+    st_from_f32<TC>(C, crow * ldc + nn, v);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -552,12 +603,68 @@ static void* pick_b(int b_type, int c_type) {
   return nullptr;
 }
 
+// the register-fed matrix-core kernel for these operand types, or null
+static void* pick_mfma(int a_type, int b_type, int c_type) {
+  if (a_type == GSI_BF16 && b_type == GSI_BF16) return pick_mfma_c<bf16_t, bf16_t>(c_type);
+  if (a_type == GSI_F16 && b_type == GSI_F16) return pick_mfma_c<f16_t, f16_t>(c_type);
+  if (a_type == GSI_F32 && b_type == GSI_BF16) return pick_mfma_c<float, bf16_t>(c_type);
+  return nullptr;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Small float32 NT GEMM on the vector ALU (the batched G (V^T V - I), T x k x k): one 16x16
+// output tile per block, one output per thread, K staged through LDS 64 columns at a time;
+// each output is a fixed-order sum.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm_nt_small_f32_kernel(const float* __restrict__ A, long long lda,
+                                                                const float* __restrict__ B, long long ldb,
+                                                                float* __restrict__ C, long long ldc, int m, int n,
+                                                                int kdim) {
+  __shared__ float As[16][65], Bs[16][65];
+  const int tm = blockIdx.y * 16, tn = blockIdx.x * 16;
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < kdim; k0 += 64) {
+    // 16 rows x 64 columns of each operand: 4 elements per thread
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = threadIdx.x + 256 * e, rr = idx >> 6, kk = idx & 63;
+      const int ra = min(tm + rr, m - 1), rb = min(tn + rr, n - 1);
+      const bool kin = k0 + kk < kdim;
+      As[rr][kk] = kin ? A[(long long)ra * lda + k0 + kk] : 0.f;
+      Bs[rr][kk] = kin ? B[(long long)rb * ldb + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 16
+    for (int kk = 0; kk < 64; ++kk) acc = __builtin_fmaf(As[r][kk], Bs[c][kk], acc);
+    __syncthreads();
+  }
+  if (tm + r < m && tn + c < n) C[(long long)(tm + r) * ldc + tn + c] = acc;
+}
+
+static void* pick_reduce(int c_type) {
+  switch (c_type) {
+    case GSI_F32: return (void*)splitk_reduce_kernel<float>;
+    case GSI_F16: return (void*)splitk_reduce_kernel<f16_t>;
+    case GSI_BF16: return (void*)splitk_reduce_kernel<bf16_t>;
+  }
+  return nullptr;
+}
+
 int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
                    const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n, int kdim,
                    const int* m_count, int sub_identity, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
   void* fn = nullptr;
   const bool same16 = a_type == b_type && (a_type == GSI_BF16 || a_type == GSI_F16);
+  // float32 products too small to fill the chip with 64x64 tiles: 16x16 tiles
+  if (a_type == GSI_F32 && b_type == GSI_F32 && c_type == GSI_F32 && !a_idx && !c_idx && !m_count && !sub_identity &&
+      (long long)((m + 63) / 64) * ((n + 63) / 64) < 128) {
+    dim3 grid((n + 15) / 16, (m + 15) / 16);
+    gemm_nt_small_f32_kernel<<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, (float*)C, ldc, m, n,
+                                                 kdim);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   // a small output with a long K and no row lists: one 16x16 tile per block, K split over 4 waves
   if (same16 && kdim % 32 == 0 && kdim >= 1024 && !a_idx && !c_idx && !m_count && m <= 1024 && n <= 1024) {
     fn = a_type == GSI_BF16 ? pick_kslice_c<bf16_t>(c_type) : pick_kslice_c<f16_t>(c_type);
@@ -593,12 +700,13 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
   // matrix cores for 16-bit operands of one type (float32 A with bf16 B through the bf16 split);
   // the vector-ALU kernel for the rest. Operand rows must start on 16 bytes (d and k are
   // multiples of 8 elements).
-  if (a_type == GSI_BF16 && b_type == GSI_BF16) fn = pick_mfma_c<bf16_t, bf16_t>(c_type);
-  else if (a_type == GSI_F16 && b_type == GSI_F16) fn = pick_mfma_c<f16_t, f16_t>(c_type);
-  else if (a_type == GSI_F32 && b_type == GSI_BF16) fn = pick_mfma_c<float, bf16_t>(c_type);
+  fn = pick_mfma(a_type, b_type, c_type);
   if (fn) {
     dim3 grid((n + 63) / 64, (m + 63) / 64);
-    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+    int k_chunk = kdim;
+    float* part = nullptr;
+    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity,
+                    &k_chunk, &part};
     hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
@@ -612,6 +720,40 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
   void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
   hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
   return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// Split-K variant for products with few output tiles and a long K (the batched fast and slow
+// paths): the register-fed matrix-core kernel over S chunks of K, raw sums into part
+// ([S, m, n] float32, at least part_elems long), then their sum in chunk order into C. Falls back
+// to launch_gemm_nt when the types have no matrix-core kernel or S would be 1.
+int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
+                         const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n,
+                         int kdim, const int* m_count, float* part, long long part_elems, hipStream_t s) {
+  if (m <= 0 || n <= 0) return GSI_OK;
+  void* fn = pick_mfma(a_type, b_type, c_type);
+  const long long tiles = (long long)((n + 63) / 64) * ((m + 63) / 64);
+  // about 1024 blocks, at least 256 K columns (8 steps) per chunk, at most kMaxSplit chunks
+  int splits = (int)std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles - 1) / tiles));
+  splits = std::min(splits, std::max(1, kdim / 256));
+  while (splits > 1 && (long long)splits * m * n > part_elems) --splits;
+  if (!fn || splits < 2 || !part)
+    return launch_gemm_nt(a_type, b_type, c_type, A, lda, a_idx, B, ldb, C, ldc, c_idx, m, n, kdim, m_count, 0, s);
+  int k_chunk = ((kdim + splits - 1) / splits + 31) / 32 * 32;
+  splits = (kdim + k_chunk - 1) / k_chunk;
+  int sub_identity = 0;
+  void* fn_out = pick_mfma(a_type, b_type, GSI_F32);
+  dim3 grid((n + 63) / 64, (m + 63) / 64, splits);
+  void* c_unused = part;       // the kernel writes part when it is given, never C
+  long long ldc_unused = n;
+  void* args[] = {&A, &lda, &a_idx, &B, &ldb, &c_unused, &ldc_unused, &c_idx, &m, &n, &kdim, &m_count,
+                  &sub_identity, &k_chunk, &part};
+  if (hipLaunchKernel(fn_out, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+  void* rf = pick_reduce(c_type);
+  if (!rf) return GSI_ERR_DTYPE;
+  const float* cpart = part;
+  void* rargs[] = {&cpart, &splits, &m, &n, &m_count, &C, &ldc, &c_idx};
+  dim3 rgrid((unsigned)std::min(16, (n + 255) / 256), m);
+  return hipLaunchKernel(rf, rgrid, dim3(256), rargs, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -733,18 +875,21 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
   if (threadIdx.x == 0) { counts[0] = base[0]; counts[1] = base[1]; }
 }
 
-size_t batched_ws_bytes(int k, int T) {
-  return 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4);
+size_t batched_ws_bytes(int k, int T, int d_out) {
+  return 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
+         align256(split_part_elems(T, d_out) * 4);
 }
-BatchedWs batched_ws_carve(void* base, int k, int T) {
+BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   char* p = (char*)base;
   BatchedWs w;
+  w.part_elems = split_part_elems(T, d_out);
   w.G = (float*)p; p += align256((size_t)T * k * 4);
   w.H = (float*)p; p += align256((size_t)T * k * 4);
   w.nx2 = (float*)p; p += align256((size_t)T * 4);
   w.fast_idx = (int*)p; p += align256((size_t)T * 4);
   w.slow_idx = (int*)p; p += align256((size_t)T * 4);
-  w.counts = (int*)p;
+  w.counts = (int*)p; p += align256(2 * 4);
+  w.part = w.part_elems ? (float*)p : nullptr;
   return w;
 }
 

@@ -164,9 +164,17 @@ struct BatchedWs {
   int* fast_idx; // [T]
   int* slow_idx; // [T]
   int* counts;   // [2]
+  float* part;   // [kMaxSplit, T, d_out] split-K partial sums of the fast and slow products
+  long long part_elems;
 };
-size_t batched_ws_bytes(int k, int T);
-BatchedWs batched_ws_carve(void* base, int k, int T);
+constexpr int kMaxSplit = 8;  // K chunks of a split product
+// partial-sum elements the batched path may use (none when every call runs one token)
+inline long long split_part_elems(int T, int d_out) { return T > 1 ? (long long)kMaxSplit * T * d_out : 0; }
+size_t batched_ws_bytes(int k, int T, int d_out);
+BatchedWs batched_ws_carve(void* base, int k, int T, int d_out);
+int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
+                         const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n,
+                         int kdim, const int* m_count, float* part, long long part_elems, hipStream_t s);
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s);
 
