@@ -499,17 +499,20 @@ template <typename T, typename TC>
 __global__ __launch_bounds__(256) void gemm_nt_kslice_kernel(const void* __restrict__ A, long long lda,
                                                              const void* __restrict__ B, long long ldb,
                                                              void* __restrict__ C, long long ldc, int m, int n,
-                                                             int kdim, int sub_identity) {
-  __shared__ mf32x4 part[3][64];
+                                                             int kdim, int sub_identity, int k_chunk,
+                                                             float* __restrict__ part) {
+  __shared__ mf32x4 part_w[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tm = blockIdx.y * 16, tn = blockIdx.x * 16;
   const int ra = min(tm + (lane & 15), m - 1), rb = min(tn + (lane & 15), n - 1);
   const mu32x4* pa = reinterpret_cast<const mu32x4*>(reinterpret_cast<const T*>(A) + (long long)ra * lda) + (lane >> 4);
   const mu32x4* pb = reinterpret_cast<const mu32x4*>(reinterpret_cast<const T*>(B) + (long long)rb * ldb) + (lane >> 4);
-  const int nk = kdim / 32;  // a K step is 4 chunks of 16 bytes per row
+  // K steps of 32 columns (4 chunks of 16 bytes per row) of this block's K chunk (split K: block
+  // z takes [z k_chunk, (z + 1) k_chunk) and writes its raw sums to part[z])
+  const int s_end = min(kdim, (int)(blockIdx.z + 1) * k_chunk) / 32;
   mf32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  int s = wave;
-  for (; s + 28 < nk; s += 32) {
+  int s = (int)blockIdx.z * k_chunk / 32 + wave;
+  for (; s + 28 < s_end; s += 32) {
     mu32x4 a[8], b[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -522,19 +525,23 @@ __global__ __launch_bounds__(256) void gemm_nt_kslice_kernel(const void* __restr
       acc1 = mfma_op<T>::run(a[u + 1], b[u + 1], acc1);
     }
   }
-  for (; s < nk; s += 4) acc0 = mfma_op<T>::run(pa[s * 4], pb[s * 4], acc0);
+  for (; s < s_end; s += 4) acc0 = mfma_op<T>::run(pa[s * 4], pb[s * 4], acc0);
   mf32x4 acc = acc0 + acc1;
-  if (wave > 0) part[wave - 1][lane] = acc;
+  if (wave > 0) part_w[wave - 1][lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    acc = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+    acc = ((acc + part_w[0][lane]) + part_w[1][lane]) + part_w[2][lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = tm + 4 * (lane >> 4) + r, nn = tn + (lane & 15);
       if (mm >= m || nn >= n) continue;
-      float v = acc[r];
-      if (sub_identity && mm == nn) v -= 1.0f;
-      st_from_f32<TC>(C, (long long)mm * ldc + nn, v);
+      if (part) {
+        part[((long long)blockIdx.z * m + mm) * n + nn] = acc[r];
+      } else {
+        float v = acc[r];
+        if (sub_identity && mm == nn) v -= 1.0f;
+        st_from_f32<TC>(C, (long long)mm * ldc + nn, v);
+      }
     }
   }
 }
@@ -613,30 +620,36 @@ static void* pick_mfma(int a_type, int b_type, int c_type) {
 
 // ---------------------------------------------------------------------------------------------
 // Small float32 NT GEMM on the vector ALU (the batched G (V^T V - I), T x k x k): one 16x16
-// output tile per block, one output per thread, K staged through LDS 64 columns at a time;
-// each output is a fixed-order sum.
+// output tile per block, one output per thread. K is staged through LDS 512 columns at a time
+// (one load phase for k <= 512, so the product waits for memory once); each output is a
+// fixed-order sum.
 // ---------------------------------------------------------------------------------------------
+constexpr int kSmallK = 512;
 __global__ __launch_bounds__(256) void gemm_nt_small_f32_kernel(const float* __restrict__ A, long long lda,
                                                                 const float* __restrict__ B, long long ldb,
                                                                 float* __restrict__ C, long long ldc, int m, int n,
                                                                 int kdim) {
-  __shared__ float As[16][65], Bs[16][65];
+  // rows padded by 4 floats: the 16 rows of B read at one K index fall in 16 different banks
+  __shared__ float As[16][kSmallK + 4], Bs[16][kSmallK + 4];
   const int tm = blockIdx.y * 16, tn = blockIdx.x * 16;
   const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
   float acc = 0.f;
-  for (int k0 = 0; k0 < kdim; k0 += 64) {
-    // 16 rows x 64 columns of each operand: 4 elements per thread
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = threadIdx.x + 256 * e, rr = idx >> 6, kk = idx & 63;
-      const int ra = min(tm + rr, m - 1), rb = min(tn + rr, n - 1);
-      const bool kin = k0 + kk < kdim;
-      As[rr][kk] = kin ? A[(long long)ra * lda + k0 + kk] : 0.f;
-      Bs[rr][kk] = kin ? B[(long long)rb * ldb + k0 + kk] : 0.f;
+  for (int k0 = 0; k0 < kdim; k0 += kSmallK) {
+    const int kn = min(kSmallK, kdim - k0);  // a multiple of 4 (kdim is a multiple of 8)
+    // 16 rows x kn columns of each operand as float4: kn / 4 per row
+    for (int idx = threadIdx.x; idx < 16 * (kSmallK / 4); idx += 256) {
+      const int rr = idx / (kSmallK / 4), q = idx % (kSmallK / 4);
+      if (4 * q < kn) {
+        const int ra = min(tm + rr, m - 1), rb = min(tn + rr, n - 1);
+        const float4 va = *reinterpret_cast<const float4*>(A + (long long)ra * lda + k0 + 4 * q);
+        const float4 vb = *reinterpret_cast<const float4*>(B + (long long)rb * ldb + k0 + 4 * q);
+        As[rr][4 * q] = va.x; As[rr][4 * q + 1] = va.y; As[rr][4 * q + 2] = va.z; As[rr][4 * q + 3] = va.w;
+        Bs[rr][4 * q] = vb.x; Bs[rr][4 * q + 1] = vb.y; Bs[rr][4 * q + 2] = vb.z; Bs[rr][4 * q + 3] = vb.w;
+      }
     }
     __syncthreads();
-#pragma unroll 16
-    for (int kk = 0; kk < 64; ++kk) acc = __builtin_fmaf(As[r][kk], Bs[c][kk], acc);
+#pragma unroll 8
+    for (int kk = 0; kk < kn; ++kk) acc = __builtin_fmaf(As[r][kk], Bs[c][kk], acc);
     __syncthreads();
   }
   if (tm + r < m && tn + c < n) C[(long long)(tm + r) * ldc + tn + c] = acc;
@@ -670,7 +683,9 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
     fn = a_type == GSI_BF16 ? pick_kslice_c<bf16_t>(c_type) : pick_kslice_c<f16_t>(c_type);
     if (!fn) return GSI_ERR_DTYPE;
     dim3 grid((n + 15) / 16, (m + 15) / 16);
-    void* args[] = {&A, &lda, &B, &ldb, &C, &ldc, &m, &n, &kdim, &sub_identity};
+    int k_chunk = kdim;
+    float* part = nullptr;
+    void* args[] = {&A, &lda, &B, &ldb, &C, &ldc, &m, &n, &kdim, &sub_identity, &k_chunk, &part};
     hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
@@ -730,6 +745,32 @@ int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long
                          const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n,
                          int kdim, const int* m_count, float* part, long long part_elems, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
+  const bool same16 = a_type == b_type && (a_type == GSI_BF16 || a_type == GSI_F16);
+  if (same16 && kdim % 32 == 0 && kdim >= 1024 && !a_idx && !c_idx && !m_count && m <= 1024 && n <= 1024 && part) {
+    // 16x16 tiles with K split over the four waves of a block and over blocks
+    const long long tiles16 = (long long)((n + 15) / 16) * ((m + 15) / 16);
+    int splits = (int)std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles16 - 1) / tiles16));
+    splits = std::min(splits, std::max(1, kdim / 512));
+    while (splits > 1 && (long long)splits * m * n > part_elems) --splits;
+    if (splits > 1) {
+      void* kf = a_type == GSI_BF16 ? pick_kslice_c<bf16_t>(GSI_F32) : pick_kslice_c<f16_t>(GSI_F32);
+      int k_chunk = ((kdim + splits - 1) / splits + 31) / 32 * 32;
+      splits = (kdim + k_chunk - 1) / k_chunk;
+      int sub_identity = 0;
+      void* c_unused = part;
+      long long ldc_unused = n;
+      dim3 grid((n + 15) / 16, (m + 15) / 16, splits);
+      void* args[] = {&A, &lda, &B, &ldb, &c_unused, &ldc_unused, &m, &n, &kdim, &sub_identity, &k_chunk, &part};
+      if (hipLaunchKernel(kf, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+      void* rf = pick_reduce(c_type);
+      if (!rf) return GSI_ERR_DTYPE;
+      const float* cpart = part;
+      const int* no_count = nullptr;
+      void* rargs[] = {&cpart, &splits, &m, &n, &no_count, &C, &ldc, &c_idx};
+      dim3 rgrid((unsigned)std::min(16, (n + 255) / 256), m);
+      return hipLaunchKernel(rf, rgrid, dim3(256), rargs, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+    }
+  }
   void* fn = pick_mfma(a_type, b_type, c_type);
   const long long tiles = (long long)((n + 63) / 64) * ((m + 63) / 64);
   // about 1024 blocks, at least 256 K columns (8 steps) per chunk, at most kMaxSplit chunks
@@ -896,8 +937,8 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s) {
   // G = X V as X (V^T)^T: [T, k] float32
-  int rc = launch_gemm_nt(dtype, dtype, GSI_F32, X, x_ld, nullptr, L.Vt, L.d, w.G, L.k, nullptr, T, L.k, L.d,
-                          nullptr, 0, s);
+  int rc = launch_gemm_nt_split(dtype, dtype, GSI_F32, X, x_ld, nullptr, L.Vt, L.d, w.G, L.k, nullptr, T, L.k, L.d,
+                                nullptr, w.part, w.part_elems, s);
   if (rc != GSI_OK) return rc;
   // H = G (V^T V - I)  (the matrix is symmetric, so its rows serve as the K-contiguous operand)
   rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.G, L.k, nullptr, L.Dl, L.k, w.H, L.k, nullptr, T, L.k, L.k,
