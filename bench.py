@@ -10,6 +10,11 @@ HBM; the timed region is `--steps` tokens after `--warmup` tokens. The roofline 
 the decode kernel against the 8 TB/s HBM peak using the algorithmic bytes of the realised gates
 (per token and site: V_k, plus M, plus W when the gate is slow), measured with HIP events on the
 kernel's stream. The CPU baseline times the fp64 oracle on a bounded sample (see --cpu-seconds).
+The line also carries the create-time precompute (M = W V_k and V_k^T V_k - I) at k = 256 and
+at k = 512 as matrix-core TFLOP/s, and the bandwidth of an in-repo streaming-read kernel.
+
+`--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
+batched path and prints its own line (tokens/s and algorithmic GB/s).
 """
 from __future__ import annotations
 
