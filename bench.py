@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--reps", type=int, default=3, help="timed repetitions (the median is reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="operating-point sweep on the GPT-J-shaped stack: rank k x fast fraction, "
+                         "against a dense batch-1 GEMV chain (prints its own line)")
+    ap.add_argument("--sweep-ranks", default="64,128,256,512")
     return ap.parse_args()
 
 
@@ -70,6 +74,9 @@ def main():
     torch.cuda.set_device(0)
     if g.gsi_device_check() != 0:
         raise SystemExit("not a gfx950 device")
+    if args.sweep:
+        sweep(args, g, torch, np)
+        return
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
         batched(args, cfg, g, torch, np)
@@ -285,6 +292,128 @@ def batched(args, cfg, g, torch, np):
         "sites_with_slow_tokens": round(float(any_slow.mean()), 4),
         "cpu_baseline": None,
     }
+    print(json.dumps(out), flush=True)
+
+
+def sweep(args, g, torch, np):
+    """Operating-point sweep on the GPT-J-shaped stack (28 blocks x QKV / out / fc_in / fc_out,
+    bf16, batch 1, eps = 0.10): for each rank k and each planned fast fraction f (fixed slow
+    counts out of 512 tokens per site), decode tokens/s through the persistent decode kernel,
+    next to a dense batch-1 chain (torch linear, i.e. the vendor BLAS GEMV, y = W x for all 112
+    sites in order) on the same weights. Per point the line gives the measured speedup over the
+    dense chain and three read-ratio models: the pages' (f M + (1 - f) W against W, the model
+    their 3.0x / 10.5x / 15.6x fit), the same with V_k's reads added, and the bytes this kernel
+    reads (V_k + M always, since M g is formed before the gate is known, plus W when slow).
+
+    Inputs: block 0's four sites get their own bases and tokens per rank (synth sweep configs);
+    blocks 1..27 hold device copies of block 0's V and tokens at their own addresses, and every
+    (block, site) has its own seeded Gaussian W drawn on the GPU. Timing is what differs from the
+    headline run, not the values, so the copies stream from HBM like distinct data (the 11.3 GB
+    of W per token is far above the 256 MB last-level cache)."""
+    import dataclasses
+
+    from synth.configs import SWEEP_SLOW_COUNTS, SlowPlan, sweep_config
+    from synth.generate import site_basis, site_tokens, store
+
+    ranks = [int(v) for v in args.sweep_ranks.split(",") if v]
+    base = sweep_config(ranks[0])
+    n_blocks, shapes = base.n_blocks, base.sites
+    n_tok = base.n_steps
+    bf16 = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6000)
+    Ws = []
+    for b in range(n_blocks):
+        for st in shapes:
+            w = torch.randn((st.d_out, st.d), generator=gen, device="cuda")
+            Ws.append((w * base.w_std).to(bf16))
+            del w
+    torch.cuda.synchronize()
+    w_bytes = np.array([st.d_out * st.d * 2 for st in shapes] * n_blocks, dtype=np.float64)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+
+    # ---- dense baseline: y = W x for every site in order, one token at a time ----
+    xs = [torch.randn((1, st.d), generator=gen, device="cuda").to(bf16) for st in shapes]
+    F = torch.nn.functional
+
+    def dense(tokens):
+        for _ in range(tokens):
+            for i, W in enumerate(Ws):
+                F.linear(xs[i % len(shapes)], W)
+
+    dense(4)
+    torch.cuda.synchronize()
+    n_dense = 64
+    ev0.record(stream)
+    dense(n_dense)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_dense = ev0.elapsed_time(ev1) / 1e3 / n_dense
+    dense_tok_s = 1.0 / t_dense
+    log(f"[sweep] dense chain: {dense_tok_s:.1f} tokens/s, {w_bytes.sum() / t_dense / 1e9:.0f} GB/s")
+    rows = []
+    for k in ranks:
+        cfg = sweep_config(k)
+        t0 = time.time()
+        bases = [site_basis(cfg, 0, s) for s in range(len(shapes))]
+        Vd = [store(v, cfg.dtype).cuda() for v, _ in bases]
+        layers, keep = [], []
+        for b in range(n_blocks):
+            for s in range(len(shapes)):
+                V = Vd[s] if b == 0 else Vd[s].clone()
+                layers.append(g.create_layer(Ws[b * len(shapes) + s], V))
+                keep.append(V)
+        stack = g.gsi_stack_create(layers)
+        torch.cuda.synchronize()
+        v_bytes = np.array([st.d * k * 2 for st in shapes] * n_blocks, dtype=np.float64)
+        m_bytes = np.array([st.d_out * k * 2 for st in shapes] * n_blocks, dtype=np.float64)
+        ws = g.new_workspace(g.gsi_stack_workspace_bytes(stack, 1))
+        y_ld = sum(st.d_out for st in shapes) * n_blocks
+        Y = torch.zeros((n_tok, y_ld), dtype=bf16, device="cuda")
+        gates = torch.zeros((n_tok, len(layers)), dtype=torch.uint8, device="cuda")
+        log(f"[sweep] k={k}: bases and layers in {time.time() - t0:.1f}s")
+        for n_slow in SWEEP_SLOW_COUNTS:
+            c = dataclasses.replace(cfg, slow=SlowPlan("fixed", count=n_slow))
+            blk = torch.cat([site_tokens(c, 0, s, basis=bases[s])[0] for s in range(len(shapes))], dim=1).cuda()
+            X = blk.repeat(1, n_blocks).contiguous()
+            del blk
+            steps = n_tok if n_slow <= n_tok // 4 else 64
+            g.gsi_stack_decode(stack, X, 32, 1, cfg.eps, Y, gates, None, ws, stream)  # warm-up
+            times = []
+            for _ in range(3):
+                ev0.record(stream)
+                g.gsi_stack_decode(stack, X, steps, 1, cfg.eps, Y, gates, None, ws, stream)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                times.append(ev0.elapsed_time(ev1) / 1e3)
+            if g.gsi_workspace_status(ws) != 0:
+                raise SystemExit("decode kernel reported a wait timeout")
+            t = sorted(times)[1] / steps
+            slow = gates[:steps].cpu().numpy().astype(np.float64)          # [steps, sites]
+            f = 1.0 - float(slow.mean())
+            kernel_bytes = float(np.sum(v_bytes + m_bytes) + np.sum(slow.mean(axis=0) * w_bytes))
+            pages_bytes = float(np.sum(f * m_bytes + (1.0 - f) * w_bytes))
+            vinc_bytes = pages_bytes + float(np.sum(v_bytes))
+            rows.append({"k": k, "planned_slow_per_512": n_slow, "fast_fraction": round(f, 5),
+                         "tokens_s": round(1.0 / t, 1), "ms_per_token": round(t * 1e3, 4),
+                         "kernel_gbps": round(kernel_bytes / t / 1e9, 1),
+                         "speedup_vs_dense": round(t_dense / t, 3),
+                         "model_pages_read_ratio": round(float(w_bytes.sum()) / pages_bytes, 3),
+                         "model_with_vk": round(float(w_bytes.sum()) / vinc_bytes, 3),
+                         "model_kernel_bytes": round(float(w_bytes.sum()) / kernel_bytes, 3)})
+            log(f"[sweep] {rows[-1]}")
+            del X
+        del stack, layers, keep, Vd, ws, Y, gates
+        torch.cuda.synchronize()
+    out = {"metric": "GSI operating-point sweep: batch-1 decode tokens/s vs rank k and fast fraction, "
+                     "GPT-J-6B-shaped stack", "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"gptj-6b-shaped sweep: {n_blocks} blocks x 4 sites, eps=0.1, batch 1, "
+                                  f"{n_tok} tokens per site"},
+           "dense": {"tokens_s": round(dense_tok_s, 1), "ms_per_token": round(t_dense * 1e3, 4),
+                     "gbps": round(float(w_bytes.sum()) / t_dense / 1e9, 1),
+                     "what": "torch linear (vendor BLAS) y = W x, 112 sites in order, batch 1"},
+           "rows": rows}
     print(json.dumps(out), flush=True)
 
 

@@ -95,3 +95,21 @@ CONFIGS = {
 
 def get(cid: int) -> Config:
     return CONFIGS[cid]
+
+
+SWEEP_RANKS = (64, 128, 256, 512)
+# slow tokens per site out of 512: fast fractions 1, 0.998 (the GPT-J operating point), 0.949,
+# 0.85, 0.5 and 0
+SWEEP_SLOW_COUNTS = (0, 1, 26, 77, 256, 512)
+
+
+def sweep_config(k: int) -> Config:
+    """The GPT-J-shaped stack at rank k and eps = 0.10, for the operating-point sweep (registered
+    under its own id, so every rank has its own bases and tokens). The slow plan is replaced per
+    sweep point with dataclasses.replace(cfg, slow=SlowPlan("fixed", count=n))."""
+    cid = 600 + k
+    if cid not in CONFIGS:
+        CONFIGS[cid] = Config(cid, f"gptj-6b-sweep-k{k}-bf16", "bf16", 28, GPTJ_SITES, k=k, eps=0.10,
+                              t_step=1, n_steps=512, slow=SlowPlan("fixed", count=1), w_std=0.02,
+                              notes="operating-point sweep: rank k, fixed slow count per site")
+    return CONFIGS[cid]

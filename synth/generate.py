@@ -173,10 +173,11 @@ def planned_ratios(cfg: Config, block: int, site: int, n_steps: int | None = Non
     return rho, slow
 
 
-def site_tokens(cfg: Config, block: int, site: int, n_steps: int | None = None):
-    """Tokens for one site: (X stored [steps*t_step, d], planned slow mask [steps*t_step], rho*)."""
-    shp = cfg.sites[site]
-    v, c = site_basis(cfg, block, site)
+def site_tokens(cfg: Config, block: int, site: int, n_steps: int | None = None, basis=None):
+    """Tokens for one site: (X stored [steps*t_step, d], planned slow mask [steps*t_step], rho*).
+
+    `basis` = (V_k, C) from site_basis(cfg, block, site), when the caller already holds it."""
+    v, c = site_basis(cfg, block, site) if basis is None else basis
     rho, slow = planned_ratios(cfg, block, site, n_steps)
     n = rho.size
     rng = _rng(cfg.cid, block, site, _S_TOKENS)

@@ -100,3 +100,23 @@ def test_seeds_reproducible():
     assert w1.equal(w2)
     c = synth.site_inputs(cfg, 3, 2)
     assert not a.X[:, :8].equal(c.X[:, :8])
+
+
+@pytest.mark.parametrize("k", [64, 128, 256, 512])
+def test_sweep_points_margins(k):
+    """Operating-point sweep inputs (GPT-J-shaped sites at rank k): at every slow count, the
+    realised gates equal the plan, with the 1e-3 margin, so the fast fraction is the one planned."""
+    import dataclasses
+    from synth.configs import SWEEP_SLOW_COUNTS, SlowPlan, sweep_config
+    from synth.generate import site_basis, site_tokens
+    cfg = sweep_config(k)
+    for site in range(4):
+        basis = site_basis(cfg, 0, site)
+        V = synth.store(basis[0], cfg.dtype)
+        for n_slow in SWEEP_SLOW_COUNTS:
+            c = dataclasses.replace(cfg, slow=SlowPlan("fixed", count=n_slow))
+            X, planned, _ = site_tokens(c, 0, site, basis=basis)
+            out = orc.gate_only(V, X, cfg.eps)
+            assert np.all(np.abs(out["rho"] - cfg.eps) > 1e-3), (k, site, n_slow)
+            assert np.array_equal(out["gate"].astype(bool), planned)
+            assert int(out["gate"].sum()) == n_slow
