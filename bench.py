@@ -52,6 +52,10 @@ def parse():
                     help="operating-point sweep on the GPT-J-shaped stack: rank k x fast fraction, "
                          "against a dense batch-1 GEMV chain (prints its own line)")
     ap.add_argument("--sweep-ranks", default="64,128,256,512")
+    ap.add_argument("--calibration", action="store_true",
+                    help="depth-cascade calibration of the bases on the GPT-J-shaped chain (prints its own line)")
+    ap.add_argument("--cal-cold", type=int, default=8, help="subspace-iteration steps of a cold start")
+    ap.add_argument("--cal-warm", type=int, default=2, help="steps of a cascade (warm) start")
     return ap.parse_args()
 
 
@@ -76,6 +80,9 @@ def main():
         raise SystemExit("not a gfx950 device")
     if args.sweep:
         sweep(args, g, torch, np)
+        return
+    if args.calibration:
+        calibration(args, g, torch, np)
         return
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
@@ -414,6 +421,97 @@ def sweep(args, g, torch, np):
                      "gbps": round(float(w_bytes.sum()) / t_dense / 1e9, 1),
                      "what": "torch linear (vendor BLAS) y = W x, 112 sites in order, batch 1"},
            "rows": rows}
+    print(json.dumps(out), flush=True)
+
+
+def calibration(args, g, torch, np):
+    """Calibration of the bases with the depth cascade [GSI §2.3] on the GPT-J-shaped chain:
+    28 layers of 2048 calibration tokens x 4096 (float32), k = 256, planted subspaces 25 degrees
+    apart. Three ways, each timed with HIP events on the GPU:
+      cascade  layer 0 from a Gaussian start (--cal-cold steps), every later layer from the
+               previous layer's basis (--cal-warm steps);
+      cold     every layer from the Gaussian start (--cal-cold steps);
+      svd      a full SVD of every layer's activation matrix (torch.linalg.svd, the vendor
+               solver), timed on a sample of layers and scaled to 28.
+    Accuracy: the largest principal sine of each basis against the leading right singular
+    vectors of that layer's SVD (the exact subspace) on the sampled layers, and against the
+    planted basis on every layer. Bytes and flops per subspace-iteration step: the two float32
+    products read A twice (2 n d 4 B) and do 4 n d k flops; the Gram-Schmidt kernel re-reads the
+    earlier rows, k^2 d 4 B per projection pass."""
+    import math
+
+    from oracle import gsi_calibration as cal
+    from synth.calibration import GPTJ_CALIBRATION as c
+    from synth.calibration import activations, cold_start, planted_bases
+
+    t0 = time.time()
+    P = planted_bases(c)
+    As = [activations(c, l, P[l]).cuda() for l in range(c.n_layers)]
+    Om = cold_start(c).cuda()
+    log(f"[calibration] generated {c.n_layers} layers of {c.n} x {c.d} in {time.time() - t0:.1f}s")
+    ws = torch.empty(g.gsi_calibrate_workspace_bytes(c.n, c.d, c.k), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((c.k, c.d), dtype=torch.float32, device="cuda") for _ in range(c.n_layers)]
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()  # warm-up (first launches)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3
+
+    def cascade():
+        for l in range(c.n_layers):
+            g.gsi_calibrate(As[l], Om if l == 0 else outs[l - 1], args.cal_cold if l == 0 else args.cal_warm,
+                            outs[l], ws)
+
+    def cold():
+        for l in range(c.n_layers):
+            g.gsi_calibrate(As[l], Om, args.cal_cold, outs[l], ws)
+
+    def one_step():
+        g.gsi_calibrate(As[0], Om, 1, outs[0], ws)
+
+    t_step = timed(one_step)
+    t_cold = timed(cold)
+    sines_cold = [cal.principal_sines(P[l], outs[l].double().cpu().numpy().T)[0] for l in range(c.n_layers)]
+    cold_q = {l: outs[l].double().cpu().numpy().T for l in (0, 1, c.n_layers - 1)}
+    t_cascade = timed(cascade)
+    casc_q = [outs[l].double().cpu().numpy().T for l in range(c.n_layers)]
+    sines_casc = [cal.principal_sines(P[l], casc_q[l])[0] for l in range(c.n_layers)]
+    sample = [0, 1, c.n_layers - 1]
+    svd_t = []
+    exact = {}
+    for l in sample:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        _, _, vh = torch.linalg.svd(As[l], full_matrices=False)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        svd_t.append(ev0.elapsed_time(ev1) / 1e3)
+        exact[l] = vh[: c.k].double().cpu().numpy().T
+    t_svd = float(np.median(svd_t)) * c.n_layers
+    acc = {f"layer_{l}": {"cascade_vs_exact": float(cal.principal_sines(exact[l], casc_q[l])[0]),
+                          "cold_vs_exact": float(cal.principal_sines(exact[l], cold_q[l])[0]),
+                          "exact_vs_planted": float(cal.principal_sines(P[l], exact[l])[0])} for l in sample}
+    step_bytes = 2.0 * c.n * c.d * 4
+    step_flop = 4.0 * c.n * c.d * c.k
+    out = {"metric": "GSI basis calibration with the depth cascade: GPU time for all layers, GPT-J-shaped chain",
+           "unit": "s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"calibration chain: {c.n_layers} layers, {c.n} tokens x d={c.d}, k={c.k}, "
+                                  f"planted subspaces {c.theta_deg} degrees apart, cold {args.cal_cold} steps, "
+                                  f"warm {args.cal_warm} steps"},
+           "cascade_s": round(t_cascade, 4), "cold_every_layer_s": round(t_cold, 4),
+           "svd_every_layer_s": round(t_svd, 4), "svd_sampled_layers_s": [round(v, 4) for v in svd_t],
+           "cascade_saving_vs_svd": round(1.0 - t_cascade / t_svd, 4),
+           "cascade_saving_vs_cold": round(1.0 - t_cascade / t_cold, 4),
+           "step_ms": round(t_step * 1e3, 3),
+           "step_products": {"bytes": step_bytes, "flop": step_flop},
+           "accuracy": acc,
+           "max_sine_vs_planted": {"cascade": round(float(max(sines_casc)), 5), "cold": round(float(max(sines_cold)), 5)}}
     print(json.dumps(out), flush=True)
 
 

@@ -4,6 +4,6 @@ The compute path is libgsi (hand-written HIP kernels behind the C ABI in include
 package only marshals arguments to it. Importing it without the built library raises.
 """
 from ._binding import (GSI_BF16, GSI_F16, GSI_F32, GSI_OK, LIB_PATH, SIGNATURES, STATUS_NAMES, GsiError,  # noqa: F401
-                       Layer, Stack, create_layer, dtype_code, gsi_device_check, gsi_forward, gsi_layer_aux_bytes,
-                       gsi_layer_create, gsi_stack_create, gsi_stack_decode, gsi_stack_workspace_bytes,
+                       Layer, Stack, create_layer, dtype_code, gsi_calibrate, gsi_calibrate_workspace_bytes,
+                       gsi_device_check, gsi_forward, gsi_layer_aux_bytes, gsi_layer_create, gsi_stack_create, gsi_stack_decode, gsi_stack_workspace_bytes,
                        gsi_workspace_bytes, gsi_workspace_status, layer_image, lib, new_workspace)

@@ -39,6 +39,8 @@ SIGNATURES = [
     ("gsi_stack_workspace_bytes", _sz, [_vp, _int]),
     ("gsi_stack_decode", _int, [_vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp, _sz, _vp]),
     ("gsi_workspace_status", _int, [_vp, _sz, ctypes.POINTER(_int), _vp]),
+    ("gsi_calibrate_workspace_bytes", _sz, [_int, _int, _int]),
+    ("gsi_calibrate", _int, [_int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp]),
 ]
 
 
@@ -171,6 +173,20 @@ def gsi_workspace_status(ws: torch.Tensor, stream=None) -> int:
     rc = lib.gsi_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(out), _stream(stream))
     _check(rc, "gsi_workspace_status")
     return out.value
+
+
+def gsi_calibrate_workspace_bytes(n: int, d: int, k: int) -> int:
+    return lib.gsi_calibrate_workspace_bytes(n, d, k)
+
+
+def gsi_calibrate(A: torch.Tensor, Q0t: torch.Tensor, n_iter: int, Qt: torch.Tensor, ws: torch.Tensor,
+                  stream=None) -> None:
+    """Subspace iteration with DGKS Gram-Schmidt on the GPU: A [n, d] float32, Q0t and Qt [k, d]."""
+    n, d = A.shape
+    k = Q0t.shape[0]
+    rc = lib.gsi_calibrate(n, d, k, _ptr(A), _ptr(Q0t), int(n_iter), _ptr(Qt), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "gsi_calibrate")
 
 
 # ------------------------------------------------------------------------------------------------

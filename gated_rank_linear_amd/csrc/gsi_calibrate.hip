@@ -1,0 +1,181 @@
+// Calibration of a layer's activation basis V_k on the GPU, with the depth cascade.
+//
+// Method: "Gated Subspace Inference for transformer acceleration" technical summary
+// (gist.science, arXiv 2605.03109), §2.3 (depth cascade and calibration): a layer's basis is
+// computed once from a calibration forward pass; the next layer's basis starts from this one
+// and needs only a few rank-1 (DGKS) corrections instead of a full SVD per layer.
+//
+// One calibration call runs n_iter steps of subspace iteration
+//     Q <- orth(A^T (A Q)),   A [n, d] calibration activations (one token per row)
+// where orth is Gram-Schmidt over the columns in order, each column projected against the
+// orthonormal columns before it (a rank-1 extension of the factor) and projected a second time
+// when the first projection leaves less than eta = 1/sqrt(2) of its norm (the Daniel-Gragg-
+// Kaufman-Stewart criterion). The start Q0 is a Gaussian draw for the first layer and the
+// previous layer's basis for the cascade. Bases are stored by rows: Qt [k, d], row j = column j.
+//
+// Kernels: the two products run on the float32 NT GEMM of the dense path (Zt = Qt A^T, then
+// Yt = Zt (A^T)^T with A^T transposed once per call); the orthonormalisation is one workgroup,
+// since column j depends on every column before it.
+#include <cmath>
+
+#include "gsi_internal.h"
+
+namespace gsi {
+namespace {
+
+constexpr int kOrthThreads = 1024;
+constexpr int kOrthWaves = kOrthThreads / 64;
+constexpr int kOrthMaxD = 16384;  // the working column lives in LDS (64 KB)
+constexpr int kOrthMaxK = 512;
+constexpr int kCalMaxIter = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup in a fixed order (butterflies inside each wave, then the wave sums in
+// index order); every thread receives the result. Also a barrier for LDS and global memory.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();  // red is free, and every write before this call is visible after the next
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kOrthWaves; ++i) s += red[i];
+  return s;
+}
+
+// Gram-Schmidt with DGKS reorthogonalisation over the k rows of Y (each d long), result in Q
+// (a different buffer). Column j: v = y_j; h_i = <q_i, v> for i < j (one wave per i); v -= sum
+// h_i q_i (one thread per element, fixed order over i); a second projection when |v|^2 fell
+// below eta2 of its value before; q_j = v / |v|. Rows of Q are written before any later column
+// reads them (the barrier at the end of each column orders them).
+__global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __restrict__ Y, float* Q, int k, int d,
+                                                                 float eta2) {
+  __shared__ float v[kOrthMaxD];
+  __shared__ float h[kOrthMaxK];
+  __shared__ float red[kOrthWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int j = 0; j < k; ++j) {
+    const float* y = Y + (long long)j * d;
+    float s = 0.f;
+    for (int e = tid; e < d; e += kOrthThreads) {
+      const float a = y[e];
+      v[e] = a;
+      s = __builtin_fmaf(a, a, s);
+    }
+    const float before = block_sum(s, red);
+    float after = before;
+    for (int pass = 0; pass < 2 && j > 0; ++pass) {
+      for (int i = wave; i < j; i += kOrthWaves) {
+        const float* q = Q + (long long)i * d;
+        float a = 0.f;
+        for (int e = lane; e < d; e += 64) a = __builtin_fmaf(q[e], v[e], a);
+        a = wave_sum(a);
+        if (lane == 0) h[i] = a;
+      }
+      __syncthreads();
+      float s2 = 0.f;
+      for (int e = tid; e < d; e += kOrthThreads) {
+        float acc = 0.f;
+        for (int i = 0; i < j; ++i) acc = __builtin_fmaf(h[i], Q[(long long)i * d + e], acc);
+        const float a = v[e] - acc;
+        v[e] = a;
+        s2 = __builtin_fmaf(a, a, s2);
+      }
+      after = block_sum(s2, red);
+      if (!(after < eta2 * before)) break;  // enough of the column survived one projection
+    }
+    const float inv = 1.0f / sqrtf(after);
+    float* q = Q + (long long)j * d;
+    for (int e = tid; e < d; e += kOrthThreads) q[e] = v[e] * inv;
+    __syncthreads();
+  }
+}
+
+struct CalWs {
+  float* At;  // [d, n]
+  float* Zt;  // [k, n]
+  float* Yt;  // [k, d]
+};
+
+size_t cal_ws_bytes(int n, int d, int k) {
+  return align256((size_t)d * n * 4) + align256((size_t)k * n * 4) + align256((size_t)k * d * 4);
+}
+
+CalWs cal_ws_carve(void* ws, int n, int d, int k) {
+  char* c = (char*)ws;
+  CalWs w;
+  w.At = (float*)c;
+  c += align256((size_t)d * n * 4);
+  w.Zt = (float*)c;
+  c += align256((size_t)k * n * 4);
+  w.Yt = (float*)c;
+  return w;
+}
+
+int cal_shape(int n, int d, int k, int n_iter) {
+  if (k < 8 || k > kOrthMaxK) return GSI_ERR_SHAPE;
+  if (d < k || d > kOrthMaxD || d % 8 != 0) return GSI_ERR_SHAPE;
+  if (n < k || n % 8 != 0 || n > (1 << 20)) return GSI_ERR_SHAPE;
+  if (n_iter < 1 || n_iter > kCalMaxIter) return GSI_ERR_SHAPE;
+  return GSI_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+}  // namespace gsi
+
+using namespace gsi;
+
+extern "C" {
+
+size_t gsi_calibrate_workspace_bytes(int n, int d, int k) {
+  if (cal_shape(n, d, k, 1) != GSI_OK) return 0;
+  return cal_ws_bytes(n, d, k);
+}
+
+int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_iter, float* Qt, void* ws,
+                  size_t ws_bytes, void* stream) {
+  int rc = cal_shape(n, d, k, n_iter);
+  if (rc != GSI_OK) return rc;
+  if (!A || !Q0t || !Qt || !ws) return GSI_ERR_NULL;
+  if (!aligned16(A) || !aligned16(Q0t) || !aligned16(Qt) || !aligned16(ws)) return GSI_ERR_ALIGN;
+  if (ws_bytes < cal_ws_bytes(n, d, k)) return GSI_ERR_WORKSPACE;
+  // the result must not overlap the inputs it is computed from, except Qt == Q0t exactly
+  const char* qa = (const char*)Qt;
+  const char* qe = qa + (size_t)k * d * 4;
+  const char* aa = (const char*)A;
+  const char* ae = aa + (size_t)n * d * 4;
+  const char* wa = (const char*)ws;
+  const char* we = wa + cal_ws_bytes(n, d, k);
+  const char* sa = (const char*)Q0t;
+  const char* se = sa + (size_t)k * d * 4;
+  if ((qa < ae && aa < qe) || (qa < we && wa < qe) || (sa != qa && qa < se && sa < qe)) return GSI_ERR_SHAPE;
+  if ((rc = gsi_device_check()) != GSI_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const CalWs w = cal_ws_carve(ws, n, d, k);
+  // A^T [d, n] once per call: the second product contracts over the tokens
+  if ((rc = launch_transpose(GSI_F32, A, w.At, n, d, s)) != GSI_OK) return rc;
+  const float eta2 = 0.5f;  // eta = 1/sqrt(2)
+  for (int it = 0; it < n_iter; ++it) {
+    const float* Qin = it == 0 ? Q0t : Qt;
+    // Zt [k, n] = Qt A^T: row j holds (A q_j)^T
+    if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, Qin, d, nullptr, A, d, w.Zt, n, nullptr, k, n, d, nullptr, 0,
+                             s)) != GSI_OK)
+      return rc;
+    // Yt [k, d] = Zt A: row j holds (A^T A q_j)^T
+    if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.Zt, n, nullptr, w.At, n, w.Yt, d, nullptr, k, d, n, nullptr,
+                             0, s)) != GSI_OK)
+      return rc;
+    dgks_rows_kernel<<<1, kOrthThreads, 0, s>>>(w.Yt, Qt, k, d, eta2);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+  }
+  return GSI_OK;
+}
+
+}  // extern "C"

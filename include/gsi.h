@@ -138,6 +138,31 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
  */
 int gsi_workspace_status(void* ws, size_t ws_bytes, int* host_status, void* stream);
 
+/*
+ * Calibration of a layer's activation basis with the depth cascade [GSI §2.3]: the basis is
+ * computed once from calibration activations (one forward pass over a representative sequence);
+ * the basis of layer l + 1 starts from the basis of layer l and is corrected by a few rank-1
+ * (DGKS) updates instead of a full SVD per layer.
+ *
+ * gsi_calibrate runs n_iter (1..64) steps of subspace iteration  Q <- orth(A^T (A Q))  from the
+ * start Q0, where orth is Gram-Schmidt over the columns in order (each column projected against
+ * the orthonormal columns before it, and a second time when the first projection leaves less
+ * than 1/sqrt(2) of its norm: the Daniel-Gragg-Kaufman-Stewart criterion). All float32:
+ *   A    [n, d]  calibration activations, one token per row (device)
+ *   Q0t  [k, d]  start basis BY ROWS (row j = column j of Q0): a Gaussian draw for the first
+ *                layer, the previous layer's calibrated basis for the cascade (device)
+ *   Qt   [k, d]  result by rows, orthonormal rows spanning the k-dimensional leading subspace of
+ *                A^T A as far as n_iter steps reach it (device). Qt may be Q0t itself; it must
+ *                not overlap A or the workspace otherwise (GSI_ERR_SHAPE).
+ * Shapes: 8 <= k <= 512, k <= d <= 16384 with d a multiple of 8, k <= n <= 2^20 with n a multiple
+ * of 8. The basis is used by the layer as V = transpose(Qt), rounded to the weight dtype by the
+ * caller. The workspace (gsi_calibrate_workspace_bytes, no zero-fill needed) holds A^T and the
+ * two products; calls on one workspace must not overlap. Enqueues on `stream` and returns.
+ */
+size_t gsi_calibrate_workspace_bytes(int n, int d, int k);
+int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_iter, float* Qt, void* ws,
+                  size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,3 +83,30 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         g._binding._ptr(torch.zeros(4))
+
+
+@pytest.mark.parametrize("n,d,k,ok", [
+    (2048, 4096, 256, True), (512, 16384, 512, True), (64, 64, 8, True), (2048, 4096, 4, False),
+    (2048, 4096, 1024, False), (2048, 32768, 256, False), (2048, 4100, 256, False), (100, 4096, 256, False),
+    (2044, 4096, 256, False), ((1 << 20) + 8, 64, 8, False),
+])
+def test_calibrate_workspace_sizes(n, d, k, ok):
+    w = lib.gsi_calibrate_workspace_bytes(n, d, k)
+    if ok:
+        assert w >= 4 * (d * n + k * n + k * d)
+    else:
+        assert w == 0
+
+
+def test_calibrate_rejects_before_the_device():
+    n, d, k = 64, 64, 8
+    ws = lib.gsi_calibrate_workspace_bytes(n, d, k)
+    A, Q0, Q, W = 1 << 20, 2 << 20, 3 << 20, 4 << 20   # never dereferenced: every call fails first
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 0, Q, W, ws, None) == -2          # n_iter < 1
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 65, Q, W, ws, None) == -2         # n_iter > 64
+    assert lib.gsi_calibrate(n, d, k, None, Q0, 1, Q, W, ws, None) == -1
+    assert lib.gsi_calibrate(n, d, k, A + 4, Q0, 1, Q, W, ws, None) == -6
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 1, Q, W, ws - 1, None) == -5
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 1, A + 256, W, ws, None) == -2    # result overlaps A
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 1, Q0 + 16, W, ws, None) == -2    # partial overlap with Q0
+    assert lib.gsi_calibrate(n, d, k, A, Q0, 1, W, W, ws, None) == -2          # result overlaps workspace
