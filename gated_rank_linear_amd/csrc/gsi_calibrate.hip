@@ -48,18 +48,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Gram-Schmidt with DGKS reorthogonalisation over the k rows of Y (each d long), result in Q
-// (a different buffer). Column j: v = y_j; h_i = <q_i, v> for i < j (one wave per i); v -= sum
-// h_i q_i (one thread per element, fixed order over i); a second projection when |v|^2 fell
-// below eta2 of its value before; q_j = v / |v|. Rows of Q are written before any later column
-// reads them (the barrier at the end of each column orders them).
-__global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __restrict__ Y, float* Q, int k, int d,
-                                                                 float eta2) {
+// Gram-Schmidt with DGKS reorthogonalisation over rows j0 <= j < j1 of Y (each d long), result
+// in the same rows of Q (a different buffer), each row projected against the rows i0 <= i < j of
+// Q. Column j: v = y_j; h_i = <q_i, v> (one wave per i); v -= sum h_i q_i (one thread per
+// element, fixed order over i); a second projection when |v|^2 fell below eta2 of its value
+// before; q_j = v / |v|. Rows of Q are written before any later column reads them (the barrier
+// at the end of each column orders them).
+__global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __restrict__ Y, float* Q, int j0, int j1,
+                                                                 int i0, int d, float eta2) {
   __shared__ float v[kOrthMaxD];
   __shared__ float h[kOrthMaxK];
   __shared__ float red[kOrthWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int j = 0; j < k; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const float* y = Y + (long long)j * d;
     float s = 0.f;
     for (int e = tid; e < d; e += kOrthThreads) {
@@ -69,19 +70,19 @@ __global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __
     }
     const float before = block_sum(s, red);
     float after = before;
-    for (int pass = 0; pass < 2 && j > 0; ++pass) {
-      for (int i = wave; i < j; i += kOrthWaves) {
+    for (int pass = 0; pass < 2 && j > i0; ++pass) {
+      for (int i = i0 + wave; i < j; i += kOrthWaves) {
         const float* q = Q + (long long)i * d;
         float a = 0.f;
         for (int e = lane; e < d; e += 64) a = __builtin_fmaf(q[e], v[e], a);
         a = wave_sum(a);
-        if (lane == 0) h[i] = a;
+        if (lane == 0) h[i - i0] = a;
       }
       __syncthreads();
       float s2 = 0.f;
       for (int e = tid; e < d; e += kOrthThreads) {
         float acc = 0.f;
-        for (int i = 0; i < j; ++i) acc = __builtin_fmaf(h[i], Q[(long long)i * d + e], acc);
+        for (int i = i0; i < j; ++i) acc = __builtin_fmaf(h[i - i0], Q[(long long)i * d + e], acc);
         const float a = v[e] - acc;
         v[e] = a;
         s2 = __builtin_fmaf(a, a, s2);
@@ -96,14 +97,41 @@ __global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __
   }
 }
 
+// One projection of a panel of rows against every earlier row of Q, on the whole chip:
+// Y[r, e] -= sum_{i < p0} H[r, i] Q[i, e] for the `rows` rows of the panel, H = Y_panel Q^T
+// ([rows, p0], computed before by the NT GEMM). One thread per column e, the panel's rows of H
+// staged in LDS, fixed order over i.
+constexpr int kPanel = 16;
+__global__ __launch_bounds__(256) void panel_project_kernel(float* __restrict__ Y, const float* __restrict__ H,
+                                                            const float* __restrict__ Q, int rows, int p0, int d) {
+  __shared__ float hs[kPanel][kOrthMaxK];
+  for (int idx = threadIdx.x; idx < rows * p0; idx += 256) hs[idx / p0][idx % p0] = H[idx];
+  __syncthreads();
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= d) return;
+  float acc[kPanel];
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) acc[r] = 0.f;
+  for (int i = 0; i < p0; ++i) {
+    const float q = Q[(long long)i * d + e];
+#pragma unroll
+    for (int r = 0; r < kPanel; ++r) acc[r] = __builtin_fmaf(hs[r][i], q, acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r)
+    if (r < rows) Y[(long long)r * d + e] -= acc[r];
+}
+
 struct CalWs {
   float* At;  // [d, n]
   float* Zt;  // [k, n]
   float* Yt;  // [k, d]
+  float* H;   // [kPanel, k] projections of a panel on the earlier rows
 };
 
 size_t cal_ws_bytes(int n, int d, int k) {
-  return align256((size_t)d * n * 4) + align256((size_t)k * n * 4) + align256((size_t)k * d * 4);
+  return align256((size_t)d * n * 4) + align256((size_t)k * n * 4) + align256((size_t)k * d * 4) +
+         align256((size_t)kPanel * k * 4);
 }
 
 CalWs cal_ws_carve(void* ws, int n, int d, int k) {
@@ -114,6 +142,8 @@ CalWs cal_ws_carve(void* ws, int n, int d, int k) {
   w.Zt = (float*)c;
   c += align256((size_t)k * n * 4);
   w.Yt = (float*)c;
+  c += align256((size_t)k * d * 4);
+  w.H = (float*)c;
   return w;
 }
 
@@ -172,8 +202,22 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
     if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.Zt, n, nullptr, w.At, n, w.Yt, d, nullptr, k, d, n, nullptr,
                              0, s)) != GSI_OK)
       return rc;
-    dgks_rows_kernel<<<1, kOrthThreads, 0, s>>>(w.Yt, Qt, k, d, eta2);
-    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+    // orth(Yt) by panels of kPanel rows: each panel is projected against all earlier rows twice
+    // on the whole chip (the second projection is the DGKS reorthogonalisation, taken always),
+    // then Gram-Schmidt with the DGKS criterion runs inside the panel in one workgroup
+    for (int p0 = 0; p0 < k; p0 += kPanel) {
+      const int rows = k - p0 < kPanel ? k - p0 : kPanel;
+      float* Yp = w.Yt + (long long)p0 * d;
+      for (int pass = 0; pass < 2 && p0 > 0; ++pass) {
+        if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, Yp, d, nullptr, Qt, d, w.H, p0, nullptr, rows, p0, d,
+                                 nullptr, 0, s)) != GSI_OK)
+          return rc;
+        panel_project_kernel<<<(d + 255) / 256, 256, 0, s>>>(Yp, w.H, Qt, rows, p0, d);
+        if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+      }
+      dgks_rows_kernel<<<1, kOrthThreads, 0, s>>>(w.Yt, Qt, p0, p0 + rows, p0, d, eta2);
+      if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+    }
   }
   return GSI_OK;
 }

@@ -99,3 +99,30 @@ def test_in_place_and_reproducible(g):
     q = Om.clone()
     _gpu_calibrate(g, A, q, 3, out=q)
     assert torch.equal(a, b) and torch.equal(a, q)
+
+
+def test_reorthogonalisation_on_ill_conditioned_rows(g):
+    """With A = I (A^T A = I exactly in float32) one call orthonormalises Q0 itself. Q0's rows
+    are B S R (B orthonormal, S = diag from 1 to 1e-4, R a random rotation): condition number
+    1e4, so one Gram-Schmidt pass loses orthogonality (|Q Q^T - I| ~ u cond^2 ~ 0.2 in float32,
+    checked on the CPU) while the DGKS second projection keeps it at float32 rounding. The span
+    of every leading block of rows matches the oracle's within u times that block's condition
+    number (at most 1e4 here, so <= 1e-3)."""
+    d, k = 256, 48
+    rng = np.random.default_rng(5)
+    B = np.linalg.qr(rng.standard_normal((d, k)))[0]
+    R = np.linalg.qr(rng.standard_normal((k, k)))[0]
+    Q0 = torch.from_numpy((B @ np.diag(np.geomspace(1.0, 1e-4, k)) @ R).T.astype(np.float32).copy())
+    A = torch.eye(d, dtype=torch.float32)
+    say("case: calibration DGKS on ill-conditioned rows (A = I)")
+    Qt = _gpu_calibrate(g, A.cuda(), Q0.cuda(), 1)
+    Qg = Qt.double().cpu().numpy().T
+    orth = np.max(np.abs(Qg.T @ Qg - np.eye(k)))
+    say(f"  orthonormality {orth:.2e}")
+    assert orth <= 1e-5
+    ref, twice = cal.dgks_orthonormalize(Q0.double().numpy().T)
+    assert twice.sum() > k // 2
+    for j in (4, 16, 32, 48):
+        sin = cal.principal_sines(ref[:, :j], Qg[:, :j])[0]
+        say(f"  leading {j} rows: largest sine {sin:.2e}")
+        assert sin <= (1e-5 if j == 4 else 1e-3), j
