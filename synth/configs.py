@@ -71,6 +71,9 @@ class Config:
 GPT2_SITES = (Site("qkv", 768, 2304), Site("out", 768, 768), Site("fc", 768, 3072), Site("proj", 3072, 768))
 GPTJ_SITES = (Site("qkv", 4096, 12288), Site("out", 4096, 4096), Site("fc_in", 4096, 16384),
               Site("fc_out", 16384, 4096))
+# GPT-J's attention and MLP read the same block input (parallel residual), so q/k/v and fc_in can
+# share one basis, one g and one gate: a single site with the four projections stacked
+GPTJ_SHARED_SITES = (Site("qkv_fc_in", 4096, 28672), Site("out", 4096, 4096), Site("fc_out", 16384, 4096))
 OPT_SITES = (Site("qkv", 4096, 12288), Site("out", 4096, 4096), Site("fc1", 4096, 16384),
              Site("fc2", 16384, 4096))
 
@@ -90,6 +93,9 @@ CONFIGS = {
     5: Config(5, "gptj-6b-batched-bf16", "bf16", 28, GPTJ_SITES, k=512, eps=0.10,
               t_step=64, n_steps=200, slow=SlowPlan("binomial", p=0.2), w_std=0.02,
               token_pool_steps=20, notes="T=64 per step, Bin(64, 0.2) slow tokens per (site, step)"),
+    6: Config(6, "gptj-6b-shared-input-bf16", "bf16", 28, GPTJ_SHARED_SITES, k=256, eps=0.10,
+              t_step=1, n_steps=512, slow=SlowPlan("fixed", count=1), w_std=0.02,
+              notes="GPT-J-shaped stack with q/k/v and fc_in as one shared-input site (3 sites per block)"),
 }
 
 

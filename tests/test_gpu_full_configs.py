@@ -163,3 +163,19 @@ def test_precompute_tile_paths(g, dtype, shape):
     ref_g = orc.gate_only(V, X, eps)
     keep = np.abs(ref_g["rho"] - eps) > 1e-3
     assert np.array_equal(gate.cpu().numpy()[keep], ref_g["gate"][keep])
+
+
+def test_config6_shared_input_block(g):
+    """Shared-input sites: one GPT-J-shaped block whose q/k/v and fc_in form one 4096 -> 28672
+    site (one basis, one g, one gate), then out and fc_out; 64 batch-1 tokens, 1 slow per site."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.get(6), n_blocks=1, n_steps=64)
+    say("case: config 6 shared-input block (3 sites, QKV+fc_in 4096->28672), 64 tokens")
+    built = Built(cfg, blocks=[0], keep_w_for="all")
+    Y, gates, _, _ = decode(built, cfg.eps)
+    Ys = built.split_outputs(Y)
+    worst = 0.0
+    for i in range(len(built.sites)):
+        worst = max(worst, check_site(built, i, Ys[i], gates[:, i], cfg.eps, with_y=True))
+    say(f"  gates exact, worst y rel L2 {worst:.2e}")
+    assert worst <= TOL["bf16"]

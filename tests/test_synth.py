@@ -120,3 +120,12 @@ def test_sweep_points_margins(k):
             assert np.all(np.abs(out["rho"] - cfg.eps) > 1e-3), (k, site, n_slow)
             assert np.array_equal(out["gate"].astype(bool), planned)
             assert int(out["gate"].sum()) == n_slow
+
+
+def test_config6_shared_input_margins():
+    """The shared-input variant (q/k/v and fc_in stacked into one 4096 -> 28672 site)."""
+    cfg = synth.get(6)
+    assert [s.d_out for s in cfg.sites] == [28672, 4096, 4096]
+    for site in range(3):
+        si, out = _margin_check(cfg, 0, site)
+        assert int(out["gate"].sum()) == 1
