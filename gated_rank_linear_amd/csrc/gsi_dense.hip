@@ -356,6 +356,115 @@ __device__ __forceinline__ void skinny_tiles(const void* __restrict__ A, long lo
     }
 }
 
+// Fast product of the batched path (float32 g rows against bf16 M, at most 64 rows): the skinny
+// layout of gemm_nt_skinny_kernel, with the rows of A staged once per block through LDS. Per
+// sub-chunk of 256 K columns the block converts its A rows (mv valid, the rest zero) into bf16
+// high and low parts (|a - hi - lo| <= 2^-18 |a|) stored in the A-operand order of
+// v_mfma_f32_16x16x32_bf16 (row tile t, step s, lane l at ((t * 8 + s) * 64 + l)), so every
+// element is read from global memory and split once per block instead of once per wave and every
+// LDS read is one conflict-free 16-byte load; the eight steps of B (M) of a sub-chunk are loaded
+// before the products, and the next sub-chunk's before this one's products.
+template <int NRT>
+__device__ __forceinline__ void skinny_f32a_tiles(const float* __restrict__ A, long long lda,
+                                                  const int* __restrict__ a_idx, const bf16_t* __restrict__ B,
+                                                  long long ldb, int mv, int n, int kb, int ke,
+                                                  float* __restrict__ part, mu32x4* __restrict__ lds_hi,
+                                                  mu32x4* __restrict__ lds_lo) {
+  constexpr int kSteps = 8;  // 32-column steps per sub-chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int nn = blockIdx.x * 64 + wave * 16 + r16;
+  const bool bok = nn < n;
+  const long long brow = bok ? (long long)nn * ldb : 0;
+  mf32x4 acc[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) acc[t] = mf32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) {
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int kk = k0 + 32 * st + 8 * kq;
+      const bool kin = kk < ke;  // K bounds are multiples of 8: a chunk is all in or all out
+      const mu32x4 w = reinterpret_cast<const mu32x4*>(B + brow + (kin ? kk : kb))[0];
+      bv[st] = (bok && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  mu32x4 bcur[kSteps], bnxt[kSteps];
+  load_b(kb, bcur);
+  for (int k0 = kb; k0 < ke; k0 += 32 * kSteps) {
+    __syncthreads();  // the previous sub-chunk's A fragments are no longer read
+    // stage A: NRT * 8 * 64 fragments of 8 elements
+    for (int f = tid; f < NRT * kSteps * 64; f += 256) {
+      const int l = f & 63, st = (f >> 6) & (kSteps - 1), t = f >> 9;
+      const int mm = 16 * t + (l & 15);
+      const int kk = k0 + 32 * st + 8 * (l >> 4);
+      float v[8];
+      if (mm < mv && kk < ke) {
+        const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
+        const mu32x4* pa = reinterpret_cast<const mu32x4*>(A + row + kk);
+        const mu32x4 r0 = pa[0], r1 = pa[1];
+        const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(raw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+      unsigned short h[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16_t hb = from_f32<bf16_t>(v[e]);
+        const bf16_t lb = from_f32<bf16_t>(v[e] - to_f32(hb));
+        h[e] = hb.b;
+        lo[e] = lb.b;
+      }
+      lds_hi[f] = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
+                         h[6] | ((unsigned)h[7] << 16)};
+      lds_lo[f] = mu32x4{lo[0] | ((unsigned)lo[1] << 16), lo[2] | ((unsigned)lo[3] << 16),
+                         lo[4] | ((unsigned)lo[5] << 16), lo[6] | ((unsigned)lo[7] << 16)};
+    }
+    __syncthreads();
+    if (k0 + 32 * kSteps < ke) load_b(k0 + 32 * kSteps, bnxt);  // uniform
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+#pragma unroll
+      for (int t = 0; t < NRT; ++t) {
+        const int f = (t * kSteps + st) * 64 + lane;
+        acc[t] = mfma_op<bf16_t>::run(lds_hi[f], bcur[st], acc[t]);
+        acc[t] = mfma_op<bf16_t>::run(lds_lo[f], bcur[st], acc[t]);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) bcur[st] = bnxt[st];
+  }
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 16 * t + 4 * kq + r;
+      if (mm < mv && bok) part[(long long)mm * n + nn] = acc[t][r];
+    }
+}
+
+__global__ __launch_bounds__(256) void gemm_nt_skinny_f32a_kernel(const void* __restrict__ A, long long lda,
+                                                                  const int* __restrict__ a_idx,
+                                                                  const void* __restrict__ B, long long ldb, int m,
+                                                                  int n, int kdim, const int* __restrict__ m_count,
+                                                                  int k_chunk, float* __restrict__ part) {
+  __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[4 * 8 * 64];  // 64 KB
+  const int mv = m_count ? min(m, *m_count) : m;
+  if (mv <= 0) return;
+  const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
+  float* pz = part + (long long)blockIdx.z * m * n;
+  const float* a = reinterpret_cast<const float*>(A);
+  const bf16_t* b = reinterpret_cast<const bf16_t*>(B);
+  switch ((mv + 15) >> 4) {  // uniform
+    case 1: skinny_f32a_tiles<1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    case 2: skinny_f32a_tiles<2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    case 3: skinny_f32a_tiles<3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    default: skinny_f32a_tiles<4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+  }
+}
+
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void gemm_nt_skinny_kernel(const void* __restrict__ A, long long lda,
                                                              const int* __restrict__ a_idx,
@@ -902,7 +1011,7 @@ int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long
   if (m <= 64) {  // at most 64 rows (a token list): the skinny kernel, B loaded once per block
     void* sk = a_type == GSI_BF16 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_kernel<bf16_t, bf16_t>
                : a_type == GSI_F16 && b_type == GSI_F16 ? (void*)gemm_nt_skinny_kernel<f16_t, f16_t>
-               : a_type == GSI_F32 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_kernel<float, bf16_t>
+               : a_type == GSI_F32 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_f32a_kernel
                                                         : nullptr;
     if (sk) {
       dim3 grid((n + 63) / 64, 1, splits);
