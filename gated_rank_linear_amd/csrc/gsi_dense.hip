@@ -257,119 +257,25 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
 }
 
 // Skinny NT GEMM on the matrix cores for products with at most 64 rows of A whose count is a
-// device-side token count (the batched fast and slow products): a block covers 64 columns of C
-// and wave w the 16-column tile n0 + 16 w, so every element of B is loaded once per block; each
-// wave runs only the NRT = ceil(mv / 16) row tiles that hold valid rows (mv is uniform, read
-// once), so empty row tiles issue no loads and no products. K is split over blockIdx.z; the raw
-// float32 sums of a chunk go to part[z][mm][nn] (rows mm < mv), added later in chunk order.
-// Operand layouts as in gemm_nt_mfma_kernel (a float32 A is split into bf16 high and low parts).
+// device-side token count (the batched fast product, float32 g rows against bf16 M, and slow
+// product, 16-bit x rows against W): a block covers 64 columns of C and wave w the 16-column tile
+// n0 + 16 w, so every element of B is loaded once per block; each wave runs only the
+// NRT = ceil(mv / 16) row tiles that hold valid rows (mv is uniform, read once). The rows of A
+// are staged once per block through LDS. K is split over blockIdx.z; the raw float32 sums of a
+// chunk go to part[z][mm][nn] (rows mm < mv), added later in chunk order. Per sub-chunk of 256 K
+// columns the block copies its A rows (mv valid, the rest zero) into LDS, a float32 A split into
+// bf16 high and low parts (|a - hi - lo| <= 2^-18 |a|), stored in the A-operand order of
+// v_mfma_f32_16x16x32_{bf16,f16} (row tile t, step s, lane l at ((t * 8 + s) * 64 + l)), so every
+// element is read from global memory (and split) once per block instead of once per wave and
+// every LDS read is one conflict-free 16-byte load; the eight steps of B of a sub-chunk are
+// loaded before its products, and the next sub-chunk's before this one's products.
 template <typename TA, typename TB, int NRT>
-__device__ __forceinline__ void skinny_tiles(const void* __restrict__ A, long long lda, const int* __restrict__ a_idx,
-                                             const void* __restrict__ B, long long ldb, int mv, int n, int kb,
-                                             int ke, float* __restrict__ part) {
+__device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, long long lda,
+                                                    const int* __restrict__ a_idx, const TB* __restrict__ B,
+                                                    long long ldb, int mv, int n, int kb, int ke,
+                                                    float* __restrict__ part, mu32x4* __restrict__ lds_hi,
+                                                    mu32x4* __restrict__ lds_lo) {
   constexpr bool kSplit = sizeof(TA) == 4;
-  constexpr int kAC = kSplit ? 2 : 1;                       // 16-byte chunks of A per row tile and step
-  constexpr int kGroup = NRT * kAC + 1 <= 5 ? 4 : 2;        // K steps whose loads are issued together
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int nn = blockIdx.x * 64 + wave * 16 + r16;
-  const bool bok = nn < n;
-  const long long brow = bok ? (long long)nn * ldb : 0;
-  long long arow[NRT];
-  bool aok[NRT];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    const int mm = 16 * t + r16;
-    aok[t] = mm < mv;
-    arow[t] = aok[t] ? (long long)(a_idx ? a_idx[mm] : mm) * lda : 0;
-  }
-  mf32x4 acc[NRT];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) acc[t] = mf32x4{0.f, 0.f, 0.f, 0.f};
-  struct Frag {
-    mu32x4 a[NRT][kAC];
-    mu32x4 b;
-  };
-  auto load_step = [&](int k0, Frag& f) {
-    const int kk = k0 + kq * 8;
-    const bool kin = kk < ke;  // K bounds are multiples of 8: a chunk is all in or all out
-    const int kc = kin ? kk : kb;
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      const bool ok = aok[t] && kin;
-      if constexpr (kSplit) {
-        const mu32x4* pa = reinterpret_cast<const mu32x4*>(reinterpret_cast<const float*>(A) + arow[t] + kc);
-        f.a[t][0] = ok ? pa[0] : mu32x4{0u, 0u, 0u, 0u};
-        f.a[t][1] = ok ? pa[1] : mu32x4{0u, 0u, 0u, 0u};
-      } else {
-        const mu32x4 v = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TA*>(A) + arow[t] + kc)[0];
-        f.a[t][0] = ok ? v : mu32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    const mu32x4 w = reinterpret_cast<const mu32x4*>(reinterpret_cast<const TB*>(B) + brow + kc)[0];
-    f.b = (bok && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
-  };
-  auto compute_step = [&](const Frag& f) {
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      if constexpr (kSplit) {
-        const mu32x4 r0 = f.a[t][0], r1 = f.a[t][1];
-        const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-        unsigned short h[8], l[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = __uint_as_float(raw[e]);
-          const bf16_t hb = from_f32<bf16_t>(v);
-          const bf16_t lb = from_f32<bf16_t>(v - to_f32(hb));
-          h[e] = hb.b;
-          l[e] = lb.b;
-        }
-        const mu32x4 ah{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
-                        h[6] | ((unsigned)h[7] << 16)};
-        const mu32x4 al{l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16), l[4] | ((unsigned)l[5] << 16),
-                        l[6] | ((unsigned)l[7] << 16)};
-        acc[t] = mfma_op<TB>::run(ah, f.b, acc[t]);
-        acc[t] = mfma_op<TB>::run(al, f.b, acc[t]);
-      } else {
-        acc[t] = mfma_op<TB>::run(f.a[t][0], f.b, acc[t]);
-      }
-    }
-  };
-  Frag cur[kGroup], nxt[kGroup];
-#pragma unroll
-  for (int u = 0; u < kGroup; ++u) load_step(kb + 32 * u, cur[u]);
-  for (int k0 = kb; k0 < ke; k0 += 32 * kGroup) {
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) load_step(k0 + 32 * (kGroup + u), nxt[u]);
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) compute_step(cur[u]);
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) cur[u] = nxt[u];
-  }
-  // D of a 16x16 tile: lane l holds column l mod 16, rows 4 (l / 16) .. + 3
-#pragma unroll
-  for (int t = 0; t < NRT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int mm = 16 * t + 4 * kq + r;
-      if (mm < mv && bok) part[(long long)mm * n + nn] = acc[t][r];
-    }
-}
-
-// Fast product of the batched path (float32 g rows against bf16 M, at most 64 rows): the skinny
-// layout of gemm_nt_skinny_kernel, with the rows of A staged once per block through LDS. Per
-// sub-chunk of 256 K columns the block converts its A rows (mv valid, the rest zero) into bf16
-// high and low parts (|a - hi - lo| <= 2^-18 |a|) stored in the A-operand order of
-// v_mfma_f32_16x16x32_bf16 (row tile t, step s, lane l at ((t * 8 + s) * 64 + l)), so every
-// element is read from global memory and split once per block instead of once per wave and every
-// LDS read is one conflict-free 16-byte load; the eight steps of B (M) of a sub-chunk are loaded
-// before the products, and the next sub-chunk's before this one's products.
-template <int NRT>
-__device__ __forceinline__ void skinny_f32a_tiles(const float* __restrict__ A, long long lda,
-                                                  const int* __restrict__ a_idx, const bf16_t* __restrict__ B,
-                                                  long long ldb, int mv, int n, int kb, int ke,
-                                                  float* __restrict__ part, mu32x4* __restrict__ lds_hi,
-                                                  mu32x4* __restrict__ lds_lo) {
   constexpr int kSteps = 8;  // 32-column steps per sub-chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -397,30 +303,39 @@ __device__ __forceinline__ void skinny_f32a_tiles(const float* __restrict__ A, l
       const int l = f & 63, st = (f >> 6) & (kSteps - 1), t = f >> 9;
       const int mm = 16 * t + (l & 15);
       const int kk = k0 + 32 * st + 8 * (l >> 4);
-      float v[8];
-      if (mm < mv && kk < ke) {
-        const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
-        const mu32x4* pa = reinterpret_cast<const mu32x4*>(A + row + kk);
-        const mu32x4 r0 = pa[0], r1 = pa[1];
-        const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      if constexpr (kSplit) {
+        float v[8];
+        if (mm < mv && kk < ke) {
+          const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
+          const mu32x4* pa = reinterpret_cast<const mu32x4*>(A + row + kk);
+          const mu32x4 r0 = pa[0], r1 = pa[1];
+          const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(raw[e]);
+          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(raw[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+        unsigned short h[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bf16_t hb = from_f32<bf16_t>(v[e]);
+          const bf16_t lb = from_f32<bf16_t>(v[e] - to_f32(hb));
+          h[e] = hb.b;
+          lo[e] = lb.b;
+        }
+        lds_hi[f] = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16),
+                           h[4] | ((unsigned)h[5] << 16), h[6] | ((unsigned)h[7] << 16)};
+        lds_lo[f] = mu32x4{lo[0] | ((unsigned)lo[1] << 16), lo[2] | ((unsigned)lo[3] << 16),
+                           lo[4] | ((unsigned)lo[5] << 16), lo[6] | ((unsigned)lo[7] << 16)};
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        mu32x4 v = mu32x4{0u, 0u, 0u, 0u};
+        if (mm < mv && kk < ke) {
+          const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
+          v = reinterpret_cast<const mu32x4*>(A + row + kk)[0];
+        }
+        lds_hi[f] = v;
       }
-      unsigned short h[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bf16_t hb = from_f32<bf16_t>(v[e]);
-        const bf16_t lb = from_f32<bf16_t>(v[e] - to_f32(hb));
-        h[e] = hb.b;
-        lo[e] = lb.b;
-      }
-      lds_hi[f] = mu32x4{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
-                         h[6] | ((unsigned)h[7] << 16)};
-      lds_lo[f] = mu32x4{lo[0] | ((unsigned)lo[1] << 16), lo[2] | ((unsigned)lo[3] << 16),
-                         lo[4] | ((unsigned)lo[5] << 16), lo[6] | ((unsigned)lo[7] << 16)};
     }
     __syncthreads();
     if (k0 + 32 * kSteps < ke) load_b(k0 + 32 * kSteps, bnxt);  // uniform
@@ -429,8 +344,8 @@ __device__ __forceinline__ void skinny_f32a_tiles(const float* __restrict__ A, l
 #pragma unroll
       for (int t = 0; t < NRT; ++t) {
         const int f = (t * kSteps + st) * 64 + lane;
-        acc[t] = mfma_op<bf16_t>::run(lds_hi[f], bcur[st], acc[t]);
-        acc[t] = mfma_op<bf16_t>::run(lds_lo[f], bcur[st], acc[t]);
+        acc[t] = mfma_op<TB>::run(lds_hi[f], bcur[st], acc[t]);
+        if constexpr (kSplit) acc[t] = mfma_op<TB>::run(lds_lo[f], bcur[st], acc[t]);
       }
     }
 #pragma unroll
@@ -445,41 +360,25 @@ __device__ __forceinline__ void skinny_f32a_tiles(const float* __restrict__ A, l
     }
 }
 
-__global__ __launch_bounds__(256) void gemm_nt_skinny_f32a_kernel(const void* __restrict__ A, long long lda,
-                                                                  const int* __restrict__ a_idx,
-                                                                  const void* __restrict__ B, long long ldb, int m,
-                                                                  int n, int kdim, const int* __restrict__ m_count,
-                                                                  int k_chunk, float* __restrict__ part) {
-  __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[4 * 8 * 64];  // 64 KB
-  const int mv = m_count ? min(m, *m_count) : m;
-  if (mv <= 0) return;
-  const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
-  float* pz = part + (long long)blockIdx.z * m * n;
-  const float* a = reinterpret_cast<const float*>(A);
-  const bf16_t* b = reinterpret_cast<const bf16_t*>(B);
-  switch ((mv + 15) >> 4) {  // uniform
-    case 1: skinny_f32a_tiles<1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    case 2: skinny_f32a_tiles<2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    case 3: skinny_f32a_tiles<3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    default: skinny_f32a_tiles<4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-  }
-}
-
 template <typename TA, typename TB>
-__global__ __launch_bounds__(256) void gemm_nt_skinny_kernel(const void* __restrict__ A, long long lda,
-                                                             const int* __restrict__ a_idx,
-                                                             const void* __restrict__ B, long long ldb, int m, int n,
-                                                             int kdim, const int* __restrict__ m_count, int k_chunk,
-                                                             float* __restrict__ part) {
+__global__ __launch_bounds__(256) void gemm_nt_skinny_staged_kernel(const void* __restrict__ A, long long lda,
+                                                                    const int* __restrict__ a_idx,
+                                                                    const void* __restrict__ B, long long ldb, int m,
+                                                                    int n, int kdim, const int* __restrict__ m_count,
+                                                                    int k_chunk, float* __restrict__ part) {
+  constexpr bool kSplit = sizeof(TA) == 4;
+  __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[kSplit ? 4 * 8 * 64 : 1];  // 64 KB (32 KB for 16-bit A)
   const int mv = m_count ? min(m, *m_count) : m;
   if (mv <= 0) return;
   const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
   float* pz = part + (long long)blockIdx.z * m * n;
-  switch ((mv + 15) >> 4) {  // uniform: row tiles that hold valid rows
-    case 1: skinny_tiles<TA, TB, 1>(A, lda, a_idx, B, ldb, mv, n, kb, ke, pz); break;
-    case 2: skinny_tiles<TA, TB, 2>(A, lda, a_idx, B, ldb, mv, n, kb, ke, pz); break;
-    case 3: skinny_tiles<TA, TB, 3>(A, lda, a_idx, B, ldb, mv, n, kb, ke, pz); break;
-    default: skinny_tiles<TA, TB, 4>(A, lda, a_idx, B, ldb, mv, n, kb, ke, pz); break;
+  const TA* a = reinterpret_cast<const TA*>(A);
+  const TB* b = reinterpret_cast<const TB*>(B);
+  switch ((mv + 15) >> 4) {  // uniform
+    case 1: skinny_staged_tiles<TA, TB, 1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    case 2: skinny_staged_tiles<TA, TB, 2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    case 3: skinny_staged_tiles<TA, TB, 3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    default: skinny_staged_tiles<TA, TB, 4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
   }
 }
 
@@ -1009,9 +908,9 @@ int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long
   int k_chunk = ((kdim + splits - 1) / splits + 31) / 32 * 32;
   splits = (kdim + k_chunk - 1) / k_chunk;
   if (m <= 64) {  // at most 64 rows (a token list): the skinny kernel, B loaded once per block
-    void* sk = a_type == GSI_BF16 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_kernel<bf16_t, bf16_t>
-               : a_type == GSI_F16 && b_type == GSI_F16 ? (void*)gemm_nt_skinny_kernel<f16_t, f16_t>
-               : a_type == GSI_F32 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_f32a_kernel
+    void* sk = a_type == GSI_BF16 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_staged_kernel<bf16_t, bf16_t>
+               : a_type == GSI_F16 && b_type == GSI_F16 ? (void*)gemm_nt_skinny_staged_kernel<f16_t, f16_t>
+               : a_type == GSI_F32 && b_type == GSI_BF16 ? (void*)gemm_nt_skinny_staged_kernel<float, bf16_t>
                                                         : nullptr;
     if (sk) {
       dim3 grid((n + 63) / 64, 1, splits);
