@@ -179,3 +179,33 @@ def test_config6_shared_input_block(g):
         worst = max(worst, check_site(built, i, Ys[i], gates[:, i], cfg.eps, with_y=True))
     say(f"  gates exact, worst y rel L2 {worst:.2e}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("eps", [0.0, 1.5])
+def test_batched_all_slow_and_all_fast(g, dtype, eps):
+    """T = 64 through the batched path with every token slow (eps = 0: the slow product on all
+    four 16-row tiles, an empty fast list) or every token fast (eps = 1.5: the fast product on
+    four tiles, an empty slow list), against the oracle."""
+    d_out, d, k, T = 1000, 2048, 256, 64
+    rng = np.random.default_rng(71)
+    Q, R = np.linalg.qr(rng.standard_normal((d, k + 64)))
+    Q = Q * np.sign(np.diag(R))
+    W = torch.from_numpy(rng.standard_normal((d_out, d)) * 0.03).to(dtype)
+    V = torch.from_numpy(Q[:, :k]).to(dtype)
+    X = torch.from_numpy(_planned_tokens(rng, Q[:, :k], Q[:, k:], 0.1, T, 0.3)).to(dtype)
+    say(f"case: batched T=64, eps={eps}, {dtype}")
+    L = g.create_layer(W.cuda(), V.cuda())
+    y = torch.zeros((T, d_out), dtype=dtype, device="cuda")
+    gate = torch.full((T,), 9, dtype=torch.uint8, device="cuda")
+    ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, d_out, d, k, T))
+    g.gsi_forward(L, X.cuda().contiguous(), eps, y, gate, None, ws)
+    torch.cuda.synchronize()
+    assert g.gsi_workspace_status(ws) == 0
+    gb = gate.cpu().numpy()
+    assert np.all(gb == (1 if eps == 0.0 else 0))
+    ref = orc.forward(W, V, X, eps)
+    assert np.array_equal(gb, ref["gate"])
+    err = rel_l2(to_np(y), ref["y"])
+    say(f"  y rel L2 {err:.2e}")
+    assert err <= TOL["bf16"]
