@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kOrthThreads = 1024;
 constexpr int kOrthWaves = kOrthThreads / 64;
-constexpr int kOrthMaxD = 16384;  // the working column lives in LDS (64 KB)
+constexpr int kOrthMaxD = 16384;  // a thread holds at most 16 elements of a panel row
 constexpr int kOrthMaxK = 512;
 constexpr int kCalMaxIter = 64;
 
@@ -48,53 +48,94 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Gram-Schmidt with DGKS reorthogonalisation over rows j0 <= j < j1 of Y (each d long), result
-// in the same rows of Q (a different buffer), each row projected against the rows i0 <= i < j of
-// Q. Column j: v = y_j; h_i = <q_i, v> (one wave per i); v -= sum h_i q_i (one thread per
-// element, fixed order over i); a second projection when |v|^2 fell below eta2 of its value
-// before; q_j = v / |v|. Rows of Q are written before any later column reads them (the barrier
-// at the end of each column orders them).
-__global__ __launch_bounds__(kOrthThreads) void dgks_rows_kernel(const float* __restrict__ Y, float* Q, int j0, int j1,
-                                                                 int i0, int d, float eta2) {
-  __shared__ float v[kOrthMaxD];
-  __shared__ float h[kOrthMaxK];
-  __shared__ float red[kOrthWaves];
+// Gram-Schmidt with DGKS reorthogonalisation inside one panel of `rows` rows (j0 .. j0 + rows - 1
+// of Y, each d long), result in the same rows of Q (a different buffer). One workgroup; thread
+// tid holds elements tid + 1024 u (u < EPT) of every row of the panel in registers, so a column
+// costs workgroup sums only: v = y_j; h_i = <q_i, v> for the panel rows i < j (per-thread
+// partial products, then one fixed-order workgroup sum per i); v -= sum h_i q_i; a second
+// projection when |v|^2 fell below eta2 of its value before; q_j = v / |v|.
+template <int EPT>
+__global__ __launch_bounds__(kOrthThreads) void dgks_panel_kernel(const float* __restrict__ Y, float* __restrict__ Q,
+                                                                  int j0, int rows, int d, float eta2) {
+  constexpr int PMAX = EPT >= 8 ? 64 / EPT : 16;  // rows held per thread (registers)
+  __shared__ float red[PMAX][kOrthWaves];
+  __shared__ float h[PMAX];
+  __shared__ float nred[kOrthWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int j = j0; j < j1; ++j) {
-    const float* y = Y + (long long)j * d;
-    float s = 0.f;
-    for (int e = tid; e < d; e += kOrthThreads) {
-      const float a = y[e];
-      v[e] = a;
-      s = __builtin_fmaf(a, a, s);
+  float yv[PMAX][EPT];
+#pragma unroll
+  for (int r = 0; r < PMAX; ++r)
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = tid + kOrthThreads * u;
+      yv[r][u] = (r < rows && e < d) ? Y[(long long)(j0 + r) * d + e] : 0.f;
     }
-    const float before = block_sum(s, red);
+  auto norm2 = [&](const float (&v)[EPT]) {
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) s = __builtin_fmaf(v[u], v[u], s);
+    return block_sum(s, nred);
+  };
+#pragma clang loop unroll(full)
+  for (int j = 0; j < PMAX; ++j) {
+    if (j >= rows) continue;  // uniform
+    float v[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) v[u] = yv[j][u];
+    const float before = norm2(v);
     float after = before;
-    for (int pass = 0; pass < 2 && j > i0; ++pass) {
-      for (int i = i0 + wave; i < j; i += kOrthWaves) {
-        const float* q = Q + (long long)i * d;
-        float a = 0.f;
-        for (int e = lane; e < d; e += 64) a = __builtin_fmaf(q[e], v[e], a);
-        a = wave_sum(a);
-        if (lane == 0) h[i - i0] = a;
+    for (int pass = 0; pass < 2 && j > 0; ++pass) {
+      // h_i = <q_i, v>, i < j: per-thread partials, wave sums, then the wave sums in index order
+#pragma unroll
+      for (int i = 0; i < PMAX; ++i) {
+        if (i < j) {  // uniform
+          float a = 0.f;
+#pragma unroll
+          for (int u = 0; u < EPT; ++u) a = __builtin_fmaf(yv[i][u], v[u], a);
+          a = wave_sum(a);
+          if (lane == 0) red[i][wave] = a;
+        }
       }
       __syncthreads();
-      float s2 = 0.f;
-      for (int e = tid; e < d; e += kOrthThreads) {
-        float acc = 0.f;
-        for (int i = i0; i < j; ++i) acc = __builtin_fmaf(h[i - i0], Q[(long long)i * d + e], acc);
-        const float a = v[e] - acc;
-        v[e] = a;
-        s2 = __builtin_fmaf(a, a, s2);
+      if (tid < j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kOrthWaves; ++w) sum += red[tid][w];
+        h[tid] = sum;
       }
-      after = block_sum(s2, red);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < EPT; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < PMAX; ++i)
+          if (i < j) acc = __builtin_fmaf(h[i], yv[i][u], acc);
+        v[u] -= acc;
+      }
+      after = norm2(v);
       if (!(after < eta2 * before)) break;  // enough of the column survived one projection
     }
     const float inv = 1.0f / sqrtf(after);
-    float* q = Q + (long long)j * d;
-    for (int e = tid; e < d; e += kOrthThreads) q[e] = v[e] * inv;
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      yv[j][u] = v[u] * inv;
+      const int e = tid + kOrthThreads * u;
+      if (e < d) Q[(long long)(j0 + j) * d + e] = yv[j][u];
+    }
   }
+}
+
+// Rows per panel for a row length d: a thread holds ceil(d / 1024) elements of each panel row.
+int panel_rows(int d) { return d <= 4096 ? 16 : d <= 8192 ? 8 : 4; }
+
+int launch_dgks_panel(const float* Y, float* Q, int j0, int rows, int d, float eta2, hipStream_t s) {
+  const int ept = (d + kOrthThreads - 1) / kOrthThreads;
+  if (ept <= 1) dgks_panel_kernel<1><<<1, kOrthThreads, 0, s>>>(Y, Q, j0, rows, d, eta2);
+  else if (ept <= 2) dgks_panel_kernel<2><<<1, kOrthThreads, 0, s>>>(Y, Q, j0, rows, d, eta2);
+  else if (ept <= 4) dgks_panel_kernel<4><<<1, kOrthThreads, 0, s>>>(Y, Q, j0, rows, d, eta2);
+  else if (ept <= 8) dgks_panel_kernel<8><<<1, kOrthThreads, 0, s>>>(Y, Q, j0, rows, d, eta2);
+  else dgks_panel_kernel<16><<<1, kOrthThreads, 0, s>>>(Y, Q, j0, rows, d, eta2);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 // One projection of a panel of rows against every earlier row of Q, on the whole chip:
@@ -202,11 +243,12 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
     if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.Zt, n, nullptr, w.At, n, w.Yt, d, nullptr, k, d, n, nullptr,
                              0, s)) != GSI_OK)
       return rc;
-    // orth(Yt) by panels of kPanel rows: each panel is projected against all earlier rows twice
-    // on the whole chip (the second projection is the DGKS reorthogonalisation, taken always),
-    // then Gram-Schmidt with the DGKS criterion runs inside the panel in one workgroup
-    for (int p0 = 0; p0 < k; p0 += kPanel) {
-      const int rows = k - p0 < kPanel ? k - p0 : kPanel;
+    // orth(Yt) by panels of up to kPanel rows: each panel is projected against all earlier rows
+    // twice on the whole chip (the second projection is the DGKS reorthogonalisation, taken
+    // always), then Gram-Schmidt with the DGKS criterion runs inside the panel in one workgroup
+    const int panel = panel_rows(d);
+    for (int p0 = 0; p0 < k; p0 += panel) {
+      const int rows = k - p0 < panel ? k - p0 : panel;
       float* Yp = w.Yt + (long long)p0 * d;
       for (int pass = 0; pass < 2 && p0 > 0; ++pass) {
         if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, Yp, d, nullptr, Qt, d, w.H, p0, nullptr, rows, p0, d,
@@ -215,8 +257,7 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
         panel_project_kernel<<<(d + 255) / 256, 256, 0, s>>>(Yp, w.H, Qt, rows, p0, d);
         if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
       }
-      dgks_rows_kernel<<<1, kOrthThreads, 0, s>>>(w.Yt, Qt, p0, p0 + rows, p0, d, eta2);
-      if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+      if ((rc = launch_dgks_panel(w.Yt, Qt, p0, rows, d, eta2, s)) != GSI_OK) return rc;
     }
   }
   return GSI_OK;
