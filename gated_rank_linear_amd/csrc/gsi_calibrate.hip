@@ -14,8 +14,10 @@
 // previous layer's basis for the cascade. Bases are stored by rows: Qt [k, d], row j = column j.
 //
 // Kernels: the two products run on the float32 NT GEMM of the dense path (Zt = Qt A^T, then
-// Yt = Zt (A^T)^T with A^T transposed once per call); the orthonormalisation is one workgroup,
-// since column j depends on every column before it.
+// Yt = Zt (A^T)^T with A^T transposed once per call). The orthonormalisation goes by panels of
+// rows: each panel is projected against the earlier rows on the whole chip (H = Y_panel Q^T split
+// over K, then Y_panel -= H Q), and Gram-Schmidt inside the panel runs in one workgroup, since
+// column j depends on every column before it.
 #include <cmath>
 
 #include "gsi_internal.h"
@@ -168,11 +170,13 @@ struct CalWs {
   float* Zt;  // [k, n]
   float* Yt;  // [k, d]
   float* H;   // [kPanel, k] projections of a panel on the earlier rows
+  float* Hp;  // [kHSplits, kPanel, k] split-K partial sums of H
 };
+constexpr int kHSplits = 16;
 
 size_t cal_ws_bytes(int n, int d, int k) {
   return align256((size_t)d * n * 4) + align256((size_t)k * n * 4) + align256((size_t)k * d * 4) +
-         align256((size_t)kPanel * k * 4);
+         align256((size_t)kPanel * k * 4) + align256((size_t)kHSplits * kPanel * k * 4);
 }
 
 CalWs cal_ws_carve(void* ws, int n, int d, int k) {
@@ -185,6 +189,8 @@ CalWs cal_ws_carve(void* ws, int n, int d, int k) {
   w.Yt = (float*)c;
   c += align256((size_t)k * d * 4);
   w.H = (float*)c;
+  c += align256((size_t)kPanel * k * 4);
+  w.Hp = (float*)c;
   return w;
 }
 
@@ -251,8 +257,8 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
       const int rows = k - p0 < panel ? k - p0 : panel;
       float* Yp = w.Yt + (long long)p0 * d;
       for (int pass = 0; pass < 2 && p0 > 0; ++pass) {
-        if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, Yp, d, nullptr, Qt, d, w.H, p0, nullptr, rows, p0, d,
-                                 nullptr, 0, s)) != GSI_OK)
+        if ((rc = launch_gemm_nt_f32_splitk(Yp, d, Qt, d, w.H, p0, rows, p0, d, w.Hp,
+                                            (long long)kHSplits * kPanel * k, s)) != GSI_OK)
           return rc;
         panel_project_kernel<<<(d + 255) / 256, 256, 0, s>>>(Yp, w.H, Qt, rows, p0, d);
         if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;

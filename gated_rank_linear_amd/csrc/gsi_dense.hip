@@ -754,14 +754,16 @@ constexpr int kSmallK = 512;
 __global__ __launch_bounds__(256) void gemm_nt_small_f32_kernel(const float* __restrict__ A, long long lda,
                                                                 const float* __restrict__ B, long long ldb,
                                                                 float* __restrict__ C, long long ldc, int m, int n,
-                                                                int kdim) {
+                                                                int kdim, int k_chunk, float* __restrict__ part) {
   // rows padded by 4 floats: the 16 rows of B read at one K index fall in 16 different banks
   __shared__ float As[16][kSmallK + 4], Bs[16][kSmallK + 4];
   const int tm = blockIdx.y * 16, tn = blockIdx.x * 16;
   const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  // K split over blockIdx.z (raw sums of chunk z to part[z][m][n]) when part is given
+  const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
   float acc = 0.f;
-  for (int k0 = 0; k0 < kdim; k0 += kSmallK) {
-    const int kn = min(kSmallK, kdim - k0);  // a multiple of 4 (kdim is a multiple of 8)
+  for (int k0 = kb; k0 < ke; k0 += kSmallK) {
+    const int kn = min(kSmallK, ke - k0);  // a multiple of 4 (kdim and k_chunk are multiples of 8)
     // 16 rows x kn columns of each operand as float4: kn / 4 per row
     for (int idx = threadIdx.x; idx < 16 * (kSmallK / 4); idx += 256) {
       const int rr = idx / (kSmallK / 4), q = idx % (kSmallK / 4);
@@ -778,7 +780,12 @@ __global__ __launch_bounds__(256) void gemm_nt_small_f32_kernel(const float* __r
     for (int kk = 0; kk < kn; ++kk) acc = __builtin_fmaf(As[r][kk], Bs[c][kk], acc);
     __syncthreads();
   }
-  if (tm + r < m && tn + c < n) C[(long long)(tm + r) * ldc + tn + c] = acc;
+  if (tm + r < m && tn + c < n) {
+    if (part)
+      part[((long long)blockIdx.z * m + tm + r) * n + tn + c] = acc;
+    else
+      C[(long long)(tm + r) * ldc + tn + c] = acc;
+  }
 }
 
 static void* pick_reduce(int c_type) {
@@ -801,7 +808,7 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
       (long long)((m + 63) / 64) * ((n + 63) / 64) < 128) {
     dim3 grid((n + 15) / 16, (m + 15) / 16);
     gemm_nt_small_f32_kernel<<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, (float*)C, ldc, m, n,
-                                                 kdim);
+                                                 kdim, kdim, nullptr);
     return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
   // a small output with a long K and no row lists: one 16x16 tile per block, K split over 4 waves
@@ -861,6 +868,36 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
   void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
   hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
   return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// Float32 C[m, n] = A B^T for a small output with a long K (the calibration's projections of a
+// panel on the earlier rows): 16 x 16 tiles with K split into up to 16 chunks so that about 256
+// blocks run, raw sums per chunk into part ([splits, m, n], at least part_elems long), then
+// their sum in chunk order into C. One chunk (no reduction) when part is too small.
+int launch_gemm_nt_f32_splitk(const float* A, long long lda, const float* B, long long ldb, float* C, long long ldc,
+                              int m, int n, int kdim, float* part, long long part_elems, hipStream_t s) {
+  if (m <= 0 || n <= 0) return GSI_OK;
+  const long long tiles = (long long)((n + 15) / 16) * ((m + 15) / 16);
+  int splits = (int)std::min<long long>(16, std::max<long long>(1, (256 + tiles - 1) / tiles));
+  splits = std::min(splits, std::max(1, kdim / 256));
+  while (splits > 1 && (long long)splits * m * n > part_elems) --splits;
+  int k_chunk = ((kdim + splits - 1) / splits + 7) / 8 * 8;
+  splits = (kdim + k_chunk - 1) / k_chunk;
+  dim3 grid((n + 15) / 16, (m + 15) / 16, splits);
+  if (splits < 2 || !part) {
+    gemm_nt_small_f32_kernel<<<dim3(grid.x, grid.y), 256, 0, s>>>(A, lda, B, ldb, C, ldc, m, n, kdim, kdim, nullptr);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
+  gemm_nt_small_f32_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, C, ldc, m, n, kdim, k_chunk, part);
+  if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+  const float* cpart = part;
+  const int* no_count = nullptr;
+  const int* no_idx = nullptr;
+  void* Cv = C;
+  void* rargs[] = {&cpart, &splits, &m, &n, &no_count, &Cv, &ldc, &no_idx};
+  dim3 rgrid((unsigned)std::min(16, (n + 255) / 256), m);
+  return hipLaunchKernel((void*)splitk_reduce_kernel<float>, rgrid, dim3(256), rargs, 0, s) == hipSuccess ? GSI_OK
+                                                                                                     : GSI_ERR_HIP;
 }
 
 // Split-K variant for products with few output tiles and a long K (the batched fast and slow

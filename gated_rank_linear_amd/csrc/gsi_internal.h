@@ -156,6 +156,10 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
                    const int* m_count, int sub_identity, hipStream_t s);
 // dst[k, d] = transpose(src[d, k])
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s);
+// float32 C[m, n] = A B^T for a small output and a long K, K split over blocks (partial sums in
+// part, at least part_elems floats), reduced in chunk order
+int launch_gemm_nt_f32_splitk(const float* A, long long lda, const float* B, long long ldb, float* C, long long ldc,
+                              int m, int n, int kdim, float* part, long long part_elems, hipStream_t s);
 
 struct BatchedWs {
   float* G;      // [T, k]  g = V^T x per token
