@@ -61,9 +61,12 @@ def test_cascade_small_chain(g):
         _compare(Q, ref[l], f"layer {l}")
 
 
-@pytest.mark.parametrize("n,d,k,iters", [(200, 136, 24, 3), (64, 64, 8, 1), (1000, 520, 40, 2), (96, 264, 72, 5)])
+@pytest.mark.parametrize("n,d,k,iters", [(200, 136, 24, 3), (64, 64, 8, 1), (1000, 520, 40, 2), (96, 264, 72, 5),
+                                         (304, 2040, 40, 2), (256, 8192, 72, 1), (128, 6152, 20, 2)])
 def test_ragged_shapes(g, n, d, k, iters):
-    """Sizes off every tile (rows, columns and K tails of the products; k not a power of two)."""
+    """Sizes off every tile (rows, columns and K tails of the products; k not a power of two);
+    every width class of the in-panel Gram-Schmidt (1, 2, 4, 8 and 16 elements of a row per
+    thread: panels of 16, 16, 16, 8 and 4 rows), the ragged last panel included."""
     rng = np.random.default_rng(n + d + k)
     B = np.linalg.qr(rng.standard_normal((d, k)))[0]
     A = (rng.standard_normal((n, k)) * np.linspace(6, 3, k)) @ B.T + 0.3 * rng.standard_normal((n, d))
