@@ -209,3 +209,35 @@ def test_batched_all_slow_and_all_fast(g, dtype, eps):
     err = rel_l2(to_np(y), ref["y"])
     say(f"  y rel L2 {err:.2e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(64, 65536, 512), (262144, 64, 64)])
+def test_maximum_sizes(g, shape):
+    """The widest input the ABI accepts (d = 65536, at the largest rank 512: V rows and the input
+    row far beyond an LDS region and the register window) and the most output rows (d_out =
+    262144: 1024 rows of y per decode block, most of M read from HBM), bf16, per-token (T = 1, 3)
+    and batched (T = 17) paths, against the oracle."""
+    d_out, d, k = shape
+    rng = np.random.default_rng(d_out + d + k)
+    Q, R = np.linalg.qr(rng.standard_normal((d, min(d, k + 64))))
+    Q = Q * np.sign(np.diag(R))
+    V64, C64 = Q[:, :k], Q[:, k:]
+    W = torch.from_numpy((rng.standard_normal((d_out, d)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    V = torch.from_numpy(V64).to(torch.bfloat16)
+    eps = 0.2
+    say(f"case: maximum sizes {shape}")
+    L = g.create_layer(W.cuda(), V.cuda())
+    for T in (1, 3, 17):
+        X = torch.from_numpy(_planned_tokens(rng, V64, C64, eps, T, 0.4)).to(torch.bfloat16)
+        ref = orc.forward(W, V, X, eps)
+        keep = np.abs(orc.gate_only(V, X, eps)["rho"] - eps) > 1e-3
+        y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+        gate = torch.full((T,), 9, dtype=torch.uint8, device="cuda")
+        ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, d_out, d, k, T))
+        g.gsi_forward(L, X.cuda().contiguous(), eps, y, gate, None, ws)
+        torch.cuda.synchronize()
+        assert g.gsi_workspace_status(ws) == 0
+        assert np.array_equal(gate.cpu().numpy()[keep], ref["gate"][keep]), f"T={T}"
+        err = rel_l2(to_np(y)[keep], ref["y"][keep])
+        say(f"  T={T}: y rel L2 {err:.2e}")
+        assert err <= TOL["bf16"], f"T={T}: {err}"
