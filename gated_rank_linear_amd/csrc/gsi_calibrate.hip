@@ -171,12 +171,16 @@ struct CalWs {
   float* Yt;  // [k, d]
   float* H;   // [kPanel, k] projections of a panel on the earlier rows
   float* Hp;  // [kHSplits, kPanel, k] split-K partial sums of H
+  float* P;   // [kPSplits, k, max(n, d)] split-K partial sums of the token products
 };
 constexpr int kHSplits = 16;
+constexpr int kPSplits = 8;
+inline long long prod_part_elems(int n, int d, int k) { return (long long)kPSplits * k * (n > d ? n : d); }
 
 size_t cal_ws_bytes(int n, int d, int k) {
   return align256((size_t)d * n * 4) + align256((size_t)k * n * 4) + align256((size_t)k * d * 4) +
-         align256((size_t)kPanel * k * 4) + align256((size_t)kHSplits * kPanel * k * 4);
+         align256((size_t)kPanel * k * 4) + align256((size_t)kHSplits * kPanel * k * 4) +
+         align256((size_t)prod_part_elems(n, d, k) * 4);
 }
 
 CalWs cal_ws_carve(void* ws, int n, int d, int k) {
@@ -191,6 +195,8 @@ CalWs cal_ws_carve(void* ws, int n, int d, int k) {
   w.H = (float*)c;
   c += align256((size_t)kPanel * k * 4);
   w.Hp = (float*)c;
+  c += align256((size_t)kHSplits * kPanel * k * 4);
+  w.P = (float*)c;
   return w;
 }
 
@@ -242,13 +248,10 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
   for (int it = 0; it < n_iter; ++it) {
     const float* Qin = it == 0 ? Q0t : Qt;
     // Zt [k, n] = Qt A^T: row j holds (A q_j)^T
-    if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, Qin, d, nullptr, A, d, w.Zt, n, nullptr, k, n, d, nullptr, 0,
-                             s)) != GSI_OK)
-      return rc;
+    const long long pe = prod_part_elems(n, d, k);
+    if ((rc = launch_gemm_nt_f32_splitk(Qin, d, A, d, w.Zt, n, k, n, d, w.P, pe, s)) != GSI_OK) return rc;
     // Yt [k, d] = Zt A: row j holds (A^T A q_j)^T
-    if ((rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.Zt, n, nullptr, w.At, n, w.Yt, d, nullptr, k, d, n, nullptr,
-                             0, s)) != GSI_OK)
-      return rc;
+    if ((rc = launch_gemm_nt_f32_splitk(w.Zt, n, w.At, n, w.Yt, d, k, d, n, w.P, pe, s)) != GSI_OK) return rc;
     // orth(Yt) by panels of up to kPanel rows: each panel is projected against all earlier rows
     // twice on the whole chip (the second projection is the DGKS reorthogonalisation, taken
     // always), then Gram-Schmidt with the DGKS criterion runs inside the panel in one workgroup

@@ -870,13 +870,97 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
   return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
-// Float32 C[m, n] = A B^T for a small output with a long K (the calibration's projections of a
-// panel on the earlier rows): 16 x 16 tiles with K split into up to 16 chunks so that about 256
-// blocks run, raw sums per chunk into part ([splits, m, n], at least part_elems long), then
-// their sum in chunk order into C. One chunk (no reduction) when part is too small.
+// Float32 NT GEMM with K split over blockIdx.z (the calibration's token products, whose 64 x 64
+// tiles alone would not fill the chip): the tile scheme of gemm_nt_kernel over the columns
+// [z k_chunk, (z + 1) k_chunk), raw sums to part[z][m][n].
+__global__ __launch_bounds__(256) void gemm_nt_f32_tile64_kernel(const float* __restrict__ A, long long lda,
+                                                                 const float* __restrict__ B, long long ldb, int m,
+                                                                 int n, int kdim, int k_chunk,
+                                                                 float* __restrict__ part) {
+  __shared__ float As[GBK][GBM + 4];
+  __shared__ float Bs[GBK][GBN + 4];
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  const int kb = blockIdx.z * k_chunk, ke = min(kdim, kb + k_chunk);
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  const int lr = tid / 4, lk = (tid % 4) * 8;
+  const int am = m0 + lr, bn = n0 + lr;
+  const bool a_ok = am < m, b_ok = bn < n;
+  const float* arow = A + (long long)(a_ok ? am : 0) * lda;
+  const float* brow = B + (long long)(b_ok ? bn : 0) * ldb;
+  for (int k0 = kb; k0 < ke; k0 += GBK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kk = k0 + lk + e;
+      As[lk + e][lr] = (a_ok && kk < ke) ? arow[kk] : 0.f;
+      Bs[lk + e][lr] = (b_ok && kk < ke) ? brow[kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < GBK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* pz = part + (long long)blockIdx.z * m * n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mm = m0 + ty * 4 + i;
+    if (mm >= m) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nn = n0 + tx * 4 + j;
+      if (nn < n) pz[(long long)mm * n + nn] = acc[i][j];
+    }
+  }
+}
+
+// Float32 C[m, n] = A B^T with K split over blocks (the calibration's products): for a large
+// output 64 x 64 tiles in up to 8 K chunks, for a small output with a long K (a panel against the
+// earlier rows) 16 x 16 tiles in up to 16 chunks; raw sums per chunk into part ([splits, m, n], at
+// least part_elems long), then their sum in chunk order into C. One chunk (no reduction) when
+// part is too small.
 int launch_gemm_nt_f32_splitk(const float* A, long long lda, const float* B, long long ldb, float* C, long long ldc,
                               int m, int n, int kdim, float* part, long long part_elems, hipStream_t s) {
   if (m <= 0 || n <= 0) return GSI_OK;
+  const long long tiles64 = (long long)((n + 63) / 64) * ((m + 63) / 64);
+  if (tiles64 >= 32 && part) {
+    // a large output: 64 x 64 tiles, K split so that about 512 blocks run (at least 512 columns
+    // per chunk, at most 8 chunks)
+    int splits = (int)std::min<long long>(8, std::max<long long>(1, (512 + tiles64 - 1) / tiles64));
+    splits = std::min(splits, std::max(1, kdim / 512));
+    while (splits > 1 && (long long)splits * m * n > part_elems) --splits;
+    if (splits < 2)
+      return launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, A, lda, nullptr, B, ldb, C, ldc, nullptr, m, n, kdim, nullptr,
+                            0, s);
+    int k_chunk = ((kdim + splits - 1) / splits + GBK - 1) / GBK * GBK;
+    splits = (kdim + k_chunk - 1) / k_chunk;
+    dim3 grid((n + GBN - 1) / GBN, (m + GBM - 1) / GBM, splits);
+    gemm_nt_f32_tile64_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, m, n, kdim, k_chunk, part);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+    const float* cpart = part;
+    const int* no_count = nullptr;
+    const int* no_idx = nullptr;
+    void* Cv = C;
+    void* rargs[] = {&cpart, &splits, &m, &n, &no_count, &Cv, &ldc, &no_idx};
+    dim3 rgrid((unsigned)std::min(16, (n + 255) / 256), m);
+    return hipLaunchKernel((void*)splitk_reduce_kernel<float>, rgrid, dim3(256), rargs, 0, s) == hipSuccess
+               ? GSI_OK
+               : GSI_ERR_HIP;
+  }
   const long long tiles = (long long)((n + 15) / 16) * ((m + 15) / 16);
   int splits = (int)std::min<long long>(16, std::max<long long>(1, (256 + tiles - 1) / tiles));
   splits = std::min(splits, std::max(1, kdim / 256));
