@@ -62,7 +62,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU: libgsi has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Per-GPU work is one decode stream; see the design notes for how the path would shard.",
               file=sys.stderr)
         sys.exit(2)
