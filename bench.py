@@ -499,6 +499,22 @@ def calibration(args, g, torch, np):
                           "exact_vs_planted": float(cal.principal_sines(P[l], exact[l])[0])} for l in sample}
     step_bytes = 2.0 * c.n * c.d * 4
     step_flop = 4.0 * c.n * c.d * c.k
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the fp64 oracle's cascade on the first layers of the same chain (layer 0 cold, then warm),
+        # timed on the host cores and scaled to the 28 layers by steps
+        from threadpoolctl import threadpool_info
+        n_layers_cpu = 3
+        A_host = [As[l].cpu().numpy() for l in range(n_layers_cpu)]
+        t0 = time.perf_counter()
+        cal.calibrate_cascade(A_host, Om.cpu().numpy().T, args.cal_cold, args.cal_warm)
+        el = time.perf_counter() - t0
+        steps_cpu = args.cal_cold + (n_layers_cpu - 1) * args.cal_warm
+        steps_all = args.cal_cold + (c.n_layers - 1) * args.cal_warm
+        threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+        cpu = {"value": round(el / steps_cpu * steps_all, 3), "unit": "s", "cores": int(threads), "kind": "oracle",
+               "sample": f"fp64 oracle cascade on layers 0-{n_layers_cpu - 1} ({steps_cpu} steps) in {el:.1f}s, "
+                         f"scaled to {steps_all} steps; BLAS threads {threads}"}
     out = {"metric": "GSI basis calibration with the depth cascade: GPU time for all layers, GPT-J-shaped chain",
            "unit": "s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
            "config": {"workload": f"calibration chain: {c.n_layers} layers, {c.n} tokens x d={c.d}, k={c.k}, "
@@ -511,7 +527,8 @@ def calibration(args, g, torch, np):
            "step_ms": round(t_step * 1e3, 3),
            "step_products": {"bytes": step_bytes, "flop": step_flop},
            "accuracy": acc,
-           "max_sine_vs_planted": {"cascade": round(float(max(sines_casc)), 5), "cold": round(float(max(sines_cold)), 5)}}
+           "max_sine_vs_planted": {"cascade": round(float(max(sines_casc)), 5), "cold": round(float(max(sines_cold)), 5)},
+           "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 
