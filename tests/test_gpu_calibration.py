@@ -129,3 +129,19 @@ def test_reorthogonalisation_on_ill_conditioned_rows(g):
         sin = cal.principal_sines(ref[:, :j], Qg[:, :j])[0]
         say(f"  leading {j} rows: largest sine {sin:.2e}")
         assert sin <= (1e-5 if j == 4 else 1e-3), j
+
+
+def test_cascade_at_the_measured_size(g):
+    """The cascade as the benchmark times it (GPT-J-shaped chain: 2048 tokens x 4096, k = 256,
+    layer 0 from the Gaussian start with 8 steps, then 2 warm steps per layer), on its first four
+    layers, against the oracle."""
+    from synth.calibration import GPTJ_CALIBRATION as c
+    say("case: calibration cascade at the measured size, 4 layers, n=2048 d=4096 k=256")
+    P = planted_bases(c, 4)
+    As = [activations(c, l, P[l]) for l in range(4)]
+    Om = cold_start(c)
+    ref = cal.calibrate_cascade(As, Om.numpy().T, 8, 2)
+    Q = Om.cuda()
+    for l, A in enumerate(As):
+        Q = _gpu_calibrate(g, A.cuda(), Q, 8 if l == 0 else 2)
+        _compare(Q, ref[l], f"layer {l}")
