@@ -69,6 +69,20 @@ int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, in
   BatchedWs w = batched_part(ws, L.k, T, d_out_ws);
   int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
   if (rc != GSI_OK) return rc;
+  // both products on the skinny kernel: their K-chunk sums in two buffers, one reduction into y
+  const int sa = skinny_splits(GSI_F32, dtype, T, L.d_out, L.k, w.part_elems);
+  const int sb = skinny_splits(dtype, dtype, T, L.d_out, L.d, w.part_elems);
+  if (sa >= 2 && sb >= 2 && w.part2) {
+    // fast tokens: y = M g; slow tokens: y = W x     [GSI §2.2]
+    rc = launch_skinny_partials(GSI_F32, dtype, w.G, L.k, w.fast_idx, L.M, L.k, T, L.d_out, L.k, w.counts + 0, sa,
+                                w.part, s);
+    if (rc != GSI_OK) return rc;
+    rc = launch_skinny_partials(dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, T, L.d_out, L.d, w.counts + 1, sb,
+                                w.part2, s);
+    if (rc != GSI_OK) return rc;
+    return launch_reduce2(dtype, w.part, sa, w.counts + 0, w.fast_idx, w.part2, sb, w.counts + 1, w.slow_idx, T,
+                          L.d_out, Y, y_ld, s);
+  }
   // fast tokens: y = M g     [GSI §2.2]
   rc = launch_gemm_nt_split(GSI_F32, dtype, dtype, w.G, L.k, w.fast_idx, L.M, L.k, Y, y_ld, w.fast_idx, T, L.d_out,
                             L.k, w.counts + 0, w.part, w.part_elems, s);

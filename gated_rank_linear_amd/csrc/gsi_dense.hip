@@ -984,6 +984,74 @@ int launch_gemm_nt_f32_splitk(const float* A, long long lda, const float* B, lon
                                                                                                      : GSI_ERR_HIP;
 }
 
+// K chunks the skinny kernel takes for an m <= 64 row product (0 when it does not apply): the
+// split rule of launch_gemm_nt_split, about 1024 blocks, at least 256 K columns per chunk.
+int skinny_splits(int a_type, int b_type, int m, int n, int kdim, long long part_elems) {
+  const bool ok = (a_type == GSI_BF16 && b_type == GSI_BF16) || (a_type == GSI_F16 && b_type == GSI_F16) ||
+                  (a_type == GSI_F32 && b_type == GSI_BF16);
+  if (!ok || m > 64 || m <= 0 || n <= 0) return 0;
+  const long long tiles = (long long)((n + 63) / 64);
+  int splits = (int)std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles - 1) / tiles));
+  splits = std::min(splits, std::max(1, kdim / 256));
+  while (splits > 1 && (long long)splits * m * n > part_elems) --splits;
+  if (splits < 2) return 0;
+  const int k_chunk = ((kdim + splits - 1) / splits + 31) / 32 * 32;
+  return (kdim + k_chunk - 1) / k_chunk;
+}
+
+// The skinny kernel's raw K-chunk sums only (no reduction): part[z][mm][nn] for the mv valid
+// rows, `splits` from skinny_splits.
+int launch_skinny_partials(int a_type, int b_type, const void* A, long long lda, const int* a_idx, const void* B,
+                           long long ldb, int m, int n, int kdim, const int* m_count, int splits, float* part,
+                           hipStream_t s) {
+  int k_chunk = ((kdim + splits - 1) / splits + 31) / 32 * 32;
+  void* sk = a_type == GSI_BF16 ? (void*)gemm_nt_skinny_staged_kernel<bf16_t, bf16_t>
+             : a_type == GSI_F16 ? (void*)gemm_nt_skinny_staged_kernel<f16_t, f16_t>
+                                 : (void*)gemm_nt_skinny_staged_kernel<float, bf16_t>;
+  dim3 grid((n + 63) / 64, 1, splits);
+  void* args[] = {&A, &lda, &a_idx, &B, &ldb, &m, &n, &kdim, &m_count, &k_chunk, &part};
+  return hipLaunchKernel(sk, grid, dim3(256), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// One reduction for two token lists (the batched fast and slow products): row slot mm < *ca takes
+// list a (partials pa, sa chunks, output row ia[mm]), the next *cb slots list b; sums in chunk
+// order.
+template <typename TC>
+__global__ __launch_bounds__(256) void splitk_reduce2_kernel(const float* __restrict__ pa, int sa,
+                                                             const int* __restrict__ ca, const int* __restrict__ ia,
+                                                             const float* __restrict__ pb, int sb,
+                                                             const int* __restrict__ cb, const int* __restrict__ ib,
+                                                             int m, int n, void* __restrict__ C, long long ldc) {
+  const int na = min(m, *ca), nb = min(m, *cb);
+  int mm = blockIdx.y;
+  const float* part = pa;
+  int splits = sa;
+  const int* idx = ia;
+  if (mm >= na) {
+    mm -= na;
+    if (mm >= nb) return;
+    part = pb;
+    splits = sb;
+    idx = ib;
+  }
+  const long long crow = idx[mm];
+  for (int nn = blockIdx.x * 256 + threadIdx.x; nn < n; nn += gridDim.x * 256) {
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += part[((long long)z * m + mm) * n + nn];
+    st_from_f32<TC>(C, crow * ldc + nn, v);
+  }
+}
+
+int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int* ia, const float* pb, int sb,
+                   const int* cb, const int* ib, int m, int n, void* C, long long ldc, hipStream_t s) {
+  void* fn = c_type == GSI_F32 ? (void*)splitk_reduce2_kernel<float>
+             : c_type == GSI_F16 ? (void*)splitk_reduce2_kernel<f16_t>
+                                 : (void*)splitk_reduce2_kernel<bf16_t>;
+  void* args[] = {&pa, &sa, &ca, &ia, &pb, &sb, &cb, &ib, &m, &n, &C, &ldc};
+  dim3 grid((unsigned)std::min(16, (n + 255) / 256), m);
+  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
 // Split-K variant for products with few output tiles and a long K (the batched fast and slow
 // paths): the register-fed matrix-core kernel over S chunks of K, raw sums into part
 // ([S, m, n] float32, at least part_elems long), then their sum in chunk order into C. Falls back
@@ -1182,7 +1250,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
 
 size_t batched_ws_bytes(int k, int T, int d_out) {
   return 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
-         align256(split_part_elems(T, d_out) * 4);
+         2 * align256(split_part_elems(T, d_out) * 4);
 }
 BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   char* p = (char*)base;
@@ -1195,6 +1263,8 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   w.slow_idx = (int*)p; p += align256((size_t)T * 4);
   w.counts = (int*)p; p += align256(2 * 4);
   w.part = w.part_elems ? (float*)p : nullptr;
+  p += align256(w.part_elems * 4);
+  w.part2 = w.part_elems ? (float*)p : nullptr;
   return w;
 }
 

@@ -168,7 +168,8 @@ struct BatchedWs {
   int* fast_idx; // [T]
   int* slow_idx; // [T]
   int* counts;   // [2]
-  float* part;   // [kMaxSplit, T, d_out] split-K partial sums of the fast and slow products
+  float* part;   // [kMaxSplit, T, d_out] split-K partial sums of the fast product (and the projection)
+  float* part2;  // [kMaxSplit, T, d_out] split-K partial sums of the slow product
   long long part_elems;
 };
 constexpr int kMaxSplit = 8;  // K chunks of a split product
@@ -179,6 +180,14 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out);
 int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
                          const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n,
                          int kdim, const int* m_count, float* part, long long part_elems, hipStream_t s);
+// the skinny kernel's K chunks for an m <= 64 row product (0: not applicable), its partial sums
+// without reduction, and one reduction of two token lists into C
+int skinny_splits(int a_type, int b_type, int m, int n, int kdim, long long part_elems);
+int launch_skinny_partials(int a_type, int b_type, const void* A, long long lda, const int* a_idx, const void* B,
+                           long long ldb, int m, int n, int kdim, const int* m_count, int splits, float* part,
+                           hipStream_t s);
+int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int* ia, const float* pb, int sb,
+                   const int* cb, const int* ib, int m, int n, void* C, long long ldc, hipStream_t s);
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s);
 
