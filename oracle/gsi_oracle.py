@@ -21,9 +21,9 @@ Readings where the summary is silent (each listed in the design notes):
   * |.| is the Euclidean norm.
   * The residual is formed explicitly against the stored V (which is not exactly orthonormal
     once rounded to fp16/bf16); 1 - |g|^2/|x|^2 is a different quantity and is not used.
-  * rho < eps is tested as nr2 < eps^2 * nx2. The test is evaluated in float32 on the correctly
-    rounded float32 values of nr2 and nx2 (the precision the GPU decides in); ties go slow,
-    x = 0 goes slow (0 < 0 is false), NaN/Inf go slow (comparisons with NaN are false).
+  * rho < eps is tested as nr2 < eps^2 * nx2, in float64 like every other step (the summary
+    fixes no precision for the test); ties go slow, x = 0 goes slow (0 < 0 is false), NaN/Inf go
+    slow (comparisons with NaN are false).
   * The slow path returns W x directly (the summary's "full computation"), not M g + W r.
 
 Parity pins for every function here live in tests/test_oracle_pins.py; none is unpinned.
@@ -91,16 +91,14 @@ def ratio(nr2, nx2) -> np.ndarray:
 def gate(nr2, nx2, eps) -> np.ndarray:
     """Per-token gate bits [GSI §2.2]: 0 = fast (rho < eps), 1 = slow (rho >= eps).
 
-    The comparison nr2 < eps^2 * nx2 is taken in float32 on the correctly rounded float32 values
-    of nr2, nx2 and eps: thr = fl32(eps * eps), rhs = fl32(thr * nx2), fast iff nr2 < rhs.
+    rho < eps is taken as nr2 < eps^2 * nx2 (both sides non-negative, so the two forms agree for
+    nx2 > 0 and the squared form needs no division), evaluated in float64.
     """
-    nr2 = np.asarray(nr2, dtype=np.float64).astype(np.float32)
-    nx2 = np.asarray(nx2, dtype=np.float64).astype(np.float32)
-    e = np.float32(eps)
+    nr2 = np.asarray(nr2, dtype=np.float64)
+    nx2 = np.asarray(nx2, dtype=np.float64)
+    e = float(eps)
     with np.errstate(invalid="ignore", over="ignore"):
-        thr = np.float32(e * e)
-        rhs = (thr * nx2).astype(np.float32)
-        fast = nr2 < rhs
+        fast = nr2 < (e * e) * nx2
     return np.where(fast, FAST, SLOW).astype(np.uint8)
 
 
@@ -162,22 +160,3 @@ def spectral_norm(W, tol=1e-12, max_iter=100000, seed=0) -> float:
             break
         lam = nu
     return float(np.sqrt(lam))
-
-
-def decode_stack(sites, tokens, eps) -> list:
-    """Batch-1 decode through a stack of GSI sites, token by token, site by site [GSI §3: every
-    linear map of the block]. `sites` is a list of (W, V, M or None); `tokens[s]` holds site s's
-    inputs (T x d_s). Sites are not chained numerically: each site reads its own input row.
-    Returns per site a dict like forward()'s.
-    """
-    out = [dict(y=[], gate=[], rho=[]) for _ in sites]
-    prepared = [(as_f64(W), as_f64(V), precompute_image(W, V) if M is None else as_f64(M)) for W, V, M in sites]
-    T = np.atleast_2d(as_f64(tokens[0])).shape[0]
-    xs = [np.atleast_2d(as_f64(t)) for t in tokens]
-    for t in range(T):
-        for s, (W, V, M) in enumerate(prepared):
-            r = forward(W, V, xs[s][t:t + 1], eps, M=M)
-            out[s]["y"].append(r["y"][0])
-            out[s]["gate"].append(r["gate"][0])
-            out[s]["rho"].append(r["rho"][0])
-    return [{k: np.array(v) for k, v in o.items()} for o in out]

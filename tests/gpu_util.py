@@ -85,6 +85,36 @@ def decode(built: Built, eps: float, T_step: int = 1, n_steps=None):
     return Y, gates, rho, st
 
 
+def compare_site(y_got, gate_got, ref: dict, tol: float, where: str = "", keep=None):
+    """Parity of one site's outputs with the oracle's `ref` (a forward() result): gate bits exact,
+    and y within `tol` relative L2 three ways: over the whole site, for every token on its own,
+    and over the slow tokens alone (so that a wrong slow path cannot hide among the fast tokens).
+    `keep` (bool per token) restricts the comparison to tokens whose gate is unique. Returns
+    (site error, worst token error)."""
+    gate_got = np.asarray(gate_got).astype(np.uint8)
+    ref_gate = np.asarray(ref["gate"]).astype(np.uint8)
+    y = np.asarray(y_got, dtype=np.float64)
+    Y = np.asarray(ref["y"], dtype=np.float64)
+    if keep is not None:
+        keep = np.asarray(keep, dtype=bool)
+        gate_got, ref_gate, y, Y = gate_got[keep], ref_gate[keep], y[keep], Y[keep]
+    mism = np.nonzero(gate_got != ref_gate)[0]
+    assert mism.size == 0, f"{where}: gate bits differ at tokens {mism[:10]}"
+    err = rel_l2(y, Y)
+    assert err <= tol, f"{where}: y rel L2 {err:.3e} > {tol}"
+    den = np.linalg.norm(Y, axis=1)
+    per = np.linalg.norm(y - Y, axis=1) / np.where(den > 0, den, 1.0)
+    worst = float(per.max()) if per.size else 0.0
+    if per.size:
+        t = int(np.argmax(per))
+        assert worst <= tol, f"{where}: token {t} (gate {ref_gate[t]}) y rel L2 {worst:.3e} > {tol}"
+    slow = ref_gate == 1
+    if slow.any():
+        es = rel_l2(y[slow], Y[slow])
+        assert es <= tol, f"{where}: slow tokens' y rel L2 {es:.3e} > {tol}"
+    return err, worst
+
+
 def check_site(built: Built, idx: int, Y_site: torch.Tensor, gate_col: torch.Tensor, eps: float, with_y: bool):
     b, s, si = built.sites[idx]
     ref_gate = orc.gate_only(si.V, si.X, eps)
@@ -97,7 +127,5 @@ def check_site(built: Built, idx: int, Y_site: torch.Tensor, gate_col: torch.Ten
         return None
     W = built.W_host[(b, s)]
     ref = orc.forward(W, si.V, si.X, eps)
-    err = rel_l2(to_np(Y_site), ref["y"])
-    tol = TOL[built.cfg.dtype]
-    assert err <= tol, f"site {(b, s)}: y rel L2 {err:.3e} > {tol}"
+    err, _ = compare_site(to_np(Y_site), got_gate, ref, TOL[built.cfg.dtype], where=f"site {(b, s)}")
     return err

@@ -188,6 +188,9 @@ def pin_brute_force_d8(orc):
             assert abs(out["nr2"][0] - float(nr2)) <= 1e-12 * float(nx2), f"nr2 k={k}"
             assert abs(out["nx2"][0] - float(nx2)) <= 1e-12 * float(nx2)
             assert bool(out["gate"][0] == orc.FAST) == fast, f"gate k={k}"
+            go = orc.gate_only(Vf, xi.astype(np.float64)[None, :], float(eps))
+            assert bool(go["gate"][0] == orc.FAST) == fast, f"gate_only k={k}"
+            assert abs(go["nr2"][0] - float(nr2)) <= 1e-12 * float(nx2), f"gate_only nr2 k={k}"
             assert np.max(np.abs(out["y"][0] - np.array([float(v) for v in y]))) <= 1e-11 * (1 + max(abs(float(v)) for v in y))
             # residual is the least-squares distance to span(V) for an orthonormal basis
             if k > 0:
@@ -234,6 +237,7 @@ def pin_ties_and_degenerate(orc):
     out = orc.forward(W, V, X, 0.5)
     assert out["nr2"][0] == 3.0 and out["nx2"][0] == 12.0
     assert list(out["gate"]) == [orc.SLOW, orc.SLOW, orc.FAST], f"tie rule: {out['gate']}"
+    assert list(orc.gate_only(V, X, 0.5)["gate"]) == [orc.SLOW, orc.SLOW, orc.FAST], "tie rule (gate_only)"
     z = np.zeros((1, d))
     o = orc.forward(W, V, z, 0.5)
     assert o["gate"][0] == orc.SLOW and np.all(o["y"] == 0.0) and np.isnan(o["rho"][0]), "x = 0"

@@ -110,3 +110,14 @@ def test_calibrate_rejects_before_the_device():
     assert lib.gsi_calibrate(n, d, k, A, Q0, 1, A + 256, W, ws, None) == -2    # result overlaps A
     assert lib.gsi_calibrate(n, d, k, A, Q0, 1, Q0 + 16, W, ws, None) == -2    # partial overlap with Q0
     assert lib.gsi_calibrate(n, d, k, A, Q0, 1, W, W, ws, None) == -2          # result overlaps workspace
+
+
+@pytest.mark.parametrize("eps", [-0.1, -1e-30, float("nan"), float("-inf")])
+def test_eps_rejected_before_device(eps):
+    """eps < 0 or NaN is GSI_ERR_EPS for both the layer and the stack entry points, and is
+    detected before the handle or any buffer is read (the handles here are never dereferenced)."""
+    p = vp(256)
+    fake = vp(4096)
+    assert lib.gsi_forward(fake, p, 1, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4
+    assert lib.gsi_stack_decode(fake, p, 1, 1, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4
+    assert lib.gsi_stack_decode(fake, p, 1, 64, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4

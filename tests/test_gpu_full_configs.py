@@ -9,7 +9,7 @@ import torch
 
 import synth
 from oracle import gsi_oracle as orc
-from tests.gpu_util import TOL, Built, check_site, decode, rel_l2, say, to_np
+from tests.gpu_util import TOL, Built, check_site, compare_site, decode, rel_l2, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,13 @@ def test_config4_opt_stack_batch1(g):
 
 
 def test_config5_gptj_batched_T64(g):
+    """The T = 64 workload exactly as the benchmark runs it: all 20 generated steps of the pool
+    (1280 tokens per site), every gate bit of every (token, site), y of every token on three
+    sites, one of each shape class (QKV, fc_out, fc_in) from the first and last blocks."""
     cfg = synth.get(5)
     sample = {(0, 0), (0, 3), (cfg.n_blocks - 1, 2)}
-    gates, worst = _run_stack(5, sample, n_steps=4, T_step=cfg.t_step)
+    gates, worst = _run_stack(5, sample, n_steps=cfg.token_pool_steps, T_step=cfg.t_step)
+    assert gates.shape == (cfg.token_pool_steps * cfg.t_step, cfg.n_sites)
     frac = gates.float().mean().item()
     assert 0.1 < frac < 0.3, frac
     assert worst <= TOL["bf16"]
@@ -102,13 +106,11 @@ def test_ragged_shapes(g, dtype, shape):
         g.gsi_forward(L, x, eps, y, gate, None, ws)
         torch.cuda.synchronize()
         assert g.gsi_workspace_status(ws) == 0
-        gb = gate.cpu().numpy()
-        assert np.array_equal(gb[keep], ref_gate["gate"][keep]), f"T={T}"
+        assert keep.mean() >= 0.9, f"T={T}: only {keep.sum()} of {T} tokens clear of the gate line"
         ref = orc.forward(W, V, X, eps)
         tol = TOL["f32"] if dtype == torch.float32 else TOL["bf16"]
-        # compare y only where the gate agrees (all tokens with a clear margin)
-        err = rel_l2(to_np(y)[keep], ref["y"][keep])
-        assert err <= tol, f"T={T}: y rel L2 {err}"
+        # gates and y compared where the gate is unique (tokens with a clear margin)
+        compare_site(to_np(y), gate.cpu().numpy(), ref, tol, where=f"ragged {shape} T={T}", keep=keep)
 
 
 def test_zero_tokens_is_a_no_op(g):
@@ -162,6 +164,7 @@ def test_precompute_tile_paths(g, dtype, shape):
     np.testing.assert_allclose(rho.cpu().numpy(), ref_rho, rtol=1e-4, atol=1e-6)
     ref_g = orc.gate_only(V, X, eps)
     keep = np.abs(ref_g["rho"] - eps) > 1e-3
+    assert keep.mean() >= 0.9, f"only {keep.sum()} of 3 tokens clear of the gate line"
     assert np.array_equal(gate.cpu().numpy()[keep], ref_g["gate"][keep])
 
 
@@ -205,10 +208,8 @@ def test_batched_all_slow_and_all_fast(g, dtype, eps):
     gb = gate.cpu().numpy()
     assert np.all(gb == (1 if eps == 0.0 else 0))
     ref = orc.forward(W, V, X, eps)
-    assert np.array_equal(gb, ref["gate"])
-    err = rel_l2(to_np(y), ref["y"])
-    say(f"  y rel L2 {err:.2e}")
-    assert err <= TOL["bf16"]
+    err, worst = compare_site(to_np(y), gb, ref, TOL["bf16"], where=f"batched eps={eps}")
+    say(f"  y rel L2 {err:.2e}, worst token {worst:.2e}")
 
 
 @pytest.mark.parametrize("shape", [(64, 65536, 512), (262144, 64, 64)])
@@ -231,13 +232,30 @@ def test_maximum_sizes(g, shape):
         X = torch.from_numpy(_planned_tokens(rng, V64, C64, eps, T, 0.4)).to(torch.bfloat16)
         ref = orc.forward(W, V, X, eps)
         keep = np.abs(orc.gate_only(V, X, eps)["rho"] - eps) > 1e-3
+        assert keep.mean() >= 0.9, f"T={T}: only {keep.sum()} of {T} tokens clear of the gate line"
         y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
         gate = torch.full((T,), 9, dtype=torch.uint8, device="cuda")
         ws = g.new_workspace(g.gsi_workspace_bytes(L.dtype, d_out, d, k, T))
         g.gsi_forward(L, X.cuda().contiguous(), eps, y, gate, None, ws)
         torch.cuda.synchronize()
         assert g.gsi_workspace_status(ws) == 0
-        assert np.array_equal(gate.cpu().numpy()[keep], ref["gate"][keep]), f"T={T}"
-        err = rel_l2(to_np(y)[keep], ref["y"][keep])
-        say(f"  T={T}: y rel L2 {err:.2e}")
-        assert err <= TOL["bf16"], f"T={T}: {err}"
+        err, worst = compare_site(to_np(y), gate.cpu().numpy(), ref, TOL["bf16"], where=f"max {shape} T={T}",
+                                  keep=keep)
+        say(f"  T={T}: y rel L2 {err:.2e}, worst token {worst:.2e}")
+
+
+@pytest.mark.parametrize("cid,blocks,n_tok,T_step", [(2, 2, 30, 2), (2, 2, 30, 15), (3, 1, 30, 15), (3, 1, 32, 16)])
+def test_stack_small_steps(g, cid, blocks, n_tok, T_step):
+    """Stacks decoded T_step tokens at a time: T_step 2 and 15 (the per-token kernel, sites in
+    order within each step) and 16 (the batched path), on GPT-2-shaped fp16 and GPT-J-shaped bf16
+    blocks; every gate bit and y of every token of every site against the oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.get(cid), n_blocks=blocks, n_steps=n_tok)
+    say(f"case: config {cid}, {blocks} block(s), {n_tok} tokens, T_step={T_step}")
+    built = Built(cfg, keep_w_for="all")
+    Y, gates, _, _ = decode(built, cfg.eps, T_step=T_step)
+    Ys = built.split_outputs(Y)
+    worst = 0.0
+    for i in range(len(built.sites)):
+        worst = max(worst, check_site(built, i, Ys[i], gates[:, i], cfg.eps, with_y=True))
+    say(f"  gates exact, worst site y rel L2 {worst:.2e}")

@@ -27,8 +27,7 @@ def m_pythagorean(V, X, G=None):
 
 
 def m_gate_ties_fast(nr2, nx2, eps):
-    return np.where(np.asarray(nr2, np.float32) <= np.float32(eps) ** 2 * np.asarray(nx2, np.float32),
-                    orc.FAST, orc.SLOW).astype(np.uint8)
+    return np.where(np.asarray(nr2) <= eps * eps * np.asarray(nx2), orc.FAST, orc.SLOW).astype(np.uint8)
 
 
 def m_gate_inverted(nr2, nx2, eps):
