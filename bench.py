@@ -106,17 +106,22 @@ def main():
                      torch.empty(nb, dtype=torch.uint8, device=W.device)))
         keep.append((W, V))
     pre_flop = sum(2.0 * si.d_out * si.d * cfg.k + 2.0 * cfg.k * cfg.k * si.d for si in sites)
+    # one create workspace for all layers (the creates run one after another on the stream)
+    wc = max(g.gsi_layer_create_workspace_bytes(g.dtype_code(W.dtype), si.d_out, si.d, cfg.k)
+             for si, (W, _) in zip(sites, keep))
+    ws_create = torch.empty(wc, dtype=torch.uint8, device="cuda") if wc else None
     # every layer's precompute enqueued back to back, as a model load would run it
     torch.cuda.synchronize()
     ev0.record()
     for (W, V), (M, aux) in zip(keep, bufs):
-        layers.append(g.gsi_layer_create(W, V, M, aux))
+        layers.append(g.gsi_layer_create(W, V, M, aux, ws_create))
     ev1.record()
     torch.cuda.synchronize()
     pre_ms = ev0.elapsed_time(ev1)
     del bufs
     log(f"[bench] uploaded weights and ran the M = W V precompute in {time.time() - t0:.1f}s "
         f"(precompute kernels {pre_ms:.1f} ms)")
+    del ws_create
     pre512 = precompute_rank512(g, torch, cfg, sites, keep) if cfg.dtype != "f32" and cfg.k == 256 else None
     stack = g.gsi_stack_create(layers)
     n_sites = len(layers)
@@ -175,7 +180,8 @@ def main():
     achieved = bytes_total / t_gpu / 1e9
     tok_s = args.steps / t_gpu
 
-    traffic = measured_traffic(cfg, n_tok)
+    tokens_per_launch = args.steps / n_launch
+    traffic, traffic_src = measured_traffic(cfg, tokens_per_launch)
 
     # ---------------- CPU baseline: the fp64 oracle on a bounded sample ----------------
     cpu = None
@@ -201,6 +207,7 @@ def main():
                    "batch": 1, "k": cfg.k, "eps": cfg.eps, "sites": n_sites},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "kernel": decode_kernel_name(cfg), "launches": n_launch,
                      "bytes_per_launch": bytes_total / n_launch, "launch_ms": round(t_gpu * 1e3 / n_launch, 4)},
         "cpu_baseline": cpu,
@@ -214,6 +221,9 @@ def main():
         "precompute_k512": pre512,
     }
     print(json.dumps(out), flush=True)
+    # release the stack's device table while the runtime is up, then let the process end
+    stack.destroy()
+    torch.cuda.synchronize()
 
 
 def batched(args, cfg, g, torch, np):
@@ -554,10 +564,13 @@ def precompute_rank512(g, torch, cfg, sites, keep):
         bufs.append((torch.empty((si.d_out, k), dtype=W.dtype, device="cuda"),
                      torch.empty(nb, dtype=torch.uint8, device="cuda")))
         flop += 2.0 * si.d_out * si.d * k + 2.0 * k * k * si.d
+    wc = max(g.gsi_layer_create_workspace_bytes(g.dtype_code(W.dtype), si.d_out, si.d, k)
+             for si, (W, _) in zip(sites, keep))
+    ws_create = torch.empty(wc, dtype=torch.uint8, device="cuda") if wc else None
     torch.cuda.synchronize()
     ev0.record()
     for (W, _), V, (M, aux) in zip(keep, vs, bufs):
-        made.append(g.gsi_layer_create(W, V, M, aux))
+        made.append(g.gsi_layer_create(W, V, M, aux, ws_create))
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
@@ -602,19 +615,31 @@ def decode_kernel_name(cfg) -> str:
     return f"gsi::decode_kernel<{t}, {2 if need <= 2 else 8}>"
 
 
-def measured_traffic(cfg, tokens_per_launch: int):
-    """HBM bytes per launch from the committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
-    each scaled by a 1 GiB copy), or None when the decode kernel's source changed since."""
+def decode_sources_sha256() -> str:
+    """sha256 over the sources the decode kernel is built from (kernel, work split, shared header)."""
     import hashlib
 
+    h = hashlib.sha256()
+    for f in ("gsi_decode.hip", "gsi_plan.h", "gsi_internal.h"):
+        h.update(open(os.path.join(ROOT, "gated_rank_linear_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(cfg, tokens_per_launch: float):
+    """HBM bytes of one timed launch from the committed rocprofv3 counter runs (FETCH_SIZE and
+    WRITE_SIZE of the profiled launch, each scaled by what the counter reads for a 1 GiB copy),
+    per token of the profiled launch times the tokens of the timed launch; (None, reason) when the
+    decode kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "decode_kernel_gptj_stack_bf16.traffic.json")
-    src = os.path.join(ROOT, "gated_rank_linear_amd", "csrc", "gsi_decode.hip")
     if cfg.cid != 3 or not os.path.exists(path):
-        return None
+        return None, "no counter run for this workload"
     rec = json.load(open(path))
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
-        return None
-    return round(rec["traffic_bytes_per_launch"] / rec["tokens_per_launch"] * tokens_per_launch)
+    if decode_sources_sha256() != rec.get("sources_sha256"):
+        return None, "decode kernel changed since the committed counter run"
+    per_tok = rec["traffic_bytes_per_launch"] / rec["tokens_per_launch"]
+    return round(per_tok * tokens_per_launch), (
+        f"rocprofv3 FETCH_SIZE + WRITE_SIZE of the committed profile run ({rec['tokens_per_launch']} tokens per "
+        f"launch, copy-calibrated), scaled to {tokens_per_launch:g} tokens")
 
 
 def cpu_baseline(cfg, sites, keep, seconds: float):

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 import torch
 
@@ -16,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("GSI_LIB") or os.path.join(_HERE, "_lib", "libgsi.so")
 
 GSI_F32, GSI_F16, GSI_BF16 = 0, 1, 2
+GSI_SITE_GATED, GSI_SITE_STATIC, GSI_SITE_DENSE = 0, 1, 2
 GSI_OK = 0
 STATUS_NAMES = {0: "GSI_OK", -1: "GSI_ERR_NULL", -2: "GSI_ERR_SHAPE", -3: "GSI_ERR_DTYPE", -4: "GSI_ERR_EPS",
                 -5: "GSI_ERR_WORKSPACE", -6: "GSI_ERR_ALIGN", -7: "GSI_ERR_DEVICE", -8: "GSI_ERR_HIP",
@@ -30,11 +32,15 @@ SIGNATURES = [
     ("gsi_status_string", ctypes.c_char_p, [_int]),
     ("gsi_device_check", _int, []),
     ("gsi_layer_aux_bytes", _sz, [_int, _int, _int, _int]),
-    ("gsi_layer_create", _int, [ctypes.POINTER(_vp), _int, _int, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    ("gsi_layer_create_workspace_bytes", _sz, [_int, _int, _int, _int]),
+    ("gsi_layer_create", _int, [ctypes.POINTER(_vp), _int, _int, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp, _sz,
+                                _vp]),
+    ("gsi_layer_create_dense", _int, [ctypes.POINTER(_vp), _int, _int, _int, _vp, _vp, _sz, _vp]),
     ("gsi_layer_destroy", _int, [_vp]),
     ("gsi_workspace_bytes", _sz, [_int, _int, _int, _int, _int]),
     ("gsi_forward", _int, [_vp, _vp, _int, _float, _vp, _vp, _vp, _vp, _sz, _vp]),
     ("gsi_stack_create", _int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _int]),
+    ("gsi_stack_create_modes", _int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_int), _int]),
     ("gsi_stack_destroy", _int, [_vp]),
     ("gsi_stack_workspace_bytes", _sz, [_vp, _int]),
     ("gsi_stack_decode", _int, [_vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -102,21 +108,37 @@ class Layer:
         self.dtype, self.d_out, self.d, self.k = dtype, d_out, d, k
         self._keep = keep
 
-    def __del__(self):
+    def destroy(self):
         h, self.handle = getattr(self, "handle", None), None
         if h and lib is not None:
             lib.gsi_layer_destroy(h)
 
+    def __del__(self):
+        self.destroy()   # host memory only: safe at any time
+
 
 class Stack:
+    """Host handle of a stack. destroy() frees its device table; call it before the process
+    ends. At interpreter shutdown the table is left to the process exit (the HIP runtime may
+    already be gone then)."""
+
     def __init__(self, handle: int, layers: list):
         self.handle = handle
         self.layers = layers
 
-    def __del__(self):
+    def destroy(self):
         h, self.handle = getattr(self, "handle", None), None
         if h and lib is not None:
-            lib.gsi_stack_destroy(h)
+            _check(lib.gsi_stack_destroy(h), "gsi_stack_destroy")
+
+    def __del__(self):
+        if sys.is_finalizing():
+            self.handle = None
+            return
+        try:
+            self.destroy()
+        except GsiError:
+            pass
 
 
 def gsi_device_check() -> int:
@@ -131,13 +153,19 @@ def gsi_workspace_bytes(dtype: int, d_out: int, d: int, k: int, T_max: int) -> i
     return lib.gsi_workspace_bytes(dtype, d_out, d, k, T_max)
 
 
-def gsi_layer_create(W: torch.Tensor, V: torch.Tensor, M: torch.Tensor, aux: torch.Tensor, stream=None) -> Layer:
+def gsi_layer_create_workspace_bytes(dtype: int, d_out: int, d: int, k: int) -> int:
+    return lib.gsi_layer_create_workspace_bytes(dtype, d_out, d, k)
+
+
+def gsi_layer_create(W: torch.Tensor, V: torch.Tensor, M: torch.Tensor, aux: torch.Tensor,
+                     ws: torch.Tensor | None = None, stream=None) -> Layer:
     d_out, d = W.shape
     k = V.shape[1]
     dt = dtype_code(W.dtype)
     h = _vp()
     rc = lib.gsi_layer_create(ctypes.byref(h), dt, d_out, d, k, _ptr(W), _ptr(V), _ptr(M), _ptr(aux),
-                              aux.numel() * aux.element_size(), _stream(stream))
+                              aux.numel() * aux.element_size(), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gsi_layer_create")
     return Layer(h.value, dt, d_out, d, k, (W, M, aux))
 
@@ -150,10 +178,29 @@ def gsi_forward(layer: Layer, x: torch.Tensor, eps: float, y: torch.Tensor, gate
     _check(rc, "gsi_forward")
 
 
+def gsi_layer_create_dense(W: torch.Tensor, aux: torch.Tensor, stream=None) -> Layer:
+    d_out, d = W.shape
+    dt = dtype_code(W.dtype)
+    h = _vp()
+    rc = lib.gsi_layer_create_dense(ctypes.byref(h), dt, d_out, d, _ptr(W), _ptr(aux),
+                                    aux.numel() * aux.element_size(), _stream(stream))
+    _check(rc, "gsi_layer_create_dense")
+    return Layer(h.value, dt, d_out, d, 0, (W, None, aux))
+
+
 def gsi_stack_create(layers: list) -> Stack:
     arr = (_vp * len(layers))(*[L.handle for L in layers])
     h = _vp()
     _check(lib.gsi_stack_create(ctypes.byref(h), arr, len(layers)), "gsi_stack_create")
+    return Stack(h.value, list(layers))
+
+
+def gsi_stack_create_modes(layers: list, modes) -> Stack:
+    """A stack whose site i runs in modes[i] (GSI_SITE_GATED / GSI_SITE_STATIC / GSI_SITE_DENSE)."""
+    arr = (_vp * len(layers))(*[L.handle for L in layers])
+    md = (_int * len(layers))(*[int(m) for m in modes])
+    h = _vp()
+    _check(lib.gsi_stack_create_modes(ctypes.byref(h), arr, md, len(layers)), "gsi_stack_create_modes")
     return Stack(h.value, list(layers))
 
 
@@ -197,16 +244,34 @@ def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.zeros((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
-def create_layer(W: torch.Tensor, V: torch.Tensor, stream=None) -> Layer:
-    """Allocate M and aux on W's device and run gsi_layer_create."""
+def create_layer(W: torch.Tensor, V: torch.Tensor, stream=None, ws: torch.Tensor | None = None,
+                 split: bool = True) -> Layer:
+    """Allocate M and aux on W's device and run gsi_layer_create. The create workspace is `ws`
+    when given, else (split=True) a temporary one from torch's caching allocator, released when
+    the call returns (the allocator keeps the block for later work on the same stream), or none
+    (split=False: the single-pass kernels)."""
     d_out, d = W.shape
     k = V.shape[1]
-    nb = gsi_layer_aux_bytes(dtype_code(W.dtype), d_out, d, k)
+    dt = dtype_code(W.dtype)
+    nb = gsi_layer_aux_bytes(dt, d_out, d, k)
     if nb == 0:
         _check(-2, "gsi_layer_aux_bytes")
     M = torch.empty((d_out, k), dtype=W.dtype, device=W.device)
     aux = torch.empty(nb, dtype=torch.uint8, device=W.device)
-    return gsi_layer_create(W, V, M, aux, stream)
+    if ws is None and split:
+        wb = gsi_layer_create_workspace_bytes(dt, d_out, d, k)
+        ws = torch.empty(wb, dtype=torch.uint8, device=W.device) if wb else None
+    return gsi_layer_create(W, V, M, aux, ws, stream)
+
+
+def create_dense_layer(W: torch.Tensor, stream=None) -> Layer:
+    """Allocate aux on W's device and run gsi_layer_create_dense (y = W x for every token)."""
+    d_out, d = W.shape
+    nb = gsi_layer_aux_bytes(dtype_code(W.dtype), d_out, d, 0)
+    if nb == 0:
+        _check(-2, "gsi_layer_aux_bytes")
+    aux = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    return gsi_layer_create_dense(W, aux, stream)
 
 
 def layer_image(layer: Layer) -> torch.Tensor:

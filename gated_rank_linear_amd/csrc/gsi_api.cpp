@@ -28,6 +28,14 @@ int check_shape(int dtype, int d_out, int d, int k) {
   return GSI_OK;
 }
 
+// A dense layer (k = 0): W only.
+int check_dense_shape(int dtype, int d_out, int d) {
+  if (!dtype_ok(dtype)) return GSI_ERR_DTYPE;
+  if (d_out < 1 || d < 8 || d % 8 != 0 || d > 65536) return GSI_ERR_SHAPE;
+  if (((long long)d_out + kMinBlocks - 1) / kMinBlocks > kYPart) return GSI_ERR_SHAPE;
+  return GSI_OK;
+}
+
 int check_eps(float eps) {
   if (std::isnan(eps) || eps < 0.f) return GSI_ERR_EPS;
   return GSI_OK;
@@ -35,28 +43,25 @@ int check_eps(float eps) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? GSI_OK : GSI_ERR_HIP; }
 
-// aux = [V^T (k x d, weight dtype)] [V^T V - I (k x k, float32)] [device copy of the descriptor]
+// aux = [V^T (k x d, weight dtype)] [V^T V - I (k x k, float32)] [decode plan rows (kMaxBlocks)]
+// (a dense layer, k = 0, holds the plan rows only)
 size_t aux_vt_off(int, int, int) { return 0; }
 size_t aux_dl_off(int dtype, int d, int k) { return align256((size_t)k * d * dtype_size(dtype)); }
-size_t aux_desc_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
-size_t aux_bytes(int dtype, int d, int k) { return aux_desc_off(dtype, d, k) + align256(sizeof(LayerDesc)); }
+size_t aux_plan_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
+size_t aux_bytes(int dtype, int d, int k) { return aux_plan_off(dtype, d, k) + sizeof(PlanRow) * kMaxBlocks; }
+
+// the decode kernel's input window and grid for one layer (before anything is enqueued)
+int layer_grid(gsi_layer* L) {
+  L->xr = decode_window(L->dtype, &L->desc, 1);
+  L->P = decode_grid(L->dtype, L->xr);
+  return L->P == 0 ? GSI_ERR_DEVICE : GSI_OK;
+}
 
 size_t ws_bytes_for(int k, int d_out, int T) {
   return align256(decode_ws_bytes()) + batched_ws_bytes(k, T < 1 ? 1 : T, d_out);
 }
 
 WsHeader* ws_header(void* ws) { return reinterpret_cast<WsHeader*>(ws); }
-
-void fill_decode_boxes(DecodeParams& p, void* ws) {
-  char* c = (char*)ws;
-  p.hdr = (WsHeader*)c;
-  c += sizeof(WsHeader);
-  p.box_g = (u64*)c;
-  c += (size_t)kReplicas * kMaxK * 8;
-  p.box_p = (u64*)c;
-  c += (size_t)kReplicas * kMaxBlocks * 8;
-  p.box_f = (u64*)c;
-}
 
 BatchedWs batched_part(void* ws, int k, int T, int d_out) {
   return batched_ws_carve((char*)ws + align256(decode_ws_bytes()), k, T, d_out);
@@ -69,6 +74,12 @@ int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, in
   BatchedWs w = batched_part(ws, L.k, T, d_out_ws);
   int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
   if (rc != GSI_OK) return rc;
+  if (L.mode == kSiteDense)  // every token: y = W x
+    return launch_gemm_nt_split(dtype, dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, Y, y_ld, w.slow_idx, T, L.d_out,
+                                L.d, w.counts + 1, w.part, w.part_elems, s);
+  if (L.mode == kSiteStatic)  // every token: y = M g
+    return launch_gemm_nt_split(GSI_F32, dtype, dtype, w.G, L.k, w.fast_idx, L.M, L.k, Y, y_ld, w.fast_idx, T,
+                                L.d_out, L.k, w.counts + 0, w.part, w.part_elems, s);
   // both products on the skinny kernel: their K-chunk sums in two buffers, one reduction into y
   const int sa = skinny_splits(GSI_F32, dtype, T, L.d_out, L.k, w.part_elems);
   const int sb = skinny_splits(dtype, dtype, T, L.d_out, L.d, w.part_elems);
@@ -130,33 +141,33 @@ int gsi_device_check(void) {
 }
 
 size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k) {
+  if (k == 0) return check_dense_shape(dtype, d_out, d) == GSI_OK ? aux_bytes(dtype, d, 0) : 0;
   if (check_shape(dtype, d_out, d, k) != GSI_OK) return 0;
   return aux_bytes(dtype, d, k);
 }
 
+size_t gsi_layer_create_workspace_bytes(int dtype, int d_out, int d, int k) {
+  if (check_shape(dtype, d_out, d, k) != GSI_OK) return 0;
+  return precompute_ws_bytes(dtype, d_out, d, k);
+}
+
 int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const void* W, const void* V, void* M,
-                     void* aux, size_t aux_nbytes, void* stream) {
+                     void* aux, size_t aux_nbytes, void* ws, size_t ws_nbytes, void* stream) {
   if (!out) return GSI_ERR_NULL;
   *out = nullptr;
   int rc = check_shape(dtype, d_out, d, k);
   if (rc != GSI_OK) return rc;
   if (!W || !V || !M || !aux) return GSI_ERR_NULL;
-  if (!aligned16(W) || !aligned16(V) || !aligned16(M) || !aligned16(aux)) return GSI_ERR_ALIGN;
+  if (!aligned16(W) || !aligned16(V) || !aligned16(M) || !aligned16(aux) || !aligned16(ws)) return GSI_ERR_ALIGN;
   if (aux_nbytes < aux_bytes(dtype, d, k)) return GSI_ERR_WORKSPACE;
+  if (ws && ws_nbytes < precompute_ws_bytes(dtype, d_out, d, k)) return GSI_ERR_WORKSPACE;
   if ((rc = gsi_device_check()) != GSI_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  void* Vt = (char*)aux + aux_vt_off(dtype, d, k);
-  float* Dl = (float*)((char*)aux + aux_dl_off(dtype, d, k));
-  LayerDesc* dev_desc = (LayerDesc*)((char*)aux + aux_desc_off(dtype, d, k));
-  // V^T (k x d), then M = W V = W (V^T)^T, then V^T V - I   [GSI §2.1]
-  if ((rc = launch_transpose(dtype, V, Vt, d, k, s)) != GSI_OK) return rc;
-  if ((rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s)) != GSI_OK)
-    return rc;
-  if ((rc = launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s)) != GSI_OK)
-    return rc;
   gsi_layer* L = new (std::nothrow) gsi_layer;
   if (!L) return GSI_ERR_NULL;
-  L->dev_desc = dev_desc;
+  void* Vt = (char*)aux + aux_vt_off(dtype, d, k);
+  float* Dl = (float*)((char*)aux + aux_dl_off(dtype, d, k));
+  L->plan = (PlanRow*)((char*)aux + aux_plan_off(dtype, d, k));
   L->dtype = dtype;
   L->d_out = d_out;
   L->d = d;
@@ -168,10 +179,53 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
   L->desc.d = d;
   L->desc.d_out = d_out;
   L->desc.k = k;
-  L->desc.pad = 0;
+  L->desc.mode = kSiteGated;
   L->desc.x_off = 0;
   L->desc.y_off = 0;
-  if ((rc = launch_write_desc(L->desc, dev_desc, s)) != GSI_OK) {
+  if ((rc = layer_grid(L)) != GSI_OK) {
+    delete L;
+    return rc;
+  }
+  // V^T (k x d), then M = W V = W (V^T)^T, then V^T V - I   [GSI §2.1], then the decode plan
+  if ((rc = launch_transpose(dtype, V, Vt, d, k, s)) != GSI_OK ||
+      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK ||
+      (rc = launch_plan(L->desc, L->P, (int)dtype_size(dtype), L->plan, s)) != GSI_OK) {
+    delete L;
+    return rc;
+  }
+  *out = L;
+  return GSI_OK;
+}
+
+int gsi_layer_create_dense(gsi_layer** out, int dtype, int d_out, int d, const void* W, void* aux, size_t aux_nbytes,
+                           void* stream) {
+  if (!out) return GSI_ERR_NULL;
+  *out = nullptr;
+  int rc = check_dense_shape(dtype, d_out, d);
+  if (rc != GSI_OK) return rc;
+  if (!W || !aux) return GSI_ERR_NULL;
+  if (!aligned16(W) || !aligned16(aux)) return GSI_ERR_ALIGN;
+  if (aux_nbytes < aux_bytes(dtype, d, 0)) return GSI_ERR_WORKSPACE;
+  if ((rc = gsi_device_check()) != GSI_OK) return rc;
+  gsi_layer* L = new (std::nothrow) gsi_layer;
+  if (!L) return GSI_ERR_NULL;
+  L->plan = (PlanRow*)((char*)aux + aux_plan_off(dtype, d, 0));
+  L->dtype = dtype;
+  L->d_out = d_out;
+  L->d = d;
+  L->k = 0;
+  L->desc.Vt = nullptr;
+  L->desc.M = nullptr;
+  L->desc.Dl = nullptr;
+  L->desc.W = W;
+  L->desc.d = d;
+  L->desc.d_out = d_out;
+  L->desc.k = 0;
+  L->desc.mode = kSiteDense;
+  L->desc.x_off = 0;
+  L->desc.y_off = 0;
+  if ((rc = layer_grid(L)) != GSI_OK ||
+      (rc = launch_plan(L->desc, L->P, (int)dtype_size(dtype), L->plan, (hipStream_t)stream)) != GSI_OK) {
     delete L;
     return rc;
   }
@@ -185,7 +239,8 @@ int gsi_layer_destroy(gsi_layer* L) {
 }
 
 size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max) {
-  if (check_shape(dtype, d_out, d, k) != GSI_OK || T_max < 0) return 0;
+  if (T_max < 0) return 0;
+  if (k == 0 ? check_dense_shape(dtype, d_out, d) != GSI_OK : check_shape(dtype, d_out, d, k) != GSI_OK) return 0;
   return ws_bytes_for(k, d_out, T_max);
 }
 
@@ -201,29 +256,29 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
   if (ws_nbytes < ws_bytes_for(L->k, L->d_out, T)) return GSI_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (T < 16) {
-    DecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.sites = L->dev_desc;
-    p.n_sites = 1;
-    p.n_tokens = T;
-    p.X = x;
-    p.x_ld = L->d;
-    p.Y = y;
-    p.y_ld = L->d_out;
-    p.gates = gate;
-    p.rho = rho;
-    p.gate_ld = 1;
-    p.site0 = 0;
-    p.eps = eps;
-    p.k_max = L->k;
-    p.d_max = L->d;
-    fill_decode_boxes(p, ws);
-    return launch_decode(L->dtype, p, &L->desc, s);
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.plan = L->plan;
+    a.n_sites = 1;
+    a.n_steps = 1;
+    a.t_step = T;
+    a.X = x;
+    a.x_ld = L->d;
+    a.Y = y;
+    a.y_ld = L->d_out;
+    a.gates = gate;
+    a.rho = rho;
+    a.gate_ld = 1;
+    a.eps = eps;
+    a.ws = ws;
+    a.P = L->P;
+    a.xr = L->xr;
+    return launch_decode(L->dtype, a, s);
   }
   return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, L->d_out, s);
 }
 
-int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
+int gsi_stack_create_modes(gsi_stack** out, gsi_layer* const* sites, const int* modes, int n_sites) {
   if (!out) return GSI_ERR_NULL;
   *out = nullptr;
   if (!sites) return GSI_ERR_NULL;
@@ -231,6 +286,11 @@ int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
   for (int i = 0; i < n_sites; ++i) {
     if (!sites[i]) return GSI_ERR_NULL;
     if (sites[i]->dtype != sites[0]->dtype) return GSI_ERR_DTYPE;
+    if (modes) {
+      const int m = modes[i];
+      if (m != GSI_SITE_GATED && m != GSI_SITE_STATIC && m != GSI_SITE_DENSE) return GSI_ERR_SHAPE;
+      if (sites[i]->k == 0 && m != GSI_SITE_DENSE) return GSI_ERR_SHAPE;  // a dense layer has no basis
+    }
   }
   LayerDesc* table = (LayerDesc*)std::malloc(sizeof(LayerDesc) * n_sites);
   gsi_layer** layers = (gsi_layer**)std::malloc(sizeof(gsi_layer*) * n_sites);
@@ -245,6 +305,7 @@ int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
   int kmax = 0, dmax = 0, domax = 0;
   for (int i = 0; i < n_sites; ++i) {
     table[i] = sites[i]->desc;
+    if (modes) table[i].mode = modes[i];
     table[i].x_off = xo;
     table[i].y_off = yo;
     xo += sites[i]->d;
@@ -263,24 +324,40 @@ int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
   S->y_ld = yo;
   S->layers = layers;
   S->h_table = table;
-  S->d_table = nullptr;
-  hipError_t e = hipMalloc((void**)&S->d_table, sizeof(LayerDesc) * n_sites);
-  if (e == hipSuccess) e = hipMemcpy(S->d_table, table, sizeof(LayerDesc) * n_sites, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    if (S->d_table) (void)hipFree(S->d_table);
+  S->d_plan = nullptr;
+  S->xr = decode_window(S->dtype, table, n_sites);
+  S->P = decode_grid(S->dtype, S->xr);
+  auto fail = [&](int code) {
+    if (S->d_plan) (void)hipFree(S->d_plan);
     std::free(table);
     std::free(layers);
     delete S;
-    return GSI_ERR_HIP;
-  }
+    return code;
+  };
+  if (S->P == 0) return fail(GSI_ERR_DEVICE);
+  // plan rows of every (site, block), made on the host by the same code the kernels use
+  const size_t plan_bytes = sizeof(PlanRow) * (size_t)n_sites * S->P;
+  PlanRow* h_plan = (PlanRow*)std::malloc(plan_bytes);
+  if (!h_plan) return fail(GSI_ERR_NULL);
+  const int es = (int)dtype_size(S->dtype);
+  for (int i = 0; i < n_sites; ++i)
+    for (int b = 0; b < S->P; ++b) h_plan[(size_t)i * S->P + b] = make_plan_row(table[i], b, S->P, es);
+  hipError_t e = hipMalloc((void**)&S->d_plan, plan_bytes);
+  if (e == hipSuccess) e = hipMemcpy(S->d_plan, h_plan, plan_bytes, hipMemcpyHostToDevice);
+  std::free(h_plan);
+  if (e != hipSuccess) return fail(GSI_ERR_HIP);
   *out = S;
   return GSI_OK;
+}
+
+int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites) {
+  return gsi_stack_create_modes(out, sites, nullptr, n_sites);
 }
 
 int gsi_stack_destroy(gsi_stack* S) {
   if (!S) return GSI_OK;
   int rc = GSI_OK;
-  if (S->d_table && hipFree(S->d_table) != hipSuccess) rc = GSI_ERR_HIP;
+  if (S->d_plan && hipFree(S->d_plan) != hipSuccess) rc = GSI_ERR_HIP;
   std::free(S->layers);
   std::free(S->h_table);
   delete S;
@@ -303,25 +380,26 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
   if (!aligned16(X) || !aligned16(ws)) return GSI_ERR_ALIGN;
   if (ws_nbytes < ws_bytes_for(S->k_max, S->d_out_max, T_step)) return GSI_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (T_step == 1) {
-    DecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.sites = S->d_table;
-    p.n_sites = S->n_sites;
-    p.n_tokens = n_steps;
-    p.X = X;
-    p.x_ld = S->x_ld;
-    p.Y = Y;
-    p.y_ld = S->y_ld;
-    p.gates = gates;
-    p.rho = rho;
-    p.gate_ld = S->n_sites;
-    p.site0 = 0;
-    p.eps = eps;
-    p.k_max = S->k_max;
-    p.d_max = S->d_max;
-    fill_decode_boxes(p, ws);
-    return launch_decode(S->dtype, p, S->h_table, s);
+  if (T_step < 16) {
+    if ((long long)n_steps * T_step * S->n_sites >= kMaxStepsPerLaunch) return GSI_ERR_SHAPE;
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.plan = S->d_plan;
+    a.n_sites = S->n_sites;
+    a.n_steps = n_steps;
+    a.t_step = T_step;
+    a.X = X;
+    a.x_ld = S->x_ld;
+    a.Y = Y;
+    a.y_ld = S->y_ld;
+    a.gates = gates;
+    a.rho = rho;
+    a.gate_ld = S->n_sites;
+    a.eps = eps;
+    a.ws = ws;
+    a.P = S->P;
+    a.xr = S->xr;
+    return launch_decode(S->dtype, a, s);
   }
   const size_t es = dtype_size(S->dtype);
   for (int st = 0; st < n_steps; ++st) {

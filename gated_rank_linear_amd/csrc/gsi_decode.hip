@@ -7,40 +7,43 @@
 // Every linear site of every block runs in order [GSI §3], one token at a time.
 //
 // Design (one block per CU, all blocks co-resident via a cooperative launch):
-//  * Work split per site: block b owns the g columns j = b, b + P, ... (rows of V^T: each g_j is
-//    one complete d-long dot product inside one block) and a contiguous slice of output rows of
-//    M / W.
+//  * Work split per site (gsi_plan.h): block b owns the g columns j = b, b + P, ... (rows of V^T:
+//    each g_j is one complete d-long dot product inside one block) and a contiguous slice of
+//    output rows of M / W. The split of every (site, block) is precomputed at creation as a
+//    128-byte plan row; the plan rows of the next two steps are staged in LDS ahead of use, so a
+//    step starts without waiting for descriptor loads or index arithmetic.
 //  * Two all-gather exchanges per site: (E1) every block needs all of g for its rows of M g;
 //    (E2) the gate needs the global sum of per-block pieces of g^T (V^T V - I) g. A block posts
 //    its E2 word only after its rows of y are stored, so E2 is also the completion of the site:
 //    no block starts the next site before every block has finished this one. A slow token adds
 //    (E3), the completion of the W x rows.
-//  * Weights stream into LDS ahead of use: two 64 KB site regions alternate with the site
-//    parity. Right after posting its E1 word, a block's data waves copy its slices of site s + 1
-//    (its V^T rows, its rows of V^T V - I and its rows of M) from HBM straight into the other
-//    region (global_load_lds, 16 bytes per lane, no registers); the copy drains while E1
-//    resolves and lands long before site s + 1 needs it. Nothing bulky is in flight on the CU
-//    while E2 resolves: only the next input row, read into registers after this block's rows of y
-//    are stored and used only after E2 has completed. Slices that do not fit a region are read
-//    from global memory when used.
+//  * Weights stream into LDS ahead of use: two 64 KB site regions alternate with the step
+//    parity. Right after posting its E1 word, a block's data waves copy its slices of the next
+//    step's site (its V^T rows, its rows of V^T V - I and its rows of M) from HBM straight into
+//    the other region (global_load_lds, 16 bytes per lane, no registers); the copy drains while
+//    E1 resolves. Nothing bulky is in flight on the CU while E2 resolves: only the next input row,
+//    read into registers after this block's rows of y are stored and used only after E2 has
+//    completed. Slices that do not fit a region are read from global memory when used.
+//  * y = M g runs on the vector ALU (each row split over a few lanes of one wave, DPP sums): at
+//    batch 1 the product is a matrix-vector product, bound by the bytes of M, not by arithmetic.
 //  * Exchanges use tagged 64-bit mailbox words (tag << 32 | payload) with one copy per XCD, so
-//    a block polls the copy on its own XCD's side; stores and polls are device-scope. Tags grow
-//    monotonically across launches (base kept in the workspace header), so nothing is cleared.
-//    A slot is rewritten only after every reader consumed it (the other exchange always sits in
-//    between two uses of one mailbox).
+//    a block polls the copy on its own XCD's side; stores and polls are device-scope. Tags come
+//    from the workspace's 64-bit epoch (gsi_plan.h: step_tag); every launch first rewrites the
+//    words it owns with a tag no poll uses, so no word older than the previous launch survives.
 //  * One wave per block (the sync wave) does all polling and posting; four data waves copy and
 //    compute. Every wait is bounded: past the bound the launch is marked aborted and every block
 //    leaves, so a lost block cannot hang the device.
 //  * Gate arithmetic is done identically (same data, same order) in every block, so all blocks
 //    take the same branch.
+//  * Site modes (gsi_plan.h): a static-projection site skips the V^T V - I rows and the gate
+//    (y = M g, E2 as the completion only); a dense site skips g and E1 (y = W x, then E2).
 #include <algorithm>
 
 #include "gsi_internal.h"
 
 namespace gsi {
 
-constexpr int kMaxJ = 4;       // g columns per block (k <= 512 with at least 128 blocks)
-constexpr int kSlowBatch = 8;  // W / x chunk pairs per lane in flight on the slow path
+constexpr int kSlowBatch = 8;  // W / x chunk pairs per lane in flight on the W x rows
 constexpr unsigned long long kWaitTicks = 200000000ull;  // 2 s at the 100 MHz wall clock
 
 // A 16-byte chunk as a built-in vector (address-space-qualified pointers to it copy cleanly).
@@ -48,25 +51,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1)))* g4p;  // global memory, read
 typedef __attribute__((address_space(3))) void lds_void;
 typedef u32x4 __attribute__((address_space(3))) lu32x4;  // a 16-byte chunk in LDS
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ldg(g4p p, long long i) { return p[i]; }
-
-// Descriptor table entries are read through the constant address space so the compiler issues
-// scalar loads (the index is uniform across the block).
-__device__ __forceinline__ LayerDesc load_desc(const LayerDesc* tab, int s) {
-  static_assert(sizeof(LayerDesc) % 8 == 0, "descriptor must be a whole number of 8-byte words");
-  typedef const unsigned long long __attribute__((address_space(4)))* cw;
-  const cw src = (cw)(tab + s);
-  LayerDesc d;
-  unsigned long long* dst = reinterpret_cast<unsigned long long*>(&d);
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(LayerDesc) / 8); ++i) dst[i] = src[i];
-  return d;
-}
+__device__ __forceinline__ g4p gptr(unsigned long long a) { return (g4p)(uintptr_t)a; }
 
 __device__ __forceinline__ unsigned xcc_id() {
   unsigned v;
@@ -97,15 +86,6 @@ __device__ __forceinline__ void unpack(const u32x4& q, float* out) {
   for (int i = 0; i < vec16<T>::N; ++i) out[i] = to_f32(e[i]);
 }
 
-template <typename T>
-__device__ __forceinline__ float dot_chunk(const u32x4& a, const u32x4& b, float acc) {
-  float fa[vec16<T>::N], fb[vec16<T>::N];
-  unpack<T>(a, fa);
-  unpack<T>(b, fb);
-#pragma unroll
-  for (int i = 0; i < vec16<T>::N; ++i) acc = __builtin_fmaf(fa[i], fb[i], acc);
-  return acc;
-}
 // Dot product of two 16-byte chunks of the same element type, accumulated in float32 (bf16 and
 // f16 pairs through v_dot2: the products are exact in float32). The 32-bit words are copied to
 // scalars before they are reinterpreted: reinterpreting a member of a vector held by reference
@@ -131,11 +111,16 @@ __device__ __forceinline__ float dot16<f16_t>(const u32x4& a, const u32x4& b, fl
 }
 template <>
 __device__ __forceinline__ float dot16<float>(const u32x4& a, const u32x4& b, float acc) {
-  return dot_chunk<float>(a, b, acc);
+  acc = __builtin_fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+  acc = __builtin_fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = __builtin_fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = __builtin_fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  return acc;
 }
 
+// One 16-byte chunk of a weight row against float32 values of g held in registers.
 template <typename T>
-__device__ __forceinline__ float dot_chunk_lds(const u32x4& a, const float* g, float acc) {
+__device__ __forceinline__ float dot_chunk_g(const u32x4& a, const float* g, float acc) {
   float fa[vec16<T>::N];
   unpack<T>(a, fa);
 #pragma unroll
@@ -167,140 +152,89 @@ __device__ __forceinline__ float group_reduce(float v, int width) {
   return v;
 }
 // Whole-wave sum, valid in lane 63.
-__device__ __forceinline__ float wave_reduce(float v) {
-  v += dpp_src<0x111, 0xF>(v);
-  v += dpp_src<0x112, 0xF>(v);
-  v += dpp_src<0x114, 0xF>(v);
-  v += dpp_src<0x118, 0xF>(v);
-  v += dpp_src<0x142, 0xA>(v);
-  v += dpp_src<0x143, 0xC>(v);
-  return v;
+__device__ __forceinline__ float wave_reduce(float v) { return group_reduce(v, 64); }
+
+// A plan row staged in LDS, read into scalar registers (every lane reads the same words).
+__device__ __forceinline__ PlanRow read_plan(const PlanRow* slot) {
+  PlanRow p;
+  const unsigned* src = reinterpret_cast<const unsigned*>(slot);
+  unsigned* dst = reinterpret_cast<unsigned*>(&p);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(PlanRow) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+  return p;
 }
 
-// Block b's share of one site and the layout of its LDS region (in 16-byte chunks). The region
-// holds [V^T rows | (V^T V - I) rows | M rows], each part starting on a 64-chunk boundary so that
-// every 1 KB copy instruction lies inside one part.
-struct SiteGeom {
-  int nJ;        // g columns owned by this block
-  int cprd;      // 16-byte chunks per V^T / W row (d / VW)
-  int nx;        // x chunks per data thread (ceil(cprd / 256))
-  int cprk;      // 16-byte chunks per M row (k / VW)
-  int cpk4;      // float4 chunks per (V^T V - I) row (k / 4)
-  int r0, nrows; // output rows owned
-  int nm;        // M chunks owned (nrows * cprk)
-  int nd;        // (V^T V - I) chunks owned (nJ * cpk4)
-  int vj, v_n;   // V^T rows held in the region and their chunks (at offset 0)
-  int d_off, d_n;  // (V^T V - I) part: offset and chunks held (all or none)
-  int m_off, m_n;  // M part: offset and chunks held
-  int m_rows;    // rows of the M slice held in the region (the rest is read from HBM)
-  bool mf;       // matrix-core layout of the M part (bf16 with k >= 128): 16-row x 32-column
-                 // tiles, tile (rt, kt) being one 1 KB block whose lane l holds row 16 rt +
-                 // l mod 16, columns 32 kt + 8 (l / 16) .. + 7, i.e. the A operand of
-                 // v_mfma_f32_16x16x32_bf16; otherwise the rows are stored as they are, and the
-                 // part held is all of the slice or a multiple of 256 chunks so that one pass of
-                 // the data waves never mixes LDS and global reads
-  int n_inst;    // 1 KB copy instructions that fill the region
-};
-
-__device__ __forceinline__ int align64(int v) { return (v + 63) & ~63; }
-
-template <typename T> struct is_bf16 { static constexpr bool v = false; };
-template <> struct is_bf16<bf16_t> { static constexpr bool v = true; };
-
-template <typename T>
-__device__ __forceinline__ SiteGeom geom(const LayerDesc& L, int b, int P) {
-  constexpr int VW = vec16<T>::N;
-  const int sh_P = __builtin_ctz(P);  // the grid is a power of two
-  SiteGeom g;
-  g.nJ = b < L.k ? ((L.k - 1 - b) >> sh_P) + 1 : 0;
-  g.cprd = L.d / VW;
-  g.nx = (g.cprd + kDataThreads - 1) / kDataThreads;
-  g.cprk = L.k / VW;
-  g.cpk4 = L.k / 4;
-  const int rpb = (L.d_out + P - 1) >> sh_P;
-  g.r0 = min(L.d_out, b * rpb);
-  g.nrows = min(L.d_out, g.r0 + rpb) - g.r0;
-  g.nm = g.nrows * g.cprk;
-  g.nd = g.nJ * g.cpk4;
-  g.vj = g.nJ;  // V^T rows that fit the region (at most kMaxJ: compares, no division)
-#pragma unroll
-  for (int r = kMaxJ; r >= 1; --r) g.vj = (g.vj >= r && r * g.cprd > kRegionChunks) ? r - 1 : g.vj;
-  g.v_n = g.vj * g.cprd;
-  g.d_off = align64(g.v_n);
-  g.d_n = g.d_off + g.nd <= kRegionChunks ? g.nd : 0;
-  g.m_off = align64(g.d_off + g.d_n);
-  g.mf = is_bf16<T>::v && L.k >= 128;
-  const int sh_cprk = __builtin_ctz(g.cprk);  // k / VW is a power of two
-  if (g.mf) {
-    const int tiles = min((g.nrows + 15) / 16, max(0, kRegionChunks - g.m_off) >> (sh_cprk + 4));  // 16 cprk a tile
-    g.m_n = tiles << (sh_cprk + 4);
-    g.m_rows = min(g.nrows, tiles * 16);
-  } else {
-    g.m_n = g.m_off + g.nm <= kRegionChunks ? g.nm : max(0, (kRegionChunks - g.m_off) / kDataThreads * kDataThreads);
-    g.m_rows = g.m_n >> sh_cprk;
+// Copy of plan row (site s, block b) into an LDS slot by lanes 0..7 of one wave.
+__device__ __forceinline__ void fill_plan(const PlanRow* table, int s, int b, int P, int lane, PlanRow* slot) {
+  if (lane < kPlanChunks) {
+    const char* src = reinterpret_cast<const char*>(table + (long long)s * P + b) + lane * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)slot, 16, 0, 0);
   }
-  g.n_inst = (g.m_off + g.m_n + 63) / 64;
-  return g;
 }
 
-// Copy instructions [i0, i1) of a site's region fill; instruction i (chunks 64 i .. 64 i + 63 of
-// the region) is issued by data wave i mod 4. Each lane reads one 16-byte chunk from global
-// memory straight into LDS at region + 16 (64 i + lane). Lanes past the end of a part read a
-// valid dummy chunk into the part's padding, so every lane issues exactly one load.
-template <typename T>
-__device__ __forceinline__ void fill_region(const LayerDesc& L, const SiteGeom& g, int b, int P, int wave, int lane,
-                                            int i0, int i1, lu32x4* region,
+// Copy instructions of a site's region fill; instruction i (chunks 64 i .. 64 i + 63 of the
+// region) is issued by data wave i mod 4. Each lane reads one 16-byte chunk from global memory
+// straight into LDS at region + 16 (64 i + lane). Padding chunks read a valid dummy chunk, so
+// every lane issues exactly one load.
+__device__ __forceinline__ void fill_region(const PlanRow& g, int P, int wave, int lane, lu32x4* region,
                                             const u32x4* dummy) {
-  const char* vt = reinterpret_cast<const char*>(L.Vt);
-  const char* dl = reinterpret_cast<const char*>(L.Dl);
-  const char* mp = reinterpret_cast<const char*>(L.M) + (long long)g.r0 * g.cprk * 16;
-  // k, k / 4, k / 32 and k / VW are powers of two: shifts instead of divisions
-  const int sh_cpk4 = __builtin_ctz(g.cpk4);
-  const int sh_kt = g.mf ? __builtin_ctz(g.cprk / 4) : 0;
-  for (int i = i0 + ((wave - i0) & 3); i < i1; i += 4) {
-    const int c = i * 64 + lane;
-    const char* src = reinterpret_cast<const char*>(dummy);
-    if (c < g.v_n) {  // V^T row jl = c / cprd (at most kMaxJ rows: compares, no division)
-      int jl = 0;
-#pragma unroll
-      for (int r = 1; r < kMaxJ; ++r) jl += c >= r * g.cprd ? 1 : 0;
-      const int cc = c - jl * g.cprd;
-      src = vt + ((long long)(b + jl * P) * g.cprd + cc) * 16;
-    } else if (c >= g.d_off && c < g.d_off + g.d_n) {
-      const int e = c - g.d_off;
-      const int jl = e >> sh_cpk4, cc = e & (g.cpk4 - 1);
-      src = dl + ((long long)(b + jl * P) * g.cpk4 + cc) * 16;
-    } else if (c >= g.m_off && c < g.m_off + g.m_n) {
-      if (g.mf) {  // tile (rt, kk) = instruction (i - m_off / 64) in row-tile-major order
-        const int it = i - g.m_off / 64;
-        const int rt = it >> sh_kt, kk = it & ((1 << sh_kt) - 1);
-        const int row = rt * 16 + (lane & 15);
-        if (row < g.nrows) src = mp + ((long long)row * g.cprk + kk * 4 + (lane >> 4)) * 16;
-      } else {
-        src = mp + (long long)(c - g.m_off) * 16;
-      }
-    }
+  for (int i = wave; i < g.n_inst; i += 4) {
+    const unsigned long long a = fill_source(g, P, i, lane);
+    const void* src = a ? (const void*)(uintptr_t)a : (const void*)dummy;
     // streamed once per token: non-temporal, so the copy does not displace cached lines
     __builtin_amdgcn_global_load_lds(src, (lds_void*)(region + i * 64), 16, 0, 2 /* nt */);
   }
 }
 
 // The input row's chunks tid + 256 u (u < XR) into registers; slots past the row re-read chunk 0.
-template <typename T, int XR>
-__device__ __forceinline__ void load_x(const void* xrow, const SiteGeom& g, int tid, u32x4 (&xw)[XR]) {
+template <int XR>
+__device__ __forceinline__ void load_x(const void* xrow, int cprd, int tid, u32x4 (&xw)[XR]) {
   const g4p xp = (g4p)xrow;
 #pragma unroll
   for (int u = 0; u < XR; ++u) {
     const int cc = tid + u * kDataThreads;
-    xw[u] = xp[cc < g.cprd ? cc : 0];
+    xw[u] = xp[cc < cprd ? cc : 0];
   }
 }
 
-// A block whose wait runs past its bound marks this launch (tag base + 1) as aborted; every other
+struct DecodeParams {
+  const PlanRow* plan;  // [n_sites][P] plan rows
+  int n_sites, n_steps, t_step;
+  const void* X;
+  long long x_ld;
+  void* Y;
+  long long y_ld;
+  uint8_t* gates;  // [n_steps * t_step, gate_ld]
+  float* rho;      // optional
+  int gate_ld;
+  float eps;
+  WsHeader* hdr;
+  u64* box_g;  // [kReplicas][kMaxK]       g values
+  u64* box_p;  // [kReplicas][kMaxBlocks]  per-block gate pieces / site completion
+  u64* box_f;  // [kReplicas][kMaxBlocks]  W x completion
+};
+
+// Order of the steps: steps of t_step tokens in order; inside a step the sites in order; inside a
+// site the step's tokens in order.
+struct Cursor {
+  int s, tis, step;
+  __device__ __forceinline__ void advance(int n_sites, int t_step) {
+    if (++tis == t_step) {
+      tis = 0;
+      if (++s == n_sites) {
+        s = 0;
+        ++step;
+      }
+    }
+  }
+  __device__ __forceinline__ long long token(int t_step) const { return (long long)step * t_step + tis; }
+};
+
+// A block whose wait runs past its bound marks this launch (epoch + 1) as aborted; every other
 // block polls that mark while it waits, so the whole grid leaves promptly. The mark of an older
-// launch never matches because every launch advances the tag base.
-__device__ __forceinline__ void record_abort(const DecodeParams& p, unsigned base) {
-  __hip_atomic_store(&p.hdr->abort_tag, base + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// launch never matches because every launch advances the epoch.
+__device__ __forceinline__ void record_abort(const DecodeParams& p, unsigned long long base) {
+  __hip_atomic_store(&p.hdr->abort_mark, base + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(&p.hdr->status, (int)GSI_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -309,8 +243,8 @@ __device__ __forceinline__ void record_abort(const DecodeParams& p, unsigned bas
 // (slots past n re-read entry n - 1) together with the launch's abort mark, then waits once, so
 // a poll costs one memory round trip. Returns false on timeout or abort.
 template <int NI>
-__device__ __forceinline__ bool gather(const DecodeParams& p, unsigned base, const u64* mb, int n, unsigned tag,
-                                       int lane, float (&out)[NI]) {
+__device__ __forceinline__ bool gather(const DecodeParams& p, unsigned long long base, const u64* mb, int n,
+                                       unsigned tag, int lane, float (&out)[NI]) {
   const unsigned long long t0 = wall_clock64();
   while (true) {
     u64 wv[NI];
@@ -319,7 +253,7 @@ __device__ __forceinline__ bool gather(const DecodeParams& p, unsigned base, con
       const int j = lane + 64 * i;
       wv[i] = ld_dev(mb + (j < n ? j : n - 1));
     }
-    const unsigned ab = __hip_atomic_load(&p.hdr->abort_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long ab = __hip_atomic_load(&p.hdr->abort_mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -327,7 +261,7 @@ __device__ __forceinline__ bool gather(const DecodeParams& p, unsigned base, con
       out[i] = (lane + 64 * i < n) ? __uint_as_float((unsigned)wv[i]) : 0.f;
     }
     if (__all(ok)) return true;
-    if (ab == base + 1u || wall_clock64() - t0 > kWaitTicks) {
+    if (ab == base + 1ull || wall_clock64() - t0 > kWaitTicks) {
       if (lane == 0) record_abort(p, base);
       return false;
     }
@@ -338,9 +272,9 @@ __device__ __forceinline__ bool gather(const DecodeParams& p, unsigned base, con
 // compiler can tell a copy into one region from reads of the other).
 struct Shared {
   float* gsh;    // [kMaxK] gathered g
-  lu32x4* gb;    // [kGbChunks] B operands of the matrix-core path (see mfma_rows)
   float* ypart;  // [kYPart] this block's rows of y (float32) before rounding
   float (*red)[kMaxJ + 2];  // [4][kMaxJ + 2] per-wave partial sums of phase A
+  PlanRow* plans;  // [3] plan rows of the current, next and next-but-one steps
   float* s_nx2;
   float* s_gg;
   int* s_gate;
@@ -355,12 +289,11 @@ struct RowLanes {
   int CPL, Lr, rpw, lr, lc;
   int ch[4];
 };
-template <typename T>
-__device__ __forceinline__ RowLanes row_lanes(const SiteGeom& g, int lane) {
+__device__ __forceinline__ RowLanes row_lanes(int cprk, int lane) {
   RowLanes q;
-  q.CPL = min(4, g.cprk);
-  q.Lr = g.cprk >> __builtin_ctz(q.CPL);  // lanes per row (a power of two <= 32)
-  q.rpw = 64 / q.Lr;      // rows per wave per pass
+  q.CPL = min(4, cprk);
+  q.Lr = cprk >> __builtin_ctz(q.CPL);  // lanes per row (a power of two <= 32)
+  q.rpw = 64 / q.Lr;                    // rows per wave per pass
   q.lr = lane >> __builtin_ctz(q.Lr);
   q.lc = lane & (q.Lr - 1);
 #pragma unroll
@@ -374,136 +307,133 @@ __device__ __forceinline__ void g_slices(const Shared& sh, const RowLanes& q, fl
 #pragma unroll
     for (int e = 0; e < vec16<T>::N; ++e) gl[i][e] = sh.gsh[(q.lc + q.Lr * i) * vec16<T>::N + e];
 }
-// rows [0, m_rows) from the region (stored as they are)
+// rows [0, m_rows) from the region, rows [m_rows, nrows) from HBM
 template <typename T>
-__device__ __forceinline__ void row_sums_lds(const SiteGeom& g, const lu32x4* cur, const Shared& sh, int wave,
-                                             int lane) {
-  const RowLanes q = row_lanes<T>(g, lane);
+__device__ __forceinline__ void fast_rows(const PlanRow& g, const lu32x4* cur, const Shared& sh, int wave, int lane) {
+  const RowLanes q = row_lanes(g.cprk, lane);
   float gl[4][vec16<T>::N];
   g_slices<T>(sh, q, gl);
   for (int rp = 0; rp < g.m_rows; rp += 4 * q.rpw) {
     const int r = rp + wave * q.rpw + q.lr;
     const bool ok = r < g.m_rows;
-    const int rb = g.m_off + (ok ? r : 0) * g.cprk;
+    const int rr = ok ? r : 0;
     u32x4 mv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mv[i] = cur[rb + q.ch[i]];
+    for (int i = 0; i < 4; ++i) mv[i] = cur[lds_m(g, rr, q.ch[i])];
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float d = dot_chunk_lds<T>(mv[i], gl[i], 0.f);
+      const float d = dot_chunk_g<T>(mv[i], gl[i], 0.f);
       acc += i < q.CPL ? d : 0.f;
     }
     acc = group_reduce(ok ? acc : 0.f, q.Lr);
     if (ok && q.lc == q.Lr - 1) sh.ypart[r] = acc;
   }
+  if (g.m_rows < g.nrows) {
+    const g4p mrow = gptr(g.m);
+    for (int rp = g.m_rows; rp < g.nrows; rp += 4 * q.rpw) {
+      const int r = rp + wave * q.rpw + q.lr;
+      const bool ok = r < g.nrows;
+      const long long rb = (long long)(ok ? r : 0) * g.cprk;
+      u32x4 mv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mv[i] = ldg(mrow, rb + q.ch[i]);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = dot_chunk_g<T>(mv[i], gl[i], 0.f);
+        acc += i < q.CPL ? d : 0.f;
+      }
+      acc = group_reduce(ok ? acc : 0.f, q.Lr);
+      if (ok && q.lc == q.Lr - 1) sh.ypart[r] = acc;
+    }
+  }
 }
-// rows [m_rows, nrows) read from HBM (slices that do not fit the region)
+
+// The block's rows of y = W x straight from HBM: one wave per row, each lane keeping kSlowBatch
+// chunk pairs in flight.
 template <typename T>
-__device__ __forceinline__ void row_sums_hbm(const LayerDesc& L, const SiteGeom& g, const Shared& sh, int wave,
-                                             int lane) {
-  const RowLanes q = row_lanes<T>(g, lane);
-  float gl[4][vec16<T>::N];
-  g_slices<T>(sh, q, gl);
-  const g4p mrow = (g4p)L.M + (long long)g.r0 * g.cprk;
-  for (int rp = g.m_rows; rp < g.nrows; rp += 4 * q.rpw) {
-    const int r = rp + wave * q.rpw + q.lr;
-    const bool ok = r < g.nrows;
-    const long long rb = (long long)(ok ? r : 0) * g.cprk;
-    u32x4 mv[4];
+__device__ __forceinline__ void dense_rows(const PlanRow& g, const T* x, T* yrow, int wave, int lane) {
+  const g4p x4 = (g4p)x;
+  for (int r = wave; r < g.nrows; r += kDataThreads / 64) {
+    const g4p wr = gptr(g.w) + (long long)r * g.cprd;
+    float a = 0.f;
+    for (int c0 = 0; c0 < g.cprd; c0 += kSlowBatch * 64) {
+      u32x4 wv[kSlowBatch], xv[kSlowBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mv[i] = ldg(mrow, rb + q.ch[i]);
-    float acc = 0.f;
+      for (int i = 0; i < kSlowBatch; ++i) {
+        const int c = c0 + lane + 64 * i;
+        const int cc = c < g.cprd ? c : 0;
+        wv[i] = wr[cc];
+        xv[i] = x4[cc];
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float d = dot_chunk_lds<T>(mv[i], gl[i], 0.f);
-      acc += i < q.CPL ? d : 0.f;
-    }
-    acc = group_reduce(ok ? acc : 0.f, q.Lr);
-    if (ok && q.lc == q.Lr - 1) sh.ypart[r] = acc;
-  }
-}
-
-// Matrix-core rows of y = M g (bf16, k = 32 KT). Wave w takes the 16-row tiles w, w + 4, ...
-// of the region's M part (stored as A operands of v_mfma_f32_16x16x32_bf16). B carries g as two
-// bf16 columns, column 0 its high part and column 1 the low part (g - high), every other column
-// zero; B for 32-column step s and lane group h = l / 16 is chunk 8 s + 2 h + column of sh.gb,
-// read once per site. Two accumulator chains (even and odd steps) are added at the end; then
-// D[r][0] + D[r][1] (lane l and lane l + 1 of each 16-lane row, a DPP shift) is row r of y.
-// Marks every chunk of `v` as needed here, so all of their loads are issued (and waited for once)
-// before any later use, instead of each load being issued just before its use.
-template <int N>
-__device__ __forceinline__ void hold(const u32x4 (&v)[N]) {
-  static_assert(N == 4 || N == 8, "operand group of 4 or 8 chunks");
-  if constexpr (N == 4) {
-    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
-  } else {
-    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
-  }
-}
-
-constexpr int kGbZero = kMaxK / 32 * 8;  // index of an all-zero chunk of sh.gb
-constexpr int kGbChunks = kGbZero + 1;
-template <int KT>
-__device__ __forceinline__ void mfma_rows(const SiteGeom& g, const lu32x4* cur, const Shared& sh, int wave, int lane) {
-  constexpr int KH = KT < 8 ? KT : 8;  // steps held in registers at a time
-  constexpr int NH = KT / KH;
-  const int col = lane & 15, grp = lane >> 4;
-  const int tiles = (g.m_rows + 15) / 16;
-  u32x4 bv[KH];
-  auto load_b = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < KH; ++i) bv[i] = sh.gb[col < 2 ? (k0 + i) * 8 + grp * 2 + col : kGbZero];
-    hold(bv);
-  };
-  if (NH == 1) load_b(0);
-  for (int rt = wave; rt < tiles; rt += 4) {
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      if (NH > 1) load_b(hh * KH);
-      u32x4 av[KH];
-#pragma unroll
-      for (int i = 0; i < KH; ++i) av[i] = cur[g.m_off + (rt * KT + hh * KH + i) * 64 + lane];
-      hold(av);
-#pragma unroll
-      for (int i = 0; i < KH; ++i) {
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av[i]);
-        const bf16x8 B = __builtin_bit_cast(bf16x8, bv[i]);
-        if (i & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, a1, 0, 0, 0);
-        else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, a0, 0, 0, 0);
+      for (int i = 0; i < kSlowBatch; ++i) {
+        const float v = dot16<T>(wv[i], xv[i], 0.f);
+        a += (c0 + lane + 64 * i < g.cprd) ? v : 0.f;
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = a0[r] + a1[r];
-      const float w = v + dpp_src<0x101, 0xF>(v);  // row_shl:1: lane l + 1's value
-      const int row = rt * 16 + 4 * grp + r;
-      if (col == 0 && row < g.m_rows) sh.ypart[row] = w;
-    }
+    a = wave_reduce(a);
+    if (lane == 63) yrow[r] = from_f32<T>(a);
   }
 }
 
-// One (token, site) step. `cur` holds this site's slices (filled during the previous step);
-// `nxt` receives the next site's. Returns false when the launch was aborted.
+struct StepCtx {
+  long long q, Q;
+  unsigned long long base;
+  int b, P, tid;
+  unsigned rep;
+  const u32x4* dummy;
+};
+
+// One (token, site) step. `cur` holds this step's slices (filled during the previous step);
+// `nxt` receives the next step's. Plan slots: `sc` this step, `sn` the next, `sf` receives the
+// one after. Returns false when the launch was aborted.
 template <typename T, int XR>
-__device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, int t, int s, long long Q, unsigned base,
-                                          int b, int P,
-                                          int tid, unsigned rep, const u32x4* dummy,
-                                          const lu32x4* cur, lu32x4* nxt, u32x4 (&xw)[XR],
-                                          const Shared& sh) {
-  constexpr int VW = vec16<T>::N;
+__device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& c, const Cursor& cq, const lu32x4* cur,
+                                          lu32x4* nxt, u32x4 (&xw)[XR], const Shared& sh, int sc, int sn, int sf) {
+  const int tid = c.tid, b = c.b, P = c.P;
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
-  const LayerDesc L = load_desc(p.sites, s);
-  const SiteGeom g = geom<T>(L, b, P);
-  const unsigned tag = base + (unsigned)(q * 4);
-  const unsigned tag_g = tag + 1, tag_p = tag + 2, tag_f = tag + 3;
-  const T* x = reinterpret_cast<const T*>(p.X) + (long long)t * p.x_ld + L.x_off;
-  const bool has_next = q + 1 < Q;
-  const int sn = s + 1 < p.n_sites ? s + 1 : 0, tn = s + 1 < p.n_sites ? t : t + 1;
-  const LayerDesc Ln = load_desc(p.sites, has_next ? sn : s);
-  const SiteGeom gn = geom<T>(Ln, b, P);
+  const PlanRow g = read_plan(sh.plans + sc);
+  const PlanRow gn = read_plan(sh.plans + sn);
+  const bool has_next = c.q + 1 < c.Q, has_next2 = c.q + 2 < c.Q;
+  Cursor cn = cq;
+  cn.advance(p.n_sites, p.t_step);
+  Cursor c2 = cn;
+  c2.advance(p.n_sites, p.t_step);
+  const long long t = cq.token(p.t_step);
+  const unsigned tag_g = step_tag(c.base, c.q, 1), tag_p = step_tag(c.base, c.q, 2), tag_f = step_tag(c.base, c.q, 3);
+  const T* x = reinterpret_cast<const T*>(p.X) + t * p.x_ld + g.x_off;
+  T* yrow = reinterpret_cast<T*>(p.Y) + t * p.y_ld + g.y_off;
+  const long long vt_stride = (long long)P * g.cprd;  // chunks between owned V^T rows
+
+  if (g.mode == kSiteDense) {
+    // ---------------- dense site: y = W x for the owned rows, then the completion exchange -------------
+    if (!is_sync) {
+      dense_rows<T>(g, x, yrow, wave, lane);
+      if (has_next) {
+        fill_region(gn, P, wave, lane, nxt, c.dummy);
+        if (wave == 0 && has_next2) fill_plan(p.plan, c2.s, b, P, lane, sh.plans + sf);
+        load_x<XR>(reinterpret_cast<const T*>(p.X) + cn.token(p.t_step) * p.x_ld + gn.x_off, gn.cprd, tid, xw);
+      }
+      wait_vmcnt<0>();  // rows of y stored; next region, plan row and input row complete
+    }
+    __syncthreads();
+    if (is_sync) {
+      if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, 0.f));
+      float pv[kMaxBlocks / 64];
+      const bool ok = gather(p, c.base, p.box_p + (long long)c.rep * kMaxBlocks, P, tag_p, lane, pv);
+      if (!ok && lane == 0) *sh.s_abort = 1;
+      if (b == 0 && lane == 0) {
+        const long long o = t * p.gate_ld + cq.s;
+        p.gates[o] = 1;
+        if (p.rho) p.rho[o] = __builtin_nanf("");
+      }
+    }
+    __syncthreads();
+    return !*sh.s_abort;
+  }
 
   // ---------------- phase A (data waves): g_j for owned columns and |x|^2 ----------------
   if (!is_sync) {
@@ -521,14 +451,13 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
 #pragma unroll
     for (int jl = 0; jl < kMaxJ; ++jl) {
       if (jl < g.vj) {  // uniform
-        const int rb = jl * g.cprd;
         float a = 0.f;
 #pragma unroll
         for (int u = 0; u < XR; ++u) {
           if (u * kDataThreads < g.cprd) {  // uniform
             const int cc = tid + u * kDataThreads;
             const bool in = cc < g.cprd;
-            const u32x4 vv = cur[rb + (in ? cc : 0)];
+            const u32x4 vv = cur[lds_vt(g, jl, in ? cc : 0)];
             const float part = dot16<T>(vv, xw[u], 0.f);
             a += in ? part : 0.f;
           }
@@ -544,8 +473,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
         sx = dot16<T>(xv, xv, sx);
       }
       for (int jl = 0; jl < g.nJ; ++jl) {
-        const long long j = b + (long long)jl * P;
-        const g4p vr = (g4p)L.Vt + j * g.cprd;
+        const g4p vr = gptr(g.vt) + (long long)jl * vt_stride;
         float a = 0.f;
         for (int cc = tid + (jl < g.vj ? XR : 0) * kDataThreads; cc < g.cprd; cc += kDataThreads)
           a = dot16<T>(ldg(vr, cc), ldg(x4, cc), a);
@@ -578,26 +506,19 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
   }
   lds_barrier();  // the g words are issued ahead of the copy below
   if (!is_sync) {
-    if (has_next) fill_region<T>(Ln, gn, b, P, wave, lane, 0, gn.n_inst, nxt, dummy);
+    if (has_next) {
+      fill_region(gn, P, wave, lane, nxt, c.dummy);
+      if (wave == 0 && has_next2) fill_plan(p.plan, c2.s, b, P, lane, sh.plans + sf);
+    }
   } else {
     float gv[kMaxK / 64];
-    const bool ok = gather(p, base, p.box_g + (long long)rep * kMaxK, L.k, tag_g, lane, gv);
+    const bool ok = gather(p, c.base, p.box_g + (long long)c.rep * kMaxK, g.k, tag_g, lane, gv);
     if (!ok && lane == 0) *sh.s_abort = 1;
     float gg = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxK / 64; ++i) {
       const int j = lane + 64 * i;
-      if (j < L.k) {
-        sh.gsh[j] = gv[i];
-        if (g.mf) {  // g = hi + lo + O(2^-18 |g|), both parts bf16 (exact products with M)
-          const bf16_t hi = from_f32<bf16_t>(gv[i]);
-          const bf16_t lo = from_f32<bf16_t>(gv[i] - to_f32(hi));
-          auto* gb16 = reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(sh.gb);
-          const int c0 = ((j >> 5) * 4 + ((j >> 3) & 3)) * 2;  // chunk of (step j / 32, lane group)
-          gb16[c0 * 8 + (j & 7)] = hi.b;
-          gb16[(c0 + 1) * 8 + (j & 7)] = lo.b;
-        }
-      }
+      if (j < g.k) sh.gsh[j] = gv[i];
       gg = __builtin_fmaf(gv[i], gv[i], gg);
     }
     gg = wave_reduce(gg);
@@ -609,38 +530,20 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
   // ------- phase B (data waves): this block's rows of y = M g; (sync wave) the gate piece -------
   float pb = 0.f;
   if (!is_sync) {
-    if (g.mf) {
-      switch (g.cprk / 4) {  // 32-column steps per row: k / 32
-        case 4: mfma_rows<4>(g, cur, sh, wave, lane); break;
-        case 8: mfma_rows<8>(g, cur, sh, wave, lane); break;
-        default: mfma_rows<16>(g, cur, sh, wave, lane); break;
-      }
-    } else {
-      row_sums_lds<T>(g, cur, sh, wave, lane);
-    }
-    if (g.m_rows < g.nrows) row_sums_hbm<T>(L, g, sh, wave, lane);
-  } else {
-    // p_b = sum_j g_j ((V^T V - I) g)_j over the owned columns; chunk c covers row c / cpk4,
-    // columns 4 (c mod cpk4) .. + 3
+    fast_rows<T>(g, cur, sh, wave, lane);
+  } else if (g.mode == kSiteGated) {
+    // p_b = sum_j g_j ((V^T V - I) g)_j over the owned columns; chunk e covers owned row
+    // e / cpk4, columns 4 (e mod cpk4) .. + 3
+    const int nd = g.nJ * g.cpk4;
+    const int sh4 = __builtin_ctz(g.cpk4);
     float pp = 0.f;
-    if (g.d_n > 0) {
-      for (int c = lane; c < g.nd; c += 64) {
-        const int jl = c >> __builtin_ctz(g.cpk4), cc = c & (g.cpk4 - 1);
-        float gjl = gj_own[0];
+    for (int e = lane; e < nd; e += 64) {
+      const int jl = e >> sh4, cc = e & (g.cpk4 - 1);
+      float gjl = gj_own[0];
 #pragma unroll
-        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
-        const u32x4 dv = cur[g.d_off + c];
-        pp += dot_f32x4_lds(dv, sh.gsh + cc * 4, 0.f) * gjl;
-      }
-    } else {
-      for (int c = lane; c < g.nd; c += 64) {
-        const int jl = c >> __builtin_ctz(g.cpk4), cc = c & (g.cpk4 - 1);
-        float gjl = gj_own[0];
-#pragma unroll
-        for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
-        const u32x4 dv = ldg((g4p)L.Dl, (long long)(b + (long long)jl * P) * g.cpk4 + cc);
-        pp += dot_f32x4_lds(dv, sh.gsh + cc * 4, 0.f) * gjl;
-      }
+      for (int jj = 1; jj < kMaxJ; ++jj) gjl = (jl == jj) ? gj_own[jj] : gjl;
+      const u32x4 dv = g.d_n > 0 ? cur[lds_dl(g, e)] : ldg(gptr(g.dl), (long long)jl * P * g.cpk4 + cc);
+      pp += dot_f32x4_lds(dv, sh.gsh + cc * 4, 0.f) * gjl;
     }
     pp = wave_reduce(pp);
     pb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 63));
@@ -648,35 +551,39 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
   lds_barrier();
   // ---- the sync wave stores this block's rows of y, then posts its E2 word (site done) ----
   if (is_sync) {
-    T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off + g.r0;
     for (int r = lane; r < g.nrows; r += 64) yrow[r] = from_f32<T>(sh.ypart[r]);
     if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, pb));
   }
   lds_barrier();  // the y rows and the E2 word are issued ahead of the loads below
   if (!is_sync) {
     // the next input row streams in while E2 resolves
-    if (has_next) load_x<T, XR>(reinterpret_cast<const T*>(p.X) + (long long)tn * p.x_ld + Ln.x_off, gn, tid, xw);
-    wait_vmcnt<0>();  // the next region and input row are complete before the barrier below
+    if (has_next) load_x<XR>(reinterpret_cast<const T*>(p.X) + cn.token(p.t_step) * p.x_ld + gn.x_off, gn.cprd, tid, xw);
+    wait_vmcnt<0>();  // the next region, plan row and input row are complete before the barrier below
   } else {
     // ---------------- E2: all-gather the pieces, resolve the gate ----------------
     float pv[kMaxBlocks / 64];
-    const bool ok = gather(p, base, p.box_p + (long long)rep * kMaxBlocks, P, tag_p, lane, pv);
+    const bool ok = gather(p, c.base, p.box_p + (long long)c.rep * kMaxBlocks, P, tag_p, lane, pv);
     if (!ok && lane == 0) *sh.s_abort = 1;
     float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxBlocks / 64; ++i) ps += pv[i];
     ps = wave_reduce(ps);
     if (lane == 63) {
-      const float nx2 = *sh.s_nx2;
-      const float nr2 = (nx2 - *sh.s_gg) + ps;
-      const float thr = p.eps * p.eps;
-      const float rhs = thr * nx2;
-      const int slow = (nr2 < rhs) ? 0 : 1;
+      int slow = 0;
+      float r = __builtin_nanf("");
+      if (g.mode == kSiteGated) {
+        const float nx2 = *sh.s_nx2;
+        const float nr2 = (nx2 - *sh.s_gg) + ps;
+        const float thr = p.eps * p.eps;
+        const float rhs = thr * nx2;
+        slow = (nr2 < rhs) ? 0 : 1;
+        r = sqrtf(fmaxf(nr2, 0.f) / nx2);
+      }
       *sh.s_gate = slow;
       if (b == 0) {
-        const long long o = (long long)t * p.gate_ld + p.site0 + s;
+        const long long o = t * p.gate_ld + cq.s;
         p.gates[o] = (uint8_t)slow;
-        if (p.rho) p.rho[o] = sqrtf(fmaxf(nr2, 0.f) / nx2);
+        if (p.rho) p.rho[o] = r;
       }
     }
     wait_vmcnt<0>();  // this block's fast-path rows of y are written before a slow path rewrites them
@@ -687,36 +594,14 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, long long q, in
   // ---------------- slow path: y = W x for the owned rows, then E3 ----------------
   if (*sh.s_gate) {
     if (!is_sync) {
-      // one wave per row; each lane keeps kSlowBatch chunk pairs in flight per batch
-      const g4p x4 = (g4p)x;
-      T* yrow = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + L.y_off;
-      for (int r = g.r0 + wave; r < g.r0 + g.nrows; r += kDataThreads / 64) {
-        const g4p wr = (g4p)L.W + (long long)r * g.cprd;
-        float a = 0.f;
-        for (int c0 = 0; c0 < g.cprd; c0 += kSlowBatch * 64) {
-          u32x4 wv[kSlowBatch], xv[kSlowBatch];
-#pragma unroll
-          for (int i = 0; i < kSlowBatch; ++i) {
-            const int c = c0 + lane + 64 * i;
-            const int cc = c < g.cprd ? c : 0;
-            wv[i] = wr[cc];
-            xv[i] = x4[cc];
-          }
-#pragma unroll
-          for (int i = 0; i < kSlowBatch; ++i) {
-            const float v = dot16<T>(wv[i], xv[i], 0.f);
-            a += (c0 + lane + 64 * i < g.cprd) ? v : 0.f;
-          }
-        }
-        a = wave_reduce(a);
-        if (lane == 63) yrow[r] = from_f32<T>(a);
-      }
+      dense_rows<T>(g, x, yrow, wave, lane);
+      wait_vmcnt<0>();
     }
     __syncthreads();
     if (is_sync) {
       if (lane < kReplicas) st_dev(p.box_f + (long long)lane * kMaxBlocks + b, pack(tag_f, 0.f));
       float fv[kMaxBlocks / 64];
-      if (!gather(p, base, p.box_f + (long long)rep * kMaxBlocks, P, tag_f, lane, fv) && lane == 0) *sh.s_abort = 1;
+      if (!gather(p, c.base, p.box_f + (long long)c.rep * kMaxBlocks, P, tag_f, lane, fv) && lane == 0) *sh.s_abort = 1;
     }
     __syncthreads();
     if (*sh.s_abort) return false;
@@ -729,62 +614,93 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   __shared__ u32x4 region0[kRegionChunks];
   __shared__ u32x4 region1[kRegionChunks];
   __shared__ float gsh[kMaxK];
-  __shared__ u32x4 gb[kGbChunks];
   __shared__ float ypart[kYPart];
   __shared__ float red[kDecodeThreads / 64][kMaxJ + 2];
+  __shared__ PlanRow plans[3];
   __shared__ float s_nx2, s_gg;
   __shared__ int s_gate, s_abort;
-  __shared__ unsigned s_base;
+  __shared__ unsigned long long s_base;
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x, P = gridDim.x;
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
-  const unsigned rep = xcc_id() % kReplicas;
-  const u32x4* dummy = reinterpret_cast<const u32x4*>(p.hdr);
-  const Shared sh{gsh, (lu32x4*)gb, ypart, red, &s_nx2, &s_gg, &s_gate, &s_abort};
+  const Shared sh{gsh, ypart, red, plans, &s_nx2, &s_gg, &s_gate, &s_abort};
   lu32x4* const r0 = (lu32x4*)region0;
   lu32x4* const r1 = (lu32x4*)region1;
+  const long long Q = (long long)p.n_steps * p.t_step * p.n_sites;
 
   if (tid == 0) {
-    gb[kGbZero] = u32x4{0u, 0u, 0u, 0u};
     s_abort = 0;
     s_base = __hip_atomic_load(&p.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const long long Q = (long long)p.n_tokens * p.n_sites;
+  __syncthreads();
+  const unsigned long long base = s_base;
+  if (is_sync && lane < kReplicas) {
+    // rewrite every mailbox word this block owns (all replicas) with the launch's unused tag
+    const u64 w0 = pack((unsigned)base, 0.f);
+    for (int j = b; j < kMaxK; j += P) st_dev(p.box_g + (long long)lane * kMaxK + j, w0);
+    for (int j = b; j < kMaxBlocks; j += P) {
+      st_dev(p.box_p + (long long)lane * kMaxBlocks + j, w0);
+      st_dev(p.box_f + (long long)lane * kMaxBlocks + j, w0);
+    }
+  }
+  const StepCtx c0{0, Q, base, b, P, tid, xcc_id() % kReplicas, reinterpret_cast<const u32x4*>(p.hdr)};
 
   u32x4 xw[XR];
-  if (Q > 0 && !is_sync) {  // site 0's region and input row
-    const LayerDesc L0 = load_desc(p.sites, 0);
-    const SiteGeom g0 = geom<T>(L0, b, P);
-    load_x<T, XR>(reinterpret_cast<const T*>(p.X) + L0.x_off, g0, tid, xw);
-    fill_region<T>(L0, g0, b, P, wave, lane, 0, g0.n_inst, (lu32x4*)region0, dummy);
+  if (Q > 0 && !is_sync) {  // plan rows of steps 0 and 1, step 0's region and input row
+    if (wave == 0) fill_plan(p.plan, 0, b, P, lane, plans + 0);
+    if (wave == 1 && Q > 1) fill_plan(p.plan, p.t_step > 1 ? 0 : (p.n_sites > 1 ? 1 : 0), b, P, lane, plans + 1);
     wait_vmcnt<0>();
   }
   __syncthreads();
-  const unsigned base = s_base;
+  if (Q > 0 && !is_sync) {
+    const PlanRow g0 = read_plan(plans + 0);
+    load_x<XR>(reinterpret_cast<const T*>(p.X) + g0.x_off, g0.cprd, tid, xw);
+    fill_region(g0, P, wave, lane, r0, c0.dummy);
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
 
-  int t = 0, s = 0;  // token and site of step q
-  auto advance = [&]() {
-    if (++s == p.n_sites) {
-      s = 0;
-      ++t;
-    }
+  Cursor cq{0, 0, 0};
+  StepCtx c = c0;
+  int sc = 0, sn = 1, sf = 2;  // plan slots: this step, the next, the one after
+  auto rotate = [&]() {
+    const int tmp = sc;
+    sc = sn;
+    sn = sf;
+    sf = tmp;
   };
   for (long long q = 0; q < Q; q += 2) {
-    if (!site_step<T, XR>(p, q, t, s, Q, base, b, P, tid, rep, dummy, r0, r1, xw, sh)) break;
-    advance();
-    if (q + 1 < Q && !site_step<T, XR>(p, q + 1, t, s, Q, base, b, P, tid, rep, dummy, r1, r0, xw, sh)) break;
-    advance();
+    c.q = q;
+    if (!site_step<T, XR>(p, c, cq, r0, r1, xw, sh, sc, sn, sf)) break;
+    cq.advance(p.n_sites, p.t_step);
+    rotate();
+    if (q + 1 >= Q) break;
+    c.q = q + 1;
+    if (!site_step<T, XR>(p, c, cq, r1, r0, xw, sh, sc, sn, sf)) break;
+    cq.advance(p.n_sites, p.t_step);
+    rotate();
   }
   if (!is_sync) wait_vmcnt<0>();  // no copy into LDS outlives the block
-  // advance the tag base for the next launch (also after an abort, so its mark goes stale)
+  // advance the epoch for the next launch (also after an abort, so its mark goes stale)
   if (b == 0 && tid == 0)
-    __hip_atomic_store(&p.hdr->epoch, base + (unsigned)(Q * 4) + 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.hdr->epoch, next_epoch(base, Q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 size_t decode_ws_bytes() {
   return sizeof(WsHeader) + (size_t)kReplicas * kMaxK * 8 + 2 * (size_t)kReplicas * kMaxBlocks * 8;
+}
+
+void decode_boxes(void* ws, WsHeader** hdr, u64** box_g, u64** box_p, u64** box_f) {
+  char* c = (char*)ws;
+  *hdr = (WsHeader*)c;
+  c += sizeof(WsHeader);
+  *box_g = (u64*)c;
+  c += (size_t)kReplicas * kMaxK * 8;
+  *box_p = (u64*)c;
+  c += (size_t)kReplicas * kMaxBlocks * 8;
+  *box_f = (u64*)c;
 }
 
 // Instantiated input windows: XR chunks of 16 bytes per data thread (XR * 256 chunks cover the
@@ -803,28 +719,55 @@ static const void* decode_fn(int dtype, int xr) {
   return nullptr;
 }
 
-static int grid_blocks(const void* fn) {
+int decode_window(int dtype, const LayerDesc* sites, int n_sites) {
+  const int es = dtype == GSI_F32 ? 4 : 2;
+  int need_x = 1;
+  for (int i = 0; i < n_sites; ++i) need_x = std::max(need_x, (sites[i].d * es / 16 + kDataThreads - 1) / kDataThreads);
+  return need_x;
+}
+
+int decode_grid(int dtype, int xr) {
+  const void* fn = decode_fn(dtype, xr);
+  if (!fn) return 0;
   int dev = 0, ncu = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kDecodeThreads, 0) != hipSuccess) return 0;
   long long cap = (long long)ncu * per;
-  return (int)(cap < kMaxBlocks ? cap : kMaxBlocks);
+  int P = (int)(cap < kMaxBlocks ? cap : kMaxBlocks);
+  while (P & (P - 1)) P &= P - 1;  // a power of two: the work split uses shifts
+  return P < kMinBlocks ? 0 : P;
 }
 
-int launch_decode(int dtype, const DecodeParams& prm, const LayerDesc* host_sites, hipStream_t s) {
-  const int es = dtype == GSI_F32 ? 4 : 2;
-  int need_x = 1;
-  for (int i = 0; i < prm.n_sites; ++i)
-    need_x = std::max(need_x, (host_sites[i].d * es / 16 + kDataThreads - 1) / kDataThreads);
-  const void* fn = decode_fn(dtype, need_x);
+__global__ void plan_kernel(LayerDesc d, int P, int es, PlanRow* out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < P) out[b] = make_plan_row(d, b, P, es);
+}
+
+int launch_plan(const LayerDesc& d, int P, int es, PlanRow* out, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3((P + 255) / 256), dim3(256), 0, s, d, P, es, out);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
+  const void* fn = decode_fn(dtype, a.xr);
   if (!fn) return GSI_ERR_DTYPE;
-  int P = grid_blocks(fn);
-  while (P & (P - 1)) P &= P - 1;  // a power of two: the kernel splits work with shifts
-  if (P < kMinBlocks) return GSI_ERR_DEVICE;
-  DecodeParams p = prm;
+  DecodeParams p;
+  p.plan = a.plan;
+  p.n_sites = a.n_sites;
+  p.n_steps = a.n_steps;
+  p.t_step = a.t_step;
+  p.X = a.X;
+  p.x_ld = a.x_ld;
+  p.Y = a.Y;
+  p.y_ld = a.y_ld;
+  p.gates = a.gates;
+  p.rho = a.rho;
+  p.gate_ld = a.gate_ld;
+  p.eps = a.eps;
+  decode_boxes(a.ws, &p.hdr, &p.box_g, &p.box_p, &p.box_f);
   void* args[] = {&p};
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(kDecodeThreads), args, 0, s);
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.P), dim3(kDecodeThreads), args, 0, s);
   return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 

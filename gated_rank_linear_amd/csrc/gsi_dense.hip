@@ -399,6 +399,33 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The same sum for a dense m x n output read and written four columns at a time (n a multiple of
+// 4), with I subtracted on request (V^T V - I).
+template <typename TC>
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __restrict__ part, int splits, int m, int n,
+                                                             void* __restrict__ C, long long ldc, int sub_identity) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  const long long total = (long long)m * (n / 4);
+  if (q >= total) return;
+  const int mm = (int)(q / (n / 4)), n4 = (int)(q % (n / 4)) * 4;
+  const long long stride = (long long)m * n;
+  const float4* p = reinterpret_cast<const float4*>(part + (long long)mm * n + n4);
+  float4 v = p[0];
+  for (int z = 1; z < splits; ++z) {
+    const float4 w = p[z * (stride / 4)];
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (sub_identity && mm == n4 + e) vv[e] -= 1.0f;
+    st_from_f32<TC>(C, (long long)mm * ldc + n4 + e, vv[e]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Matrix-core NT GEMM for 16-bit A and B with K a multiple of 32, staged through LDS: 128x128
 // output tile per block of 4 waves (2 x 2, 64x64 each = 4 x 4 tiles of 16x16). Each 32-column
@@ -512,12 +539,15 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __res
 
 // ---------------------------------------------------------------------------------------------
 // Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): MT x 256
-// output tile per block of 4 waves (MT = 16, 32 or 64 rows, chosen so the grid fills the chip),
-// so A (the weight, d_out x d) streams from memory once per 256 columns. Wave w owns columns
-// 64 w .. 64 w + 63. A 64-column K step is NB operand blocks of 1 KB (A: 2 sub-steps x MT / 16
-// row tiles; B: 2 x 16 column tiles), copied straight into LDS in MFMA operand order, three
-// stages in flight. Every wave issues the same number of copies per step: when NB is not a
-// multiple of 4 the spare copies repeat the first blocks (same data to the same place).
+// output tile per block of 4 waves (MT = 16, 32, 64 or 128 rows), so A (the weight, d_out x d)
+// streams from memory once per 256 columns. Wave w owns columns 64 w .. 64 w + 63. A 64-column
+// K step is NB operand blocks of 1 KB (A: 2 sub-steps x MT / 16 row tiles; B: 2 x 16 column
+// tiles), copied straight into LDS in MFMA operand order, three stages in flight. Every wave
+// issues the same number of copies per step: when NB is not a multiple of 4 the spare copies
+// repeat the first blocks (same data to the same place).
+// Split K: block z covers K columns [z k_chunk, (z + 1) k_chunk) (k_chunk a multiple of 64) and,
+// when `part` is given, stores its raw float32 sums to part[z][m][n] for a reduction in chunk
+// order; otherwise (k_chunk >= kdim) it writes C.
 // ---------------------------------------------------------------------------------------------
 template <typename T, typename TC, int MT>
 __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restrict__ A, long long lda,
@@ -525,7 +555,8 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
                                                            const void* __restrict__ B, long long ldb,
                                                            void* __restrict__ C, long long ldc,
                                                            const int* __restrict__ c_idx, int m, int n, int kdim,
-                                                           const int* __restrict__ m_count, int sub_identity) {
+                                                           const int* __restrict__ m_count, int sub_identity,
+                                                           int k_chunk, float* __restrict__ part) {
   constexpr int RT = MT / 16, NA = 2 * RT, NB = NA + 32, CPW = (NB + 3) / 4;
   __shared__ mu32x4 st0[NB * 64], st1[NB * 64], st2[NB * 64];
   const int mv = m_count ? min(m, *m_count) : m;
@@ -580,12 +611,13 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
   do {                                                                                                 \
     dwait_vmcnt<CPW>();                                                                                \
     dlds_barrier();                                                                                    \
-    GSI_WISSUE(FUT, min((ST) + 2, nk - 1) * 64);                                                       \
+    GSI_WISSUE(FUT, kb + min((ST) + 2, nk - 1) * 64);                                                  \
     GSI_WCOMPUTE(CUR);                                                                                 \
   } while (0)
-  const int nk = kdim / 64;
-  GSI_WISSUE(st0, 0);
-  GSI_WISSUE(st1, min(1, nk - 1) * 64);
+  const int kb = (int)blockIdx.z * k_chunk;
+  const int nk = (min(kdim, kb + k_chunk) - kb) / 64;
+  GSI_WISSUE(st0, kb);
+  GSI_WISSUE(st1, kb + min(1, nk - 1) * 64);
   int s0 = 0;
   for (; s0 + 3 <= nk; s0 += 3) {
     GSI_WSTEP(st0, st2, s0);
@@ -598,6 +630,19 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
 #undef GSI_WSTEP
 #undef GSI_WCOMPUTE
 #undef GSI_WISSUE
+  if (part) {
+    float* pz = part + (long long)blockIdx.z * m * n;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = m0 + i * 16 + 4 * (lane >> 4) + r;
+        if (mm >= mv) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pz[(long long)mm * n + n0 + wave * 64 + j * 16 + (lane & 15)] = acc[i][j][r];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -684,7 +729,10 @@ static void* pick_wide_c(int c_type) {
 
 template <typename T>
 static void* pick_wide(int mt, int c_type) {
-  return mt == 64 ? pick_wide_c<T, 64>(c_type) : mt == 32 ? pick_wide_c<T, 32>(c_type) : pick_wide_c<T, 16>(c_type);
+  return mt == 128 ? pick_wide_c<T, 128>(c_type)
+         : mt == 64 ? pick_wide_c<T, 64>(c_type)
+         : mt == 32 ? pick_wide_c<T, 32>(c_type)
+                    : pick_wide_c<T, 16>(c_type);
 }
 
 template <typename T>
@@ -831,7 +879,10 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
     fn = a_type == GSI_BF16 ? pick_wide<bf16_t>(mt, c_type) : pick_wide<f16_t>(mt, c_type);
     if (!fn) return GSI_ERR_DTYPE;
     dim3 grid((m + mt - 1) / mt, n / 256);
-    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity};
+    int k_chunk = kdim;
+    float* no_part = nullptr;
+    void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity,
+                    &k_chunk, &no_part};
     hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
@@ -1056,6 +1107,86 @@ int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int
 // paths): the register-fed matrix-core kernel over S chunks of K, raw sums into part
 // ([S, m, n] float32, at least part_elems long), then their sum in chunk order into C. Falls back
 // to launch_gemm_nt when the types have no matrix-core kernel or S would be 1.
+// ---------------------------------------------------------------------------------------------
+// Create-time precompute with a workspace [GSI §2.1]: M = W V on 128 x 256 tiles split over K
+// (each K chunk at least 512 columns, about 192 or more blocks in all) with a fixed-order
+// reduction, and V^T V - I on 16 x 16 tiles split over K the same way. Without a workspace (or
+// for shapes the tiles do not fit) the single-pass kernels run instead.
+// ---------------------------------------------------------------------------------------------
+int precompute_splits(int dtype, int d_out, int d, int k) {
+  if (dtype == GSI_F32 || k % 256 != 0 || d % 512 != 0 || d_out < 128) return 1;
+  const long long tiles = (long long)((d_out + 127) / 128) * (k / 256);
+  int sp = 1;
+  // K chunks of at least 512 columns, each a whole number of 64-column steps
+  while (tiles * sp < 192 && sp < 16 && d % (2 * sp) == 0 && d / (2 * sp) >= 512 && (d / (2 * sp)) % 64 == 0) sp *= 2;
+  return sp;
+}
+
+int delta_splits(int dtype, int d, int k) {
+  if (dtype == GSI_F32 || d % 32 != 0 || d < 1024 || k > 1024) return 1;
+  const long long tiles16 = (long long)((k + 15) / 16) * ((k + 15) / 16);
+  int splits = (int)std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles16 - 1) / tiles16));
+  return std::min(splits, std::max(1, d / 512));
+}
+
+size_t precompute_ws_bytes(int dtype, int d_out, int d, int k) {
+  const int sm = precompute_splits(dtype, d_out, d, k), sd = delta_splits(dtype, d, k);
+  const long long em = sm > 1 ? (long long)sm * d_out * k : 0, ed = sd > 1 ? (long long)sd * k * k : 0;
+  const long long e = std::max(em, ed);
+  return e ? (size_t)(e * 4 + 255) / 256 * 256 : 0;
+}
+
+int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
+                      void* ws, size_t ws_bytes, hipStream_t s) {
+  float* part = (float*)ws;
+  // M = W V = W (V^T)^T
+  const int sm = precompute_splits(dtype, d_out, d, k);
+  if (ws && sm > 1 && (size_t)sm * d_out * k * 4 <= ws_bytes) {
+    void* fn = dtype == GSI_BF16 ? pick_wide<bf16_t>(128, GSI_F32) : pick_wide<f16_t>(128, GSI_F32);
+    if (!fn) return GSI_ERR_DTYPE;
+    int k_chunk = d / sm;
+    const void* A = W;
+    long long lda = d;
+    const int* no_idx = nullptr;
+    const void* B = Vt;
+    long long ldb = d;
+    void* C = part;
+    long long ldc = k;
+    int m = d_out, n = k, kdim = d, sub = 0;
+    dim3 grid((d_out + 127) / 128, k / 256, sm);
+    void* args[] = {&A, &lda, &no_idx, &B, &ldb, &C, &ldc, &no_idx, &m, &n, &kdim, &no_idx, &sub, &k_chunk, &part};
+    if (hipLaunchKernel(fn, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+    const long long groups = (long long)d_out * (k / 4);
+    if (dtype == GSI_BF16)
+      splitk_reduce4_kernel<bf16_t><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, sm, d_out, k, M, k, 0);
+    else
+      splitk_reduce4_kernel<f16_t><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, sm, d_out, k, M, k, 0);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+  } else {
+    const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
+    if (rc != GSI_OK) return rc;
+  }
+  // V^T V - I (float32)
+  const int sd = delta_splits(dtype, d, k);
+  if (ws && sd > 1 && (size_t)sd * k * k * 4 <= ws_bytes) {
+    void* kf = dtype == GSI_BF16 ? pick_kslice_c<bf16_t>(GSI_F32) : pick_kslice_c<f16_t>(GSI_F32);
+    int k_chunk = ((d + sd - 1) / sd + 31) / 32 * 32;
+    int splits = (d + k_chunk - 1) / k_chunk;
+    const void* A = Vt;
+    long long lda = d;
+    void* c_unused = part;
+    long long ldc_unused = k;
+    int m = k, n = k, kdim = d, sub = 0;
+    dim3 grid((k + 15) / 16, (k + 15) / 16, splits);
+    void* args[] = {&A, &lda, &A, &lda, &c_unused, &ldc_unused, &m, &n, &kdim, &sub, &k_chunk, &part};
+    if (hipLaunchKernel(kf, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+    const long long groups = (long long)k * (k / 4);
+    splitk_reduce4_kernel<float><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, splits, k, k, Dl, k, 1);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
+  return launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s);
+}
+
 int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
                          const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n,
                          int kdim, const int* m_count, float* part, long long part_elems, hipStream_t s) {
@@ -1146,15 +1277,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ sr
     int c = c0 + i, r = r0 + tx;
     if (r < d && c < k) dst[(long long)c * d + r] = t[tx][i];
   }
-}
-
-__global__ void write_desc_kernel(LayerDesc d, LayerDesc* dst) {
-  if (threadIdx.x == 0) *dst = d;
-}
-
-int launch_write_desc(const LayerDesc& d, LayerDesc* dst, hipStream_t s) {
-  write_desc_kernel<<<1, 64, 0, s>>>(d, dst);
-  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s) {
@@ -1268,12 +1390,36 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   return w;
 }
 
+// Gate bits and token lists of a site without a gate: a static-projection site sends every token
+// to the fast path, a dense site every token to the slow path; rho is reported as NaN.
+__global__ __launch_bounds__(256) void mode_lists_kernel(int T, int slow, uint8_t* __restrict__ gate, int gate_ld,
+                                                         float* __restrict__ rho, int* __restrict__ fast_idx,
+                                                         int* __restrict__ slow_idx, int* __restrict__ counts) {
+  for (int t = threadIdx.x; t < T; t += 256) {
+    gate[(long long)t * gate_ld] = (uint8_t)slow;
+    if (rho) rho[(long long)t * gate_ld] = __builtin_nanf("");
+    (slow ? slow_idx : fast_idx)[t] = t;
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = slow ? 0 : T;
+    counts[1] = slow ? T : 0;
+  }
+}
+
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s) {
+  if (L.mode == kSiteDense) {
+    mode_lists_kernel<<<1, 256, 0, s>>>(T, 1, gate, gate_ld, rho, w.fast_idx, w.slow_idx, w.counts);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   // G = X V as X (V^T)^T: [T, k] float32
   int rc = launch_gemm_nt_split(dtype, dtype, GSI_F32, X, x_ld, nullptr, L.Vt, L.d, w.G, L.k, nullptr, T, L.k, L.d,
                                 nullptr, w.part, w.part_elems, s);
   if (rc != GSI_OK) return rc;
+  if (L.mode == kSiteStatic) {
+    mode_lists_kernel<<<1, 256, 0, s>>>(T, 0, gate, gate_ld, rho, w.fast_idx, w.slow_idx, w.counts);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
   // H = G (V^T V - I)  (the matrix is symmetric, so its rows serve as the K-contiguous operand)
   rc = launch_gemm_nt(GSI_F32, GSI_F32, GSI_F32, w.G, L.k, nullptr, L.Dl, L.k, w.H, L.k, nullptr, T, L.k, L.k,
                       nullptr, 0, s);

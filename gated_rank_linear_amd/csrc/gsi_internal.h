@@ -6,6 +6,7 @@
 #include <stddef.h>
 
 #include "../../include/gsi.h"
+#include "gsi_plan.h"
 
 namespace gsi {
 
@@ -72,28 +73,21 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------------------------
 // Layer and stack handles
 // ---------------------------------------------------------------------------------------------
-struct LayerDesc {  // device-side description of one site (also used host-side)
-  const void* Vt;     // [k, d]
-  const void* M;      // [d_out, k]
-  const float* Dl;    // [k, k] = V^T V - I
-  const void* W;      // [d_out, d]
-  int d, d_out, k, pad;
-  long long x_off, y_off;  // column offsets into stacked X / Y rows
-};
-
 }  // namespace gsi
 
 struct gsi_layer {
   int dtype, d_out, d, k;
-  gsi::LayerDesc desc;       // x_off = y_off = 0
-  gsi::LayerDesc* dev_desc;  // device copy, stored in the layer's aux buffer
+  int P, xr;                 // decode grid and input window the plan was made for
+  gsi::LayerDesc desc;       // x_off = y_off = 0, mode = gated
+  gsi::PlanRow* plan;        // [P] plan rows of the decode kernel, in the layer's aux buffer
 };
 
 struct gsi_stack {
   int dtype, n_sites, k_max, d_max, d_out_max;
+  int P, xr;
   long long x_ld, y_ld;
-  gsi::LayerDesc* d_table;  // device copy
-  gsi::LayerDesc* h_table;  // host copy
+  gsi::PlanRow* d_plan;     // [n_sites][P] plan rows (device, owned)
+  gsi::LayerDesc* h_table;  // host copy of the site descriptors
   gsi_layer** layers;       // host copy of the borrowed handles
 };
 
@@ -101,48 +95,47 @@ namespace gsi {
 
 // Workspace header (start of every workspace)
 struct WsHeader {
-  unsigned epoch;  // exchange tag base, advanced by every persistent launch
-  int status;      // GSI_OK or GSI_ERR_TIMEOUT (sticky until read by gsi_workspace_status)
-  unsigned abort_tag;  // tag base + 1 of a launch that gave up waiting
-  unsigned pad[61];
+  unsigned long long epoch;       // exchange tag base, advanced by every persistent launch
+  unsigned long long abort_mark;  // epoch + 1 of a launch that gave up waiting
+  int status;                     // GSI_OK or GSI_ERR_TIMEOUT (sticky until read by gsi_workspace_status)
+  unsigned pad[59];
 };
+static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 
 // ---------------------------------------------------------------------------------------------
-// Persistent decode kernel (batch of n_tokens processed one token at a time through all sites)
+// Persistent decode kernel (tokens processed one at a time through the sites)
 // ---------------------------------------------------------------------------------------------
 constexpr int kReplicas = 8;       // one mailbox copy per XCD
 constexpr int kMaxBlocks = 256;    // persistent blocks (one per CU)
 constexpr int kMaxK = 512;
-constexpr int kDataThreads = 256;  // 4 data waves
 constexpr int kSyncThreads = 64;   // 1 sync wave
 constexpr int kDecodeThreads = kDataThreads + kSyncThreads;
-constexpr int kRegionChunks = 4096;  // 16-byte chunks per LDS site region (two regions, 64 KB each)
 constexpr int kYPart = 2048;         // rows of y per block held in LDS before they are stored
 constexpr int kMinBlocks = kMaxK / 4;  // the decode grid needs at least this many blocks
 
-struct DecodeParams {
-  const LayerDesc* sites;  // device table of n_sites descriptors
-  int n_sites, n_tokens;
+struct DecodeArgs {
+  const PlanRow* plan;  // [n_sites][P]
+  int n_sites, n_steps, t_step;
   const void* X;
   long long x_ld;
   void* Y;
   long long y_ld;
-  uint8_t* gates;  // [n_tokens, gate_ld]
-  float* rho;      // optional
-  int gate_ld, site0;  // column of site 0 in gates/rho
+  uint8_t* gates;
+  float* rho;
+  int gate_ld;
   float eps;
-  int k_max, d_max;
-  WsHeader* hdr;
-  u64* box_g;  // [kReplicas][kMaxK]       g values
-  u64* box_p;  // [kReplicas][kMaxBlocks]  per-block gate pieces
-  u64* box_f;  // [kReplicas][kMaxBlocks]  slow-path completion
+  void* ws;  // workspace: header and mailboxes (decode_ws_bytes)
+  int P, xr;
 };
 
 size_t decode_ws_bytes();
-// host_sites: host copy of the n_sites descriptors (used to size the register windows)
-int launch_decode(int dtype, const DecodeParams& p, const LayerDesc* host_sites, hipStream_t s);
-// enqueue a copy of `d` (passed by value) into device memory `dst`
-int launch_write_desc(const LayerDesc& d, LayerDesc* dst, hipStream_t s);
+// input window (16-byte chunks per data thread) the kernel needs for these sites
+int decode_window(int dtype, const LayerDesc* sites, int n_sites);
+// co-resident grid (a power of two >= kMinBlocks) for the kernel with that window; 0 if none
+int decode_grid(int dtype, int xr);
+// plan rows of one site for a grid of P blocks, computed on the device into out[0..P)
+int launch_plan(const LayerDesc& d, int P, int es, PlanRow* out, hipStream_t s);
+int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Dense helpers (create time and the batched path)
@@ -154,6 +147,11 @@ int launch_write_desc(const LayerDesc& d, LayerDesc* dst, hipStream_t s);
 int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
                    const void* B, long long ldb, void* C, long long ldc, const int* c_idx, int m, int n, int kdim,
                    const int* m_count, int sub_identity, hipStream_t s);
+// Create-time products M = W V and V^T V - I (float32); with a workspace of at least
+// precompute_ws_bytes() they run split over K with fixed-order reductions (0: no workspace used)
+size_t precompute_ws_bytes(int dtype, int d_out, int d, int k);
+int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
+                      void* ws, size_t ws_bytes, hipStream_t s);
 // dst[k, d] = transpose(src[d, k])
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s);
 // float32 C[m, n] = A B^T for a small output and a long K, K split over blocks (partial sums in

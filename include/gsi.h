@@ -36,7 +36,9 @@
  *    returns an error code has enqueued nothing. Faults inside kernels surface at the caller's
  *    next synchronisation; a wait inside a kernel that exceeds its time bound records
  *    GSI_ERR_TIMEOUT in the workspace (see gsi_workspace_status).
- *  - Calls on one workspace must not overlap (use one workspace per stream).
+ *  - Calls on one workspace must not overlap (use one workspace per stream). The workspace keeps
+ *    a 64-bit launch counter that tags the in-kernel exchange words; no tag repeats within the
+ *    life of a workspace, so it never needs clearing after the first zero fill.
  */
 #ifndef GSI_H
 #define GSI_H
@@ -49,6 +51,18 @@ extern "C" {
 #endif
 
 enum gsi_dtype { GSI_F32 = 0, GSI_F16 = 1, GSI_BF16 = 2 };
+
+/*
+ * What one site of a stack computes for every token.
+ *   GSI_SITE_GATED   the method: gate on rho < eps, y = M g (fast) or W x (slow) [GSI §2.2].
+ *   GSI_SITE_STATIC  static projection: y = M g for every token, with no residual norm and no
+ *                    gate (the limit eps > 1 of the gate for x != 0) [GSI §2.2, closing remark
+ *                    on static projection; §4 negative control]. gate = 0, rho = NaN.
+ *   GSI_SITE_DENSE   y = W x for every token: a linear map left outside the method, e.g. the
+ *                    attention maps of a stack that gates only its MLP maps (the MLP-only
+ *                    predecessor named in [GSI §2]). gate = 1, rho = NaN.
+ */
+enum gsi_site_mode { GSI_SITE_GATED = 0, GSI_SITE_STATIC = 1, GSI_SITE_DENSE = 2 };
 
 enum gsi_status {
   GSI_OK = 0,
@@ -74,9 +88,19 @@ int gsi_device_check(void);
 
 /*
  * Bytes of per-layer derived data ("aux") that gsi_layer_create fills: V^T [k, d] in the weight
- * dtype, then V^T V - I [k, k] in float32, each 256-byte aligned. 0 for invalid arguments.
+ * dtype, then V^T V - I [k, k] in float32, each 256-byte aligned, then the work split of the
+ * batch-1 kernel (32 KiB). k = 0 gives the size for gsi_layer_create_dense (the work split only).
+ * 0 for invalid arguments.
  */
 size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k);
+
+/*
+ * Scratch bytes gsi_layer_create can use for this shape (0 when it has no use for any). With at
+ * least this much, the precomputation runs its products split over K across the chip (float32
+ * partial sums added in a fixed order, so the result does not depend on scheduling); without it
+ * a single-pass kernel runs. 0 also for invalid arguments.
+ */
+size_t gsi_layer_create_workspace_bytes(int dtype, int d_out, int d, int k);
 
 /*
  * Create a GSI layer [GSI §2.1]: enqueue on `stream` the precomputation of the cached low-rank
@@ -84,14 +108,26 @@ size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k);
  * accumulation, rounded to nearest even) and of aux (V^T and V^T V - I). Returns after enqueueing;
  * *out receives a small host handle that borrows W, M and aux (V is not used after the
  * precomputation has run). On error *out is left NULL.
+ * ws / ws_bytes: optional device scratch (NULL, or at least gsi_layer_create_workspace_bytes;
+ * GSI_ERR_WORKSPACE if smaller), used only by the work this call enqueues: it may be reused for
+ * the next call on the same stream, or freed once the stream has passed this call.
  */
 int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const void* W, const void* V,
-                     void* M, void* aux, size_t aux_bytes, void* stream);
+                     void* M, void* aux, size_t aux_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Create a dense layer (no basis): every token takes y = W x, gate = 1, rho = NaN. Used for the
+ * linear maps a stack leaves outside the method (GSI_SITE_DENSE). aux: gsi_layer_aux_bytes with
+ * k = 0. Same shape rules as gsi_layer_create without k; same ownership and errors.
+ */
+int gsi_layer_create_dense(gsi_layer** out, int dtype, int d_out, int d, const void* W, void* aux, size_t aux_bytes,
+                           void* stream);
 
 /* Free the host handle (device buffers remain the caller's). NULL is accepted. */
 int gsi_layer_destroy(gsi_layer* L);
 
-/* Workspace bytes gsi_forward needs for up to T_max tokens on a layer of this shape. */
+/* Workspace bytes gsi_forward needs for up to T_max tokens on a layer of this shape (k = 0 for a
+ * dense layer). */
 size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max);
 
 /*
@@ -108,10 +144,16 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
 /*
  * A stack of layers ("sites") run in order, as every linear map of a transformer block
  * (QKV, output, MLP in and out) and block after block [GSI §3]. `sites` is a HOST array of
- * n_sites layer handles, all of one dtype; the stack borrows them. The library allocates a small
- * device table for the stack (freed by gsi_stack_destroy).
+ * n_sites layer handles, all of one dtype; the stack borrows them. The library allocates the
+ * work split of every (site, block) of the batch-1 kernel on the device (128 bytes each, freed by
+ * gsi_stack_destroy); creation synchronises with the device once.
+ * gsi_stack_create runs every layer in its own mode (gated, or dense for a dense layer);
+ * gsi_stack_create_modes takes a HOST array of n_sites gsi_site_mode values instead (NULL: the
+ * layers' own modes). A dense layer only accepts GSI_SITE_DENSE (GSI_ERR_SHAPE otherwise, as for
+ * an unknown mode).
  */
 int gsi_stack_create(gsi_stack** out, gsi_layer* const* sites, int n_sites);
+int gsi_stack_create_modes(gsi_stack** out, gsi_layer* const* sites, const int* modes, int n_sites);
 int gsi_stack_destroy(gsi_stack* S);
 
 /* Workspace bytes gsi_stack_decode needs for steps of T_step tokens. */
@@ -125,8 +167,10 @@ size_t gsi_stack_workspace_bytes(const gsi_stack* S, int T_step);
  *   rho   [n_steps * T_step, n_sites] float32, optional (NULL)
  * Sites run in order within a step and steps run in order; each site starts after the previous
  * site's output and gate are complete. Site inputs are read from X (they are not chained from
- * the previous site's output). T_step = 1 runs one persistent kernel for the whole decode
- * (batch-1); T_step >= 2 runs the batched path per (step, site).
+ * the previous site's output). T_step < 16 runs one persistent kernel for the whole call, one
+ * token at a time (inside a step: each site for each of the step's tokens in turn) on the vector
+ * ALU; n_steps * T_step * n_sites must then be below 2^28 (GSI_ERR_SHAPE). T_step >= 16 runs the
+ * batched path per (step, site), whose products use the matrix cores.
  */
 int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
                      float* rho, void* ws, size_t ws_bytes, void* stream);

@@ -160,3 +160,22 @@ def spectral_norm(W, tol=1e-12, max_iter=100000, seed=0) -> float:
             break
         lam = nu
     return float(np.sqrt(lam))
+
+
+def static_projection(W, V, X, M=None) -> dict:
+    """Static projection [GSI §2.2, closing remark; §4 negative control]: every token takes the
+    fast path, y = M g with g = V^T x, no gate. Returns y and g."""
+    W = as_f64(W)
+    V = as_f64(V)
+    X = np.atleast_2d(as_f64(X))
+    M = precompute_image(W, V) if M is None else as_f64(M)
+    G = project(V, X)
+    return {"y": G @ M.T, "g": G}
+
+
+def dense(W, X) -> np.ndarray:
+    """The unmodified linear map y = W x for every token (a site left outside the method)."""
+    W = as_f64(W)
+    X = np.atleast_2d(as_f64(X))
+    return X @ W.T
+

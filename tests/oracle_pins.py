@@ -15,6 +15,9 @@ copy) and raises AssertionError when the oracle disagrees with an independent fa
       stored basis where the explicit residual differs from 1 - |g|^2/|x|^2
   P8  exact ties go slow; x = 0, NaN and Inf go slow                 [GSI §2.2: slow iff rho >= eps]
   P9  per-token independence: T-row call equals T one-row calls       [GSI §2.2: per-token gate]
+  P10 static projection: y = W P x with P the orthogonal projector onto span(V), computed through
+      least squares; equal to the gated forward at eps > 1 on nonzero tokens [GSI §2.2, §4]
+  P11 dense map: exact integer W x                                    [a site outside the method]
 """
 from __future__ import annotations
 
@@ -260,9 +263,34 @@ def pin_per_token(orc):
         assert np.max(np.abs(one["y"][0] - full["y"][t])) <= 1e-14 * np.max(np.abs(full["y"][t]))
 
 
+def pin_static_projection(orc):
+    rng, W, V, C = _case(10)
+    X = _mixed_tokens(rng, V, C, n=12)
+    out = orc.static_projection(W, V, X)
+    coef = np.linalg.lstsq(V, X.T, rcond=None)[0]
+    ref = (W @ (V @ coef)).T
+    assert np.max(np.abs(out["y"] - ref)) <= 1e-11 * np.max(np.abs(ref)), "static projection != W P x"
+    # a non-orthonormal stored basis: y = M (V^T x) is what the fast path returns, not W P x
+    Vs = V * 1.01
+    o2 = orc.static_projection(W, Vs, X)
+    assert np.max(np.abs(o2["y"] - (X @ Vs) @ (W @ Vs).T)) <= 1e-12 * np.max(np.abs(o2["y"]))
+    fwd = orc.forward(W, V, X, 1.5)
+    assert np.all(fwd["gate"] == orc.FAST)
+    assert np.max(np.abs(fwd["y"] - out["y"])) <= 1e-12 * np.max(np.abs(ref))
+
+
+def pin_dense(orc):
+    rng = np.random.default_rng(12)
+    Wi = rng.integers(-9, 10, size=(7, 16))
+    Xi = rng.integers(-9, 10, size=(5, 16))
+    exact = Xi @ Wi.T                                       # integer arithmetic, exact
+    got = orc.dense(Wi.astype(np.float64), Xi.astype(np.float64))
+    assert np.array_equal(got, exact.astype(np.float64)), "dense map is not W x"
+
+
 ALL_PINS = [pin_decomposition, pin_in_span, pin_orthogonal, pin_eps_zero, pin_eps_above_one,
             pin_spectral_norm, pin_theorem4, pin_brute_force_d8, pin_non_orthonormal,
-            pin_ties_and_degenerate, pin_per_token]
+            pin_ties_and_degenerate, pin_per_token, pin_static_projection, pin_dense]
 
 
 def failing_pins(orc):

@@ -55,13 +55,35 @@ def test_aux_and_workspace_sizes(dtype, d_out, d, k, ok):
 def test_layer_create_validation_before_device():
     h = vp()
     p = vp(256)  # never dereferenced: validation fails first
-    assert lib.gsi_layer_create(None, 2, 16, 16, 8, p, p, p, p, 1 << 20, None) == -1
-    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, None, p, p, p, 1 << 20, None) == -1
+    assert lib.gsi_layer_create(None, 2, 16, 16, 8, p, p, p, p, 1 << 20, None, 0, None) == -1
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, None, p, p, p, 1 << 20, None, 0, None) == -1
     assert h.value is None
-    assert lib.gsi_layer_create(ctypes.byref(h), 7, 16, 16, 8, p, p, p, p, 1 << 20, None) == -3
-    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 24, p, p, p, p, 1 << 20, None) == -2
-    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, vp(257), p, p, p, 1 << 20, None) == -6
-    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, p, p, p, p, 16, None) == -5
+    assert lib.gsi_layer_create(ctypes.byref(h), 7, 16, 16, 8, p, p, p, p, 1 << 20, None, 0, None) == -3
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 24, p, p, p, p, 1 << 20, None, 0, None) == -2
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, vp(257), p, p, p, 1 << 20, None, 0, None) == -6
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, p, p, p, p, 16, None, 0, None) == -5
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 16, 16, 8, p, p, p, p, 1 << 20, vp(264), 1 << 20, None) == -6
+    # a create workspace smaller than asked for
+    need = lib.gsi_layer_create_workspace_bytes(2, 4096, 4096, 256)
+    assert lib.gsi_layer_create(ctypes.byref(h), 2, 4096, 4096, 256, p, p, p, p, 1 << 30, p, need - 256, None) == -5
+    assert lib.gsi_layer_create_dense(ctypes.byref(h), 2, 16, 12, p, p, 1 << 20, None) == -2
+    assert lib.gsi_layer_create_dense(ctypes.byref(h), 2, 16, 16, None, p, 1 << 20, None) == -1
+    assert lib.gsi_layer_create_dense(ctypes.byref(h), 2, 16, 16, p, p, 16, None) == -5
+
+
+@pytest.mark.parametrize("dtype,d_out,d,k,splits_m", [
+    (2, 4096, 4096, 256, 8), (2, 4096, 16384, 256, 8), (2, 12288, 4096, 256, 2), (2, 16384, 4096, 256, 2),
+    (1, 2304, 768, 256, 0), (0, 768, 768, 64, 0), (2, 4096, 4096, 512, 4), (2, 1000, 2048, 256, 4),
+])
+def test_create_workspace_sizes(dtype, d_out, d, k, splits_m):
+    """The create workspace holds the K-split partial sums of M = W V (float32, splits x d_out x
+    k) when the shape takes the split path, and of V^T V - I otherwise (0 for float32)."""
+    w = lib.gsi_layer_create_workspace_bytes(dtype, d_out, d, k)
+    if splits_m:
+        assert w >= splits_m * d_out * k * 4
+    if dtype == 0:
+        assert w == 0
+    assert lib.gsi_layer_create_workspace_bytes(dtype, d_out, d, 24) == 0
 
 
 def test_forward_and_stack_validation_before_device():
@@ -73,6 +95,8 @@ def test_forward_and_stack_validation_before_device():
     arr = (vp * 1)(None)
     assert lib.gsi_stack_create(ctypes.byref(h), arr, 1) == -1
     assert lib.gsi_stack_create(ctypes.byref(h), arr, 0) == -2
+    assert lib.gsi_stack_create_modes(ctypes.byref(h), arr, None, 0) == -2
+    assert lib.gsi_stack_create_modes(ctypes.byref(h), None, None, 1) == -1
     assert lib.gsi_stack_decode(None, p, 1, 1, ctypes.c_float(0.1), p, p, None, p, 1 << 20, None) == -1
     assert lib.gsi_stack_workspace_bytes(None, 1) == 0
     assert lib.gsi_workspace_status(None, 0, None, None) == -1

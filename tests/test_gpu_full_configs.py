@@ -128,14 +128,17 @@ def test_zero_tokens_is_a_no_op(g):
     assert torch.all(y == 7.0) and int(gate.item()) == 9
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("shape", [(12300, 1024, 256), (6150, 1024, 256), (1000, 2048, 256), (3000, 1024, 512),
-                                   (300, 4096, 512)])
-def test_precompute_tile_paths(g, dtype, shape):
-    """The precompute M = W V on the matrix-core tile paths: 64-, 32- and 16-row tiles of the wide
-    kernel (chosen by d_out), two 256-column tiles (k = 512), ragged last row tiles, and the
-    K-split kernel of V^T V - I (d >= 1024), whose effect is checked through rho of single
-    tokens (persistent path) against the oracle's residual norms."""
+                                   (300, 4096, 512), (4096, 16384, 256), (200, 2560, 256)])
+def test_precompute_tile_paths(g, dtype, shape, split):
+    """The precompute M = W V on the matrix-core tile paths: with a create workspace, 128 x 256
+    tiles split over K (2 to 16 chunks, ragged last row tiles, K chunks of 512 to 2048 columns)
+    and V^T V - I split over K; without one, the 64-, 32- and 16-row tiles of the single-pass
+    kernel (chosen by d_out), two 256-column tiles (k = 512) and the one-pass V^T V - I kernel.
+    V^T V - I is checked through rho of single tokens (persistent path) against the oracle's
+    residual norms."""
     d_out, d, k = shape
     rng = np.random.default_rng(d_out + 3 * d + k)
     Q, R = np.linalg.qr(rng.standard_normal((d, k + 32)))
@@ -143,8 +146,8 @@ def test_precompute_tile_paths(g, dtype, shape):
     V64, C64 = Q[:, :k], Q[:, k:]
     W = torch.from_numpy(rng.standard_normal((d_out, d)) * 0.03).to(dtype)
     V = torch.from_numpy(V64).to(dtype)
-    say(f"case: precompute tiles {shape} {dtype}")
-    L = g.create_layer(W.cuda(), V.cuda())
+    say(f"case: precompute tiles {shape} {dtype} split={split}")
+    L = g.create_layer(W.cuda(), V.cuda(), split=split)
     torch.cuda.synchronize()
     M = to_np(g.layer_image(L))
     ref = orc.precompute_image(W, V)

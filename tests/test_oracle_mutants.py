@@ -11,7 +11,8 @@ from oracle import gsi_oracle as orc
 from tests import oracle_pins
 
 _real = {name: getattr(orc, name) for name in ("residual", "residual_norms", "gate", "project",
-                                              "precompute_image", "forward", "spectral_norm")}
+                                              "precompute_image", "forward", "spectral_norm",
+                                              "static_projection", "dense")}
 
 
 def m_residual_sign(V, X, G=None):
@@ -84,7 +85,33 @@ def m_spectral_squared(W, **kw):
     return _real["spectral_norm"](W, **kw) ** 2
 
 
+def m_static_is_dense(W, V, X, M=None):
+    out = _real["static_projection"](W, V, X, M=M)
+    out["y"] = _real["dense"](W, X)
+    return out
+
+
+def m_static_drops_column(W, V, X, M=None):
+    Vf = orc.as_f64(V).copy()
+    Vf[:, -1] = 0.0
+    return _real["static_projection"](W, Vf, X, M=M)
+
+
+def m_dense_drops_column(W, X):
+    Xf = np.atleast_2d(orc.as_f64(X)).copy()
+    Xf[:, -1] = 0.0
+    return _real["dense"](W, Xf)
+
+
+def m_dense_rounded(W, X):
+    return _real["dense"](W, X) * (1.0 + 1e-9)
+
+
 MUTANTS = {
+    "static_is_dense": ("static_projection", m_static_is_dense),
+    "static_drops_column": ("static_projection", m_static_drops_column),
+    "dense_drops_column": ("dense", m_dense_drops_column),
+    "dense_scaled": ("dense", m_dense_rounded),
     "residual_sign": ("residual", m_residual_sign),
     "pythagorean_shortcut": ("residual_norms", m_pythagorean),
     "gate_ties_fast": ("gate", m_gate_ties_fast),
