@@ -186,10 +186,9 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
     delete L;
     return rc;
   }
-  // V^T (k x d), then M = W V = W (V^T)^T, then V^T V - I   [GSI §2.1], then the decode plan
-  if ((rc = launch_transpose(dtype, V, Vt, d, k, s)) != GSI_OK ||
-      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK ||
-      (rc = launch_plan(L->desc, L->P, (int)dtype_size(dtype), L->plan, s)) != GSI_OK) {
+  // V^T (k x d) and the decode plan, then M = W V = W (V^T)^T and V^T V - I   [GSI §2.1]
+  if ((rc = launch_transpose(dtype, V, Vt, d, k, L->desc, L->P, L->plan, s)) != GSI_OK ||
+      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK) {
     delete L;
     return rc;
   }
@@ -325,6 +324,13 @@ int gsi_stack_create_modes(gsi_stack** out, gsi_layer* const* sites, const int* 
   S->layers = layers;
   S->h_table = table;
   S->d_plan = nullptr;
+  // plan rows hold element offsets into stacked rows as 32-bit integers
+  if (xo >= (1ll << 31) || yo >= (1ll << 31)) {
+    std::free(table);
+    std::free(layers);
+    delete S;
+    return GSI_ERR_SHAPE;
+  }
   S->xr = decode_window(S->dtype, table, n_sites);
   S->P = decode_grid(S->dtype, S->xr);
   auto fail = [&](int code) {

@@ -243,7 +243,7 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
   hipStream_t s = (hipStream_t)stream;
   const CalWs w = cal_ws_carve(ws, n, d, k);
   // A^T [d, n] once per call: the second product contracts over the tokens
-  if ((rc = launch_transpose(GSI_F32, A, w.At, n, d, s)) != GSI_OK) return rc;
+  if ((rc = launch_transpose(GSI_F32, A, w.At, n, d, LayerDesc{}, 0, nullptr, s)) != GSI_OK) return rc;
   const float eta2 = 0.5f;  // eta = 1/sqrt(2)
   for (int it = 0; it < n_iter; ++it) {
     const float* Qin = it == 0 ? Q0t : Qt;

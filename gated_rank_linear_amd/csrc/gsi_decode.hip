@@ -10,8 +10,9 @@
 //  * Work split per site (gsi_plan.h): block b owns the g columns j = b, b + P, ... (rows of V^T:
 //    each g_j is one complete d-long dot product inside one block) and a contiguous slice of
 //    output rows of M / W. The split of every (site, block) is precomputed at creation as a
-//    128-byte plan row; the plan rows of the next two steps are staged in LDS ahead of use, so a
-//    step starts without waiting for descriptor loads or index arithmetic.
+//    128-byte plan row; every wave loads the row it needs a step ahead into its own registers and
+//    moves it to scalar registers while it waits anyway, so a step starts without waiting for
+//    descriptor loads or index arithmetic.
 //  * Two all-gather exchanges per site: (E1) every block needs all of g for its rows of M g;
 //    (E2) the gate needs the global sum of per-block pieces of g^T (V^T V - I) g. A block posts
 //    its E2 word only after its rows of y are stored, so E2 is also the completion of the site:
@@ -154,22 +155,20 @@ __device__ __forceinline__ float group_reduce(float v, int width) {
 // Whole-wave sum, valid in lane 63.
 __device__ __forceinline__ float wave_reduce(float v) { return group_reduce(v, 64); }
 
-// A plan row staged in LDS, read into scalar registers (every lane reads the same words).
-__device__ __forceinline__ PlanRow read_plan(const PlanRow* slot) {
-  PlanRow p;
-  const unsigned* src = reinterpret_cast<const unsigned*>(slot);
-  unsigned* dst = reinterpret_cast<unsigned*>(&p);
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(PlanRow) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
-  return p;
+// Plan rows travel through each wave's own registers: lane l (l < 5) loads 16-byte chunk l of the
+// row (the other lanes load the last chunk again, unused), and plan_unpack moves the 20 words to
+// scalar registers. A wave only ever reads rows it loaded itself, so no wave waits on another's.
+__device__ __forceinline__ u32x4 plan_load(const PlanRow* table, int s, int b, int P, int lane) {
+  return ldg((g4p)(table + (long long)s * P + b), lane < kPlanChunks ? lane : kPlanChunks - 1);
 }
-
-// Copy of plan row (site s, block b) into an LDS slot by lanes 0..7 of one wave.
-__device__ __forceinline__ void fill_plan(const PlanRow* table, int s, int b, int P, int lane, PlanRow* slot) {
-  if (lane < kPlanChunks) {
-    const char* src = reinterpret_cast<const char*>(table + (long long)s * P + b) + lane * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)slot, 16, 0, 0);
-  }
+__device__ __forceinline__ PlanRow plan_unpack(const u32x4& v) {
+  PlanRow p;
+  unsigned* dst = reinterpret_cast<unsigned*>(&p);
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(PlanRow) / 4); ++i)
+    dst[i] = (unsigned)__builtin_amdgcn_readlane((int)w[i & 3], i >> 2);
+  return p;
 }
 
 // Copy instructions of a site's region fill; instruction i (chunks 64 i .. 64 i + 63 of the
@@ -274,7 +273,6 @@ struct Shared {
   float* gsh;    // [kMaxK] gathered g
   float* ypart;  // [kYPart] this block's rows of y (float32) before rounding
   float (*red)[kMaxJ + 2];  // [4][kMaxJ + 2] per-wave partial sums of phase A
-  PlanRow* plans;  // [3] plan rows of the current, next and next-but-one steps
   float* s_nx2;
   float* s_gg;
   int* s_gate;
@@ -353,24 +351,25 @@ __device__ __forceinline__ void fast_rows(const PlanRow& g, const lu32x4* cur, c
 // The block's rows of y = W x straight from HBM: one wave per row, each lane keeping kSlowBatch
 // chunk pairs in flight.
 template <typename T>
-__device__ __forceinline__ void dense_rows(const PlanRow& g, const T* x, T* yrow, int wave, int lane) {
+__device__ __forceinline__ void dense_rows(unsigned long long w, int nrows, int cprd, const T* x, T* yrow, int wave,
+                                           int lane) {
   const g4p x4 = (g4p)x;
-  for (int r = wave; r < g.nrows; r += kDataThreads / 64) {
-    const g4p wr = gptr(g.w) + (long long)r * g.cprd;
+  for (int r = wave; r < nrows; r += kDataThreads / 64) {
+    const g4p wr = gptr(w) + (long long)r * cprd;
     float a = 0.f;
-    for (int c0 = 0; c0 < g.cprd; c0 += kSlowBatch * 64) {
+    for (int c0 = 0; c0 < cprd; c0 += kSlowBatch * 64) {
       u32x4 wv[kSlowBatch], xv[kSlowBatch];
 #pragma unroll
       for (int i = 0; i < kSlowBatch; ++i) {
         const int c = c0 + lane + 64 * i;
-        const int cc = c < g.cprd ? c : 0;
+        const int cc = c < cprd ? c : 0;
         wv[i] = wr[cc];
         xv[i] = x4[cc];
       }
 #pragma unroll
       for (int i = 0; i < kSlowBatch; ++i) {
         const float v = dot16<T>(wv[i], xv[i], 0.f);
-        a += (c0 + lane + 64 * i < g.cprd) ? v : 0.f;
+        a += (c0 + lane + 64 * i < cprd) ? v : 0.f;
       }
     }
     a = wave_reduce(a);
@@ -386,42 +385,51 @@ struct StepCtx {
   const u32x4* dummy;
 };
 
-// One (token, site) step. `cur` holds this step's slices (filled during the previous step);
-// `nxt` receives the next step's. Plan slots: `sc` this step, `sn` the next, `sf` receives the
-// one after. Returns false when the launch was aborted.
+// One (token, site) step. `cur` holds this step's slices (filled during the previous step); `nxt`
+// receives the next step's. Plan rows arrive in scalar registers: g is this step's (every wave),
+// gn the next step's (data waves only). Each wave loads the row it will need one step later at the
+// start of this step (data waves: the row after next; the sync wave: the next) and unpacks it where
+// it would otherwise wait: the data waves once their own loads have completed, the sync wave right
+// after posting its E2 word. Returns false when the launch was aborted.
 template <typename T, int XR>
 __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& c, const Cursor& cq, const lu32x4* cur,
-                                          lu32x4* nxt, u32x4 (&xw)[XR], const Shared& sh, int sc, int sn, int sf) {
+                                          lu32x4* nxt, u32x4 (&xw)[XR], const Shared& sh, PlanRow& g, PlanRow& gn) {
   const int tid = c.tid, b = c.b, P = c.P;
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
-  const PlanRow g = read_plan(sh.plans + sc);
-  const PlanRow gn = read_plan(sh.plans + sn);
   const bool has_next = c.q + 1 < c.Q, has_next2 = c.q + 2 < c.Q;
+  // what the step still needs after g and gn are replaced by the next step's rows
+  const int mode = g.mode, nrows = g.nrows, cprd = g.cprd;
+  const unsigned long long w_rows = g.w;
   Cursor cn = cq;
   cn.advance(p.n_sites, p.t_step);
   Cursor c2 = cn;
   c2.advance(p.n_sites, p.t_step);
   const long long t = cq.token(p.t_step);
+  // the plan row this wave needs one step from now (loads of a row in bounds even when unused)
+  const u32x4 plan_ahead = is_sync ? plan_load(p.plan, has_next ? cn.s : cq.s, b, P, lane)
+                                   : plan_load(p.plan, has_next2 ? c2.s : cq.s, b, P, lane);
   const unsigned tag_g = step_tag(c.base, c.q, 1), tag_p = step_tag(c.base, c.q, 2), tag_f = step_tag(c.base, c.q, 3);
   const T* x = reinterpret_cast<const T*>(p.X) + t * p.x_ld + g.x_off;
   T* yrow = reinterpret_cast<T*>(p.Y) + t * p.y_ld + g.y_off;
   const long long vt_stride = (long long)P * g.cprd;  // chunks between owned V^T rows
 
-  if (g.mode == kSiteDense) {
+  if (mode == kSiteDense) {
     // ---------------- dense site: y = W x for the owned rows, then the completion exchange -------------
     if (!is_sync) {
-      dense_rows<T>(g, x, yrow, wave, lane);
+      dense_rows<T>(w_rows, nrows, cprd, x, yrow, wave, lane);
       if (has_next) {
         fill_region(gn, P, wave, lane, nxt, c.dummy);
-        if (wave == 0 && has_next2) fill_plan(p.plan, c2.s, b, P, lane, sh.plans + sf);
         load_x<XR>(reinterpret_cast<const T*>(p.X) + cn.token(p.t_step) * p.x_ld + gn.x_off, gn.cprd, tid, xw);
       }
       wait_vmcnt<0>();  // rows of y stored; next region, plan row and input row complete
+      g = gn;
+      gn = plan_unpack(plan_ahead);
     }
     __syncthreads();
     if (is_sync) {
       if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, 0.f));
+      g = plan_unpack(plan_ahead);
       float pv[kMaxBlocks / 64];
       const bool ok = gather(p, c.base, p.box_p + (long long)c.rep * kMaxBlocks, P, tag_p, lane, pv);
       if (!ok && lane == 0) *sh.s_abort = 1;
@@ -506,10 +514,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   }
   lds_barrier();  // the g words are issued ahead of the copy below
   if (!is_sync) {
-    if (has_next) {
-      fill_region(gn, P, wave, lane, nxt, c.dummy);
-      if (wave == 0 && has_next2) fill_plan(p.plan, c2.s, b, P, lane, sh.plans + sf);
-    }
+    if (has_next) fill_region(gn, P, wave, lane, nxt, c.dummy);
   } else {
     float gv[kMaxK / 64];
     const bool ok = gather(p, c.base, p.box_g + (long long)c.rep * kMaxK, g.k, tag_g, lane, gv);
@@ -531,7 +536,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   float pb = 0.f;
   if (!is_sync) {
     fast_rows<T>(g, cur, sh, wave, lane);
-  } else if (g.mode == kSiteGated) {
+  } else if (mode == kSiteGated) {
     // p_b = sum_j g_j ((V^T V - I) g)_j over the owned columns; chunk e covers owned row
     // e / cpk4, columns 4 (e mod cpk4) .. + 3
     const int nd = g.nJ * g.cpk4;
@@ -551,7 +556,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   lds_barrier();
   // ---- the sync wave stores this block's rows of y, then posts its E2 word (site done) ----
   if (is_sync) {
-    for (int r = lane; r < g.nrows; r += 64) yrow[r] = from_f32<T>(sh.ypart[r]);
+    for (int r = lane; r < nrows; r += 64) yrow[r] = from_f32<T>(sh.ypart[r]);
     if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, pb));
   }
   lds_barrier();  // the y rows and the E2 word are issued ahead of the loads below
@@ -559,7 +564,10 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     // the next input row streams in while E2 resolves
     if (has_next) load_x<XR>(reinterpret_cast<const T*>(p.X) + cn.token(p.t_step) * p.x_ld + gn.x_off, gn.cprd, tid, xw);
     wait_vmcnt<0>();  // the next region, plan row and input row are complete before the barrier below
+    g = gn;
+    gn = plan_unpack(plan_ahead);
   } else {
+    g = plan_unpack(plan_ahead);  // overlaps the wait for the other blocks' E2 words
     // ---------------- E2: all-gather the pieces, resolve the gate ----------------
     float pv[kMaxBlocks / 64];
     const bool ok = gather(p, c.base, p.box_p + (long long)c.rep * kMaxBlocks, P, tag_p, lane, pv);
@@ -571,7 +579,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     if (lane == 63) {
       int slow = 0;
       float r = __builtin_nanf("");
-      if (g.mode == kSiteGated) {
+      if (mode == kSiteGated) {
         const float nx2 = *sh.s_nx2;
         const float nr2 = (nx2 - *sh.s_gg) + ps;
         const float thr = p.eps * p.eps;
@@ -586,15 +594,18 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
         if (p.rho) p.rho[o] = r;
       }
     }
-    wait_vmcnt<0>();  // this block's fast-path rows of y are written before a slow path rewrites them
   }
   lds_barrier();
   if (*sh.s_abort) return false;
 
   // ---------------- slow path: y = W x for the owned rows, then E3 ----------------
   if (*sh.s_gate) {
+    // the sync wave's fast-path stores to these rows of y complete before the W x rows replace
+    // them (only here: on the fast path nothing waits for stores)
+    if (is_sync) wait_vmcnt<0>();
+    __syncthreads();
     if (!is_sync) {
-      dense_rows<T>(g, x, yrow, wave, lane);
+      dense_rows<T>(w_rows, nrows, cprd, x, yrow, wave, lane);
       wait_vmcnt<0>();
     }
     __syncthreads();
@@ -616,7 +627,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   __shared__ float gsh[kMaxK];
   __shared__ float ypart[kYPart];
   __shared__ float red[kDecodeThreads / 64][kMaxJ + 2];
-  __shared__ PlanRow plans[3];
   __shared__ float s_nx2, s_gg;
   __shared__ int s_gate, s_abort;
   __shared__ unsigned long long s_base;
@@ -625,7 +635,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const int b = blockIdx.x, P = gridDim.x;
   const bool is_sync = tid >= kDataThreads;
   const int lane = tid & 63, wave = tid >> 6;
-  const Shared sh{gsh, ypart, red, plans, &s_nx2, &s_gg, &s_gate, &s_abort};
+  const Shared sh{gsh, ypart, red, &s_nx2, &s_gg, &s_gate, &s_abort};
   lu32x4* const r0 = (lu32x4*)region0;
   lu32x4* const r1 = (lu32x4*)region1;
   const long long Q = (long long)p.n_steps * p.t_step * p.n_sites;
@@ -648,39 +658,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const StepCtx c0{0, Q, base, b, P, tid, xcc_id() % kReplicas, reinterpret_cast<const u32x4*>(p.hdr)};
 
   u32x4 xw[XR];
-  if (Q > 0 && !is_sync) {  // plan rows of steps 0 and 1, step 0's region and input row
-    if (wave == 0) fill_plan(p.plan, 0, b, P, lane, plans + 0);
-    if (wave == 1 && Q > 1) fill_plan(p.plan, p.t_step > 1 ? 0 : (p.n_sites > 1 ? 1 : 0), b, P, lane, plans + 1);
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
+  // plan rows of steps 0 and 1 (every wave its own copy), step 0's region and input row
+  const int s1 = p.t_step > 1 ? 0 : (p.n_sites > 1 ? 1 : 0);
+  PlanRow g = plan_unpack(plan_load(p.plan, 0, b, P, lane));
+  PlanRow gn = plan_unpack(plan_load(p.plan, s1, b, P, lane));
   if (Q > 0 && !is_sync) {
-    const PlanRow g0 = read_plan(plans + 0);
-    load_x<XR>(reinterpret_cast<const T*>(p.X) + g0.x_off, g0.cprd, tid, xw);
-    fill_region(g0, P, wave, lane, r0, c0.dummy);
+    load_x<XR>(reinterpret_cast<const T*>(p.X) + g.x_off, g.cprd, tid, xw);
+    fill_region(g, P, wave, lane, r0, c0.dummy);
     wait_vmcnt<0>();
   }
   __syncthreads();
 
   Cursor cq{0, 0, 0};
   StepCtx c = c0;
-  int sc = 0, sn = 1, sf = 2;  // plan slots: this step, the next, the one after
-  auto rotate = [&]() {
-    const int tmp = sc;
-    sc = sn;
-    sn = sf;
-    sf = tmp;
-  };
   for (long long q = 0; q < Q; q += 2) {
     c.q = q;
-    if (!site_step<T, XR>(p, c, cq, r0, r1, xw, sh, sc, sn, sf)) break;
+    if (!site_step<T, XR>(p, c, cq, r0, r1, xw, sh, g, gn)) break;
     cq.advance(p.n_sites, p.t_step);
-    rotate();
     if (q + 1 >= Q) break;
     c.q = q + 1;
-    if (!site_step<T, XR>(p, c, cq, r1, r0, xw, sh, sc, sn, sf)) break;
+    if (!site_step<T, XR>(p, c, cq, r1, r0, xw, sh, g, gn)) break;
     cq.advance(p.n_sites, p.t_step);
-    rotate();
   }
   if (!is_sync) wait_vmcnt<0>();  // no copy into LDS outlives the block
   // advance the epoch for the next launch (also after an abort, so its mark goes stale)

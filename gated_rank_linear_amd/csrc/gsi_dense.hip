@@ -399,6 +399,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Precompute reduction: rows [0, m_img) are M, summed over sw chunks of the partials at pw (chunk
+// stride cw floats) and rounded to TC; rows [m_img, m_img + n) are V^T V, summed over sd chunks of
+// the partials at pd (chunk stride cd), stored to Dl as float32 with I subtracted. Four columns
+// per thread (n a multiple of 4), chunks added in order.
+template <typename TC>
+__global__ __launch_bounds__(256) void precompute_reduce_kernel(const float* __restrict__ pw, int sw, long long cw,
+                                                                const float* __restrict__ pd, int sd, long long cd,
+                                                                int m_img, int n, void* __restrict__ M,
+                                                                float* __restrict__ Dl) {
+  const int m = m_img + n;
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  if (q >= (long long)m * (n / 4)) return;
+  const int mm = (int)(q / (n / 4)), n4 = (int)(q % (n / 4)) * 4;
+  const bool img = mm < m_img;
+  const int r = img ? mm : mm - m_img;
+  const float4* pp = reinterpret_cast<const float4*>((img ? pw : pd) + (long long)r * n + n4);
+  const long long stride = (img ? cw : cd) / 4;
+  const int splits = img ? sw : sd;
+  float4 v = pp[0];
+  for (int z = 1; z < splits; ++z) {
+    const float4 w = pp[z * stride];
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  float vv[4] = {v.x, v.y, v.z, v.w};
+  if (img) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_from_f32<TC>(M, (long long)r * n + n4 + e, vv[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Dl[(long long)r * n + n4 + e] = vv[e] - (r == n4 + e ? 1.0f : 0.0f);
+  }
+}
+
 // The same sum for a dense m x n output read and written four columns at a time (n a multiple of
 // 4), with I subtracted on request (V^T V - I).
 template <typename TC>
@@ -556,7 +592,8 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
                                                            void* __restrict__ C, long long ldc,
                                                            const int* __restrict__ c_idx, int m, int n, int kdim,
                                                            const int* __restrict__ m_count, int sub_identity,
-                                                           int k_chunk, float* __restrict__ part) {
+                                                           int k_chunk, float* __restrict__ part,
+                                                           const void* __restrict__ A2, int m_split) {
   constexpr int RT = MT / 16, NA = 2 * RT, NB = NA + 32, CPW = (NB + 3) / 4;
   __shared__ mu32x4 st0[NB * 64], st1[NB * 64], st2[NB * 64];
   const int mv = m_count ? min(m, *m_count) : m;
@@ -566,6 +603,7 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
   // copy t of this wave fills operand block qd = (wave + 4 t) mod NB: qd < NA is A sub-step
   // qd / RT, row tile qd mod RT; qd >= NA is B sub-step (qd - NA) / 16, column tile
   // (qd - NA) mod 16. Lane l reads row + (l mod 16), elements 8 (l / 16) .. + 7 of the sub-step.
+  // Rows of A from m_split on come from A2 (row m_split of the product is row 0 of A2).
   const T* src[CPW];
   int dst[CPW];
 #pragma unroll
@@ -577,7 +615,9 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
     if (qd < NA) {
       const int mm = m0 + 16 * (qd % RT) + (lane & 15);
       const long long row = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) : 0;
-      src[t] = reinterpret_cast<const T*>(A) + row * lda + 32 * (qd / RT) + ko;
+      const T* abase = row < m_split ? reinterpret_cast<const T*>(A) + row * lda
+                                     : reinterpret_cast<const T*>(A2) + (row - m_split) * lda;
+      src[t] = abase + 32 * (qd / RT) + ko;
     } else {
       const int qb = qd - NA;
       const long long row = n0 + 16 * (qb & 15) + (lane & 15);
@@ -881,8 +921,10 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
     dim3 grid((m + mt - 1) / mt, n / 256);
     int k_chunk = kdim;
     float* no_part = nullptr;
+    const void* no_a2 = nullptr;
+    int m_split = m;
     void* args[] = {&A, &lda, &a_idx, &B, &ldb, &C, &ldc, &c_idx, &m, &n, &kdim, &m_count, &sub_identity,
-                    &k_chunk, &no_part};
+                    &k_chunk, &no_part, &no_a2, &m_split};
     hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
@@ -1113,77 +1155,103 @@ int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int
 // reduction, and V^T V - I on 16 x 16 tiles split over K the same way. Without a workspace (or
 // for shapes the tiles do not fit) the single-pass kernels run instead.
 // ---------------------------------------------------------------------------------------------
-int precompute_splits(int dtype, int d_out, int d, int k) {
-  if (dtype == GSI_F32 || k % 256 != 0 || d % 512 != 0 || d_out < 128) return 1;
-  const long long tiles = (long long)((d_out + 127) / 128) * (k / 256);
+// Split plan of the create-time products on 128 x 256 tiles (one block per CU, 256 CUs):
+//   fused:  [W; V^T] (V^T)^T = [M; V^T V] in one launch of sm K chunks;
+//   else:   W (V^T)^T in sm chunks, then V^T (V^T)^T in sd chunks, two launches.
+// The fused launch is taken when it keeps at least 3/4 of the blocks of the separate one within
+// one wave of blocks. sm = 0: the shape does not take the split path.
+struct PrecomputePlan {
+  int sm, sd;  // K chunks of the image product and (when sd > 0) of the separate V^T V product
+  bool fused;
+};
+
+static int best_splits(long long tiles, int d) {
+  // the most chunks (a power of two) that keep tiles x chunks within 256 blocks, with every chunk
+  // at least 64 columns and a whole number of 64-column steps
   int sp = 1;
-  // K chunks of at least 512 columns, each a whole number of 64-column steps
-  while (tiles * sp < 192 && sp < 16 && d % (2 * sp) == 0 && d / (2 * sp) >= 512 && (d / (2 * sp)) % 64 == 0) sp *= 2;
+  while (tiles * sp * 2 <= 256 && d % (2 * sp) == 0 && d / (2 * sp) >= 64 && (d / (2 * sp)) % 64 == 0) sp *= 2;
   return sp;
 }
 
-int delta_splits(int dtype, int d, int k) {
-  if (dtype == GSI_F32 || d % 32 != 0 || d < 1024 || k > 1024) return 1;
-  const long long tiles16 = (long long)((k + 15) / 16) * ((k + 15) / 16);
-  int splits = (int)std::min<long long>(kMaxSplit, std::max<long long>(1, (1024 + tiles16 - 1) / tiles16));
-  return std::min(splits, std::max(1, d / 512));
+static PrecomputePlan precompute_plan(int dtype, int d_out, int d, int k) {
+  PrecomputePlan pl{0, 0, false};
+  if (dtype == GSI_F32 || k % 256 != 0 || d % 512 != 0 || d_out < 128) return pl;
+  const long long cols = k / 256;
+  const long long tiles_w = (long long)((d_out + 127) / 128) * cols, tiles_f = (long long)((d_out + k + 127) / 128) * cols;
+  // the image product: K chunks of at least 512 columns
+  auto img_splits = [&](long long tiles) {
+    int sp = 1;
+    while (tiles * sp * 2 <= 256 && d % (2 * sp) == 0 && d / (2 * sp) >= 512 && (d / (2 * sp)) % 64 == 0) sp *= 2;
+    return sp;
+  };
+  const int sw = img_splits(tiles_w), sf = img_splits(tiles_f);
+  if (tiles_f * sf * 4 >= tiles_w * sw * 3 && tiles_f * sf <= 256) {
+    pl.sm = sf;
+    pl.fused = true;
+  } else {
+    pl.sm = sw;
+    pl.sd = best_splits((long long)(k / 128) * cols, d);
+  }
+  return pl;
 }
+
+int precompute_splits(int dtype, int d_out, int d, int k) { return precompute_plan(dtype, d_out, d, k).sm; }
 
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k) {
-  const int sm = precompute_splits(dtype, d_out, d, k), sd = delta_splits(dtype, d, k);
-  const long long em = sm > 1 ? (long long)sm * d_out * k : 0, ed = sd > 1 ? (long long)sd * k * k : 0;
-  const long long e = std::max(em, ed);
-  return e ? (size_t)(e * 4 + 255) / 256 * 256 : 0;
+  const PrecomputePlan pl = precompute_plan(dtype, d_out, d, k);
+  if (pl.sm == 0) return 0;
+  const size_t img = (size_t)pl.sm * (pl.fused ? d_out + k : d_out) * k * 4;
+  const size_t gram = pl.fused ? 0 : (size_t)pl.sd * k * k * 4;
+  return (img + 255) / 256 * 256 + (gram + 255) / 256 * 256;
 }
 
+static int launch_wide_partials(int dtype, const void* A, const void* A2, int m_split, const void* B, int m, int n,
+                                int kdim, int splits, float* part, hipStream_t s) {
+  void* fn = dtype == GSI_BF16 ? pick_wide<bf16_t>(128, GSI_F32) : pick_wide<f16_t>(128, GSI_F32);
+  if (!fn) return GSI_ERR_DTYPE;
+  int k_chunk = kdim / splits;
+  long long lda = kdim, ldb = kdim, ldc = n;
+  const int* no_idx = nullptr;
+  void* C = part;
+  int sub = 0;
+  dim3 grid((m + 127) / 128, n / 256, splits);
+  void* args[] = {&A, &lda, &no_idx, &B, &ldb, &C, &ldc, &no_idx, &m, &n, &kdim, &no_idx, &sub, &k_chunk, &part,
+                  &A2, &m_split};
+  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+// With the workspace: the split products above, then one reduction that rounds M and subtracts
+// I from V^T V. Without: the single-pass kernels.
 int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
                       void* ws, size_t ws_bytes, hipStream_t s) {
-  float* part = (float*)ws;
-  // M = W V = W (V^T)^T
-  const int sm = precompute_splits(dtype, d_out, d, k);
-  if (ws && sm > 1 && (size_t)sm * d_out * k * 4 <= ws_bytes) {
-    void* fn = dtype == GSI_BF16 ? pick_wide<bf16_t>(128, GSI_F32) : pick_wide<f16_t>(128, GSI_F32);
-    if (!fn) return GSI_ERR_DTYPE;
-    int k_chunk = d / sm;
-    const void* A = W;
-    long long lda = d;
-    const int* no_idx = nullptr;
-    const void* B = Vt;
-    long long ldb = d;
-    void* C = part;
-    long long ldc = k;
-    int m = d_out, n = k, kdim = d, sub = 0;
-    dim3 grid((d_out + 127) / 128, k / 256, sm);
-    void* args[] = {&A, &lda, &no_idx, &B, &ldb, &C, &ldc, &no_idx, &m, &n, &kdim, &no_idx, &sub, &k_chunk, &part};
-    if (hipLaunchKernel(fn, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
-    const long long groups = (long long)d_out * (k / 4);
-    if (dtype == GSI_BF16)
-      splitk_reduce4_kernel<bf16_t><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, sm, d_out, k, M, k, 0);
-    else
-      splitk_reduce4_kernel<f16_t><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, sm, d_out, k, M, k, 0);
-    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
-  } else {
-    const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
+  const PrecomputePlan pl = precompute_plan(dtype, d_out, d, k);
+  if (ws && pl.sm > 0 && precompute_ws_bytes(dtype, d_out, d, k) <= ws_bytes) {
+    float* pw = (float*)ws;
+    const int m_img = pl.fused ? d_out + k : d_out;
+    int rc = launch_wide_partials(dtype, W, Vt, d_out, Vt, m_img, k, d, pl.sm, pw, s);
     if (rc != GSI_OK) return rc;
-  }
-  // V^T V - I (float32)
-  const int sd = delta_splits(dtype, d, k);
-  if (ws && sd > 1 && (size_t)sd * k * k * 4 <= ws_bytes) {
-    void* kf = dtype == GSI_BF16 ? pick_kslice_c<bf16_t>(GSI_F32) : pick_kslice_c<f16_t>(GSI_F32);
-    int k_chunk = ((d + sd - 1) / sd + 31) / 32 * 32;
-    int splits = (d + k_chunk - 1) / k_chunk;
-    const void* A = Vt;
-    long long lda = d;
-    void* c_unused = part;
-    long long ldc_unused = k;
-    int m = k, n = k, kdim = d, sub = 0;
-    dim3 grid((k + 15) / 16, (k + 15) / 16, splits);
-    void* args[] = {&A, &lda, &A, &lda, &c_unused, &ldc_unused, &m, &n, &kdim, &sub, &k_chunk, &part};
-    if (hipLaunchKernel(kf, grid, dim3(256), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
-    const long long groups = (long long)k * (k / 4);
-    splitk_reduce4_kernel<float><<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(part, splits, k, k, Dl, k, 1);
+    const long long cw = (long long)m_img * k;
+    const float* pd = pw + (long long)d_out * k;  // fused: the V^T V rows follow the image rows
+    long long cd = cw;
+    int sd = pl.sm;
+    if (!pl.fused) {
+      float* pg = (float*)((char*)ws + ((size_t)pl.sm * d_out * k * 4 + 255) / 256 * 256);
+      rc = launch_wide_partials(dtype, Vt, Vt, k, Vt, k, k, d, pl.sd, pg, s);
+      if (rc != GSI_OK) return rc;
+      pd = pg;
+      cd = (long long)k * k;
+      sd = pl.sd;
+    }
+    const long long groups = (long long)(d_out + k) * (k / 4);
+    const unsigned nb = (unsigned)((groups + 255) / 256);
+    if (dtype == GSI_BF16)
+      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl);
+    else
+      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl);
     return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
+  const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
+  if (rc != GSI_OK) return rc;
   return launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s);
 }
 
@@ -1264,8 +1332,12 @@ int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long
 // dst[k, d] = transpose(src[d, k]), 32x32 tiles through LDS
 // ---------------------------------------------------------------------------------------------
 template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst, int d, int k) {
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst, int d, int k,
+                                                        LayerDesc desc, int P, PlanRow* __restrict__ plan) {
   __shared__ E t[32][33];
+  // block (0, 0) also writes the decode kernel's plan rows of the layer (one per grid block)
+  if (plan && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < P)
+    plan[threadIdx.x] = make_plan_row(desc, threadIdx.x, P, (int)sizeof(E));
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;  // src rows r (d), cols c (k)
   const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
   for (int i = ty; i < 32; i += 8) {
@@ -1279,12 +1351,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ sr
   }
 }
 
-int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s) {
+int launch_transpose(int dtype, const void* src, void* dst, int d, int k, const LayerDesc& desc, int P,
+                     PlanRow* plan, hipStream_t s) {
+  if (plan && (P < 1 || P > 256)) return GSI_ERR_DEVICE;
   dim3 grid((k + 31) / 32, (d + 31) / 32);
   if (dtype == GSI_F32)
-    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, d, k);
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, d, k, desc, P, plan);
   else
-    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, d, k);
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, d, k, desc, P, plan);
   return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 

@@ -152,8 +152,10 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k);
 int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
                       void* ws, size_t ws_bytes, hipStream_t s);
-// dst[k, d] = transpose(src[d, k])
-int launch_transpose(int dtype, const void* src, void* dst, int d, int k, hipStream_t s);
+// dst[k, d] = transpose(src[d, k]); with `plan` (P <= 256 entries), also the decode plan rows of
+// the layer described by desc
+int launch_transpose(int dtype, const void* src, void* dst, int d, int k, const LayerDesc& desc, int P,
+                     PlanRow* plan, hipStream_t s);
 // float32 C[m, n] = A B^T for a small output and a long K, K split over blocks (partial sums in
 // part, at least part_elems floats), reduced in chunk order
 int launch_gemm_nt_f32_splitk(const float* A, long long lda, const float* B, long long ldb, float* C, long long ldc,

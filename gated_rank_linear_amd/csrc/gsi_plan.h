@@ -37,7 +37,7 @@ struct LayerDesc {
 constexpr int kMaxJ = 4;             // g columns per block (k <= 512 with at least 128 blocks)
 constexpr int kRegionChunks = 4096;  // 16-byte chunks per LDS site region (64 KB)
 constexpr int kDataThreads = 256;    // 4 data waves per block
-constexpr int kPlanChunks = 8;       // 16-byte chunks of one plan row
+constexpr int kPlanChunks = 5;       // 16-byte chunks of one plan row
 
 // Block b's share of one site, for a grid of P blocks (P a power of two). Addresses are byte
 // addresses already offset to the block's first owned row.
@@ -48,29 +48,33 @@ constexpr int kPlanChunks = 8;       // 16-byte chunks of one plan row
 //    not fit are read from global memory when used: V^T rows from vj on, all of V^T V - I when it
 //    does not fit, M rows from m_rows on (m_n is all of the slice or a multiple of 256 chunks, so
 //    one pass of the 256 data threads never mixes LDS and global reads).
+// Counts are 16-bit (every one is at most 8192 for the shapes the library accepts) so that a row
+// is 80 bytes and two of them fit in a wave's scalar registers.
 struct alignas(16) PlanRow {
   unsigned long long vt;  // V^T row b; owned row jl is vt + jl * P * cprd * 16
   unsigned long long dl;  // row b of V^T V - I; owned row jl is dl + jl * P * cpk4 * 16
   unsigned long long m;   // M row r0
   unsigned long long w;   // W row r0
-  long long x_off;        // element offset of the site's input in a stacked input row
-  long long y_off;        // element offset of output row r0 in a stacked output row
-  int mode;               // SiteMode
-  int k;
-  int nJ;                 // g columns owned
-  int cprd;               // 16-byte chunks per V^T / W row (d / elements per chunk)
-  int nx;                 // input chunks per data thread (ceil(cprd / 256))
-  int cprk;               // 16-byte chunks per M row
-  int cpk4;               // 16-byte chunks per (V^T V - I) row (k / 4, float32)
-  int r0, nrows;          // output rows owned
-  int vj, v_n;            // V^T rows held in the region and their chunks (at offset 0)
-  int d_off, d_n;         // (V^T V - I) part: offset and chunks held (all or none)
-  int m_off, m_n;         // M part: offset and chunks held
-  int m_rows;             // rows of the M slice held in the region
-  int n_inst;             // 64-chunk copy instructions that fill the region
-  int pad[3];
+  int x_off;              // element offset of the site's input in a stacked input row
+  int y_off;              // element offset of output row r0 in a stacked output row
+  unsigned short mode;    // SiteMode
+  unsigned short k;
+  unsigned short nJ;      // g columns owned
+  unsigned short vj;      // V^T rows held in the region
+  unsigned short cprd;    // 16-byte chunks per V^T / W row (d / elements per chunk)
+  unsigned short nx;      // input chunks per data thread (ceil(cprd / 256))
+  unsigned short cprk;    // 16-byte chunks per M row
+  unsigned short cpk4;    // 16-byte chunks per (V^T V - I) row (k / 4, float32)
+  unsigned short nrows;   // output rows owned
+  unsigned short m_rows;  // rows of the M slice held in the region
+  unsigned short v_n;     // V^T chunks held (at offset 0)
+  unsigned short d_off, d_n;  // (V^T V - I) part: offset and chunks held (all or none)
+  unsigned short m_off, m_n;  // M part: offset and chunks held
+  unsigned short n_inst;      // 64-chunk copy instructions that fill the region
+  int r0;                 // first output row owned
+  int pad;
 };
-static_assert(sizeof(PlanRow) == kPlanChunks * 16, "a plan row is eight 16-byte chunks");
+static_assert(sizeof(PlanRow) == kPlanChunks * 16, "a plan row is five 16-byte chunks");
 
 GSI_HD int plan_align64(int v) { return (v + 63) & ~63; }
 GSI_HD int plan_ctz(unsigned v) { return __builtin_ctz(v); }  // v > 0
@@ -81,40 +85,46 @@ GSI_HD int plan_max(int a, int b) { return a > b ? a : b; }
 GSI_HD PlanRow make_plan_row(const LayerDesc& L, int b, int P, int es) {
   const int VW = 16 / es;  // elements per 16-byte chunk
   const int sh_P = plan_ctz((unsigned)P);
-  PlanRow p;
-  p.mode = L.mode;
-  p.k = L.k;
-  p.cprd = L.d / VW;
-  p.nx = (p.cprd + kDataThreads - 1) / kDataThreads;
-  p.cprk = L.k / VW;
-  p.cpk4 = L.k / 4;
+  const int cprd = L.d / VW, cprk = L.k / VW, cpk4 = L.k / 4;
   const int rpb = (L.d_out + P - 1) >> sh_P;
-  p.r0 = plan_min(L.d_out, b * rpb);
-  p.nrows = plan_min(L.d_out, p.r0 + rpb) - p.r0;
+  const int r0 = plan_min(L.d_out, b * rpb);
+  const int nrows = plan_min(L.d_out, r0 + rpb) - r0;
   const bool dense = L.mode == kSiteDense;
-  p.nJ = (!dense && b < L.k) ? ((L.k - 1 - b) >> sh_P) + 1 : 0;
-  p.vj = p.nJ;  // V^T rows that fit the region
-  while (p.vj > 0 && p.vj * p.cprd > kRegionChunks) --p.vj;
-  p.v_n = p.vj * p.cprd;
-  p.d_off = plan_align64(p.v_n);
-  const int nd = L.mode == kSiteGated ? p.nJ * p.cpk4 : 0;
-  p.d_n = p.d_off + nd <= kRegionChunks ? nd : 0;
-  p.m_off = plan_align64(p.d_off + p.d_n);
-  const int nm = dense ? 0 : p.nrows * p.cprk;
-  if (p.m_off + nm <= kRegionChunks) {
-    p.m_n = nm;
-  } else {
-    p.m_n = plan_max(0, (kRegionChunks - p.m_off) / kDataThreads * kDataThreads);
-  }
-  p.m_rows = p.cprk > 0 ? p.m_n / p.cprk : 0;
-  p.n_inst = (p.m_off + p.m_n + 63) / 64;
-  p.vt = (unsigned long long)(uintptr_t)L.Vt + (unsigned long long)b * p.cprd * 16;
-  p.dl = (unsigned long long)(uintptr_t)L.Dl + (unsigned long long)b * p.cpk4 * 16;
-  p.m = (unsigned long long)(uintptr_t)L.M + (unsigned long long)p.r0 * p.cprk * 16;
-  p.w = (unsigned long long)(uintptr_t)L.W + (unsigned long long)p.r0 * p.cprd * 16;
-  p.x_off = L.x_off;
-  p.y_off = L.y_off + p.r0;
-  p.pad[0] = p.pad[1] = p.pad[2] = 0;
+  const int nJ = (!dense && b < L.k) ? ((L.k - 1 - b) >> sh_P) + 1 : 0;
+  int vj = nJ;  // V^T rows that fit the region
+  while (vj > 0 && vj * cprd > kRegionChunks) --vj;
+  const int v_n = vj * cprd;
+  const int d_off = plan_align64(v_n);
+  const int nd = L.mode == kSiteGated ? nJ * cpk4 : 0;
+  const int d_n = d_off + nd <= kRegionChunks ? nd : 0;
+  const int m_off = plan_align64(d_off + d_n);
+  const int nm = dense ? 0 : nrows * cprk;
+  const int m_n = m_off + nm <= kRegionChunks ? nm : plan_max(0, (kRegionChunks - m_off) / kDataThreads * kDataThreads);
+  PlanRow p;
+  p.mode = (unsigned short)L.mode;
+  p.k = (unsigned short)L.k;
+  p.nJ = (unsigned short)nJ;
+  p.vj = (unsigned short)vj;
+  p.cprd = (unsigned short)cprd;
+  p.nx = (unsigned short)((cprd + kDataThreads - 1) / kDataThreads);
+  p.cprk = (unsigned short)cprk;
+  p.cpk4 = (unsigned short)cpk4;
+  p.nrows = (unsigned short)nrows;
+  p.m_rows = (unsigned short)(cprk > 0 ? m_n / cprk : 0);
+  p.v_n = (unsigned short)v_n;
+  p.d_off = (unsigned short)d_off;
+  p.d_n = (unsigned short)d_n;
+  p.m_off = (unsigned short)m_off;
+  p.m_n = (unsigned short)m_n;
+  p.n_inst = (unsigned short)((m_off + m_n + 63) / 64);
+  p.vt = (unsigned long long)(uintptr_t)L.Vt + (unsigned long long)b * cprd * 16;
+  p.dl = (unsigned long long)(uintptr_t)L.Dl + (unsigned long long)b * cpk4 * 16;
+  p.m = (unsigned long long)(uintptr_t)L.M + (unsigned long long)r0 * cprk * 16;
+  p.w = (unsigned long long)(uintptr_t)L.W + (unsigned long long)r0 * cprd * 16;
+  p.x_off = (int)L.x_off;
+  p.y_off = (int)(L.y_off + r0);
+  p.r0 = r0;
+  p.pad = 0;
   return p;
 }
 
