@@ -45,6 +45,7 @@ SIGNATURES = [
     ("gsi_stack_workspace_bytes", _sz, [_vp, _int]),
     ("gsi_stack_decode", _int, [_vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp, _sz, _vp]),
     ("gsi_workspace_status", _int, [_vp, _sz, ctypes.POINTER(_int), _vp]),
+    ("gsi_stack_decode_noalloc", _int, [_vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp]),
     ("gsi_calibrate_workspace_bytes", _sz, [_int, _int, _int]),
     ("gsi_calibrate", _int, [_int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp]),
 ]

@@ -176,6 +176,21 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
                      float* rho, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The batch-1 stack decode for callers that cannot allocate device memory or pass a workspace
+ * (code under stream capture, serving loops, harnesses that forbid allocation): gsi_stack_decode
+ * with T_step < 16, whose in-kernel exchange state (65,792 bytes) lives in a device array inside
+ * the library, one per GPU for the life of the process, instead of in a caller workspace.
+ * Arguments as for gsi_stack_decode without ws / ws_bytes. T_step >= 16 (the batched path, whose
+ * scratch grows with T_step and d_out) returns GSI_ERR_WORKSPACE; the other checks and errors are
+ * those of gsi_stack_decode. Calls share the array of their GPU: calls on one GPU must not overlap
+ * (their exchanges would race), and a wait timeout inside the kernel cannot be read back (the
+ * launch leaves early with incomplete outputs). The call allocates nothing: its first call on a
+ * device only looks up the array's address.
+ */
+int gsi_stack_decode_noalloc(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
+                             float* rho, void* stream);
+
+/*
  * Copy the workspace's status word to *host_status (host pointer) after synchronising `stream`:
  * GSI_OK, or GSI_ERR_TIMEOUT if an in-kernel wait of an earlier call ran past its bound.
  * Resets the word to GSI_OK.

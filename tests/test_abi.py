@@ -145,3 +145,18 @@ def test_eps_rejected_before_device(eps):
     assert lib.gsi_forward(fake, p, 1, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4
     assert lib.gsi_stack_decode(fake, p, 1, 1, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4
     assert lib.gsi_stack_decode(fake, p, 1, 64, ctypes.c_float(eps), p, p, None, p, 1 << 20, None) == -4
+
+
+def test_noalloc_rejects_before_device():
+    """The no-allocation decode validates like gsi_stack_decode and refuses the batched path's
+    sizes (T_step >= 16) before touching the stack handle or the device."""
+    p = vp(256)
+    fake = vp(4096)
+    f = ctypes.c_float
+    assert lib.gsi_stack_decode_noalloc(None, p, 1, 1, f(0.1), p, p, None, None) == -1
+    assert lib.gsi_stack_decode_noalloc(fake, p, -1, 1, f(0.1), p, p, None, None) == -2
+    assert lib.gsi_stack_decode_noalloc(fake, p, 1, 0, f(0.1), p, p, None, None) == -2
+    assert lib.gsi_stack_decode_noalloc(fake, p, 1, 1, f(float("nan")), p, p, None, None) == -4
+    assert lib.gsi_stack_decode_noalloc(fake, p, 1, 16, f(0.1), p, p, None, None) == -5
+    assert lib.gsi_stack_decode_noalloc(fake, p, 1, 64, f(0.1), p, p, None, None) == -5
+    assert lib.gsi_stack_decode_noalloc(fake, p, 0, 1, f(0.1), p, p, None, None) == 0
