@@ -56,6 +56,8 @@ def parse():
                     help="depth-cascade calibration of the bases on the GPT-J-shaped chain (prints its own line)")
     ap.add_argument("--cal-cold", type=int, default=8, help="subspace-iteration steps of a cold start")
     ap.add_argument("--cal-warm", type=int, default=2, help="steps of a cascade (warm) start")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (not the shared-input and T = 64 workloads)")
     return ap.parse_args()
 
 
@@ -86,8 +88,48 @@ def main():
         return
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
-        batched(args, cfg, g, torch, np)
-        return
+        out = batched(args, cfg, g, torch, np)
+    else:
+        out = batch1(args, cfg, g, torch, np)
+    if args.config == 3 and not args.no_extras:
+        out["extra_workloads"] = extra_workloads(args, g, torch, np)
+    print(json.dumps(out), flush=True)
+
+
+def extra_workloads(args, g, torch, np) -> dict:
+    """Two more workloads timed in the same run, each with its own bytes and roofline fraction:
+    the shared-input GPT-J-shaped stack (batch 1, q/k/v and fc_in as one site) and the T = 64
+    batched workload (k = 512, ~20% slow tokens per step)."""
+    import argparse
+    import gc
+
+    import synth
+    res = {}
+    a6 = argparse.Namespace(**vars(args))
+    a6.steps, a6.warmup, a6.reps, a6.no_cpu_baseline = 512, 32, 3, True
+    o6 = batch1(a6, synth.get(6), g, torch, np, light=True)
+    res["gptj_shared_input_batch1"] = {k: o6[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction")}
+    res["gptj_shared_input_batch1"]["workload"] = o6["config"]["workload"]
+    gc.collect()
+    torch.cuda.empty_cache()
+    a5 = argparse.Namespace(**vars(args))
+    a5.steps, a5.warmup, a5.reps = 40, 10, 1
+    o5 = batched(a5, synth.get(5), g, torch, np)
+    res["gptj_batched_t64"] = {k: o5[k] for k in ("value", "unit", "ms_per_step", "roofline", "slow_fraction",
+                                                    "sites_with_slow_tokens")}
+    res["gptj_batched_t64"]["workload"] = o5["config"]["workload"]
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
+def batch1(args, cfg, g, torch, np, light: bool = False) -> dict:
+    """The batch-1 stack decode of a workload with T_step = 1 (the headline when cfg is the
+    GPT-J-shaped stack). light: only the decode and its bytes (no CPU baseline, no rank-512
+    precompute, no stream-read kernel)."""
+    import synth
+    from synth.generate import config_inputs
+
     es = 2 if cfg.dtype != "f32" else 4
 
     # ---------------- inputs: generate on the host, upload, precompute M on the GPU ----------------
@@ -122,7 +164,7 @@ def main():
     log(f"[bench] uploaded weights and ran the M = W V precompute in {time.time() - t0:.1f}s "
         f"(precompute kernels {pre_ms:.1f} ms)")
     del ws_create
-    pre512 = precompute_rank512(g, torch, cfg, sites, keep) if cfg.dtype != "f32" and cfg.k == 256 else None
+    pre512 = precompute_rank512(g, torch, cfg, sites, keep) if cfg.dtype != "f32" and cfg.k == 256 and not light else None
     stack = g.gsi_stack_create(layers)
     n_sites = len(layers)
     X = torch.cat([si.X for si in sites], dim=1).contiguous().cuda()
@@ -157,8 +199,8 @@ def main():
         times.append((ev0.elapsed_time(ev1) / 1e3, t_wall))
     if g.gsi_workspace_status(ws) != 0:
         raise SystemExit("decode kernel reported a wait timeout")
-    stream_gbps = stream_read_gbps(torch)
-    if args.copy_calibration:
+    stream_gbps = stream_read_gbps(torch) if not light else None
+    if args.copy_calibration and not light:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b2 = torch.empty_like(a)
         b2.copy_(a)
@@ -213,17 +255,17 @@ def main():
         "cpu_baseline": cpu,
         "fast_fraction": round(fast_frac, 5),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
-        "stream_read_gbps": round(stream_gbps, 1),
-        "frac_of_stream_read": round(achieved / stream_gbps, 4),
+        "stream_read_gbps": round(stream_gbps, 1) if stream_gbps else None,
+        "frac_of_stream_read": round(achieved / stream_gbps, 4) if stream_gbps else None,
         "precompute": {"ms": round(pre_ms, 2), "tflop": round(pre_flop / 1e12, 4),
                        "tflops": round(pre_flop / (pre_ms / 1e3) / 1e12, 2) if pre_ms > 0 else None,
                        "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS},
         "precompute_k512": pre512,
     }
-    print(json.dumps(out), flush=True)
-    # release the stack's device table while the runtime is up, then let the process end
+    # release the stack's device table while the runtime is up
     stack.destroy()
     torch.cuda.synchronize()
+    return out
 
 
 def batched(args, cfg, g, torch, np):
@@ -309,7 +351,9 @@ def batched(args, cfg, g, torch, np):
         "sites_with_slow_tokens": round(float(any_slow.mean()), 4),
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    stack.destroy()
+    torch.cuda.synchronize()
+    return out
 
 
 def sweep(args, g, torch, np):

@@ -50,10 +50,28 @@ size_t aux_dl_off(int dtype, int d, int k) { return align256((size_t)k * d * dty
 size_t aux_plan_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
 size_t aux_bytes(int dtype, int d, int k) { return aux_plan_off(dtype, d, k) + sizeof(PlanRow) * kMaxBlocks; }
 
+// The decode kernel's grid, one answer per (device, dtype, input window class): the occupancy
+// query behind it costs tens of microseconds, once per layer creation otherwise.
+int cached_decode_grid(int dtype, int xr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices][3][2];  // 0 unknown, else grid + 1
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const int inst = xr <= 2 ? 0 : 1;
+  const bool cacheable = dev >= 0 && dev < kMaxDevices && dtype >= 0 && dtype < 3;
+  if (cacheable) {
+    const int v = known[dev][dtype][inst].load(std::memory_order_relaxed);
+    if (v != 0) return v - 1;
+  }
+  const int P = decode_grid(dtype, xr);
+  if (cacheable) known[dev][dtype][inst].store(P + 1, std::memory_order_relaxed);
+  return P;
+}
+
 // the decode kernel's input window and grid for one layer (before anything is enqueued)
 int layer_grid(gsi_layer* L) {
   L->xr = decode_window(L->dtype, &L->desc, 1);
-  L->P = decode_grid(L->dtype, L->xr);
+  L->P = cached_decode_grid(L->dtype, L->xr);
   return L->P == 0 ? GSI_ERR_DEVICE : GSI_OK;
 }
 
@@ -332,7 +350,7 @@ int gsi_stack_create_modes(gsi_stack** out, gsi_layer* const* sites, const int* 
     return GSI_ERR_SHAPE;
   }
   S->xr = decode_window(S->dtype, table, n_sites);
-  S->P = decode_grid(S->dtype, S->xr);
+  S->P = cached_decode_grid(S->dtype, S->xr);
   auto fail = [&](int code) {
     if (S->d_plan) (void)hipFree(S->d_plan);
     std::free(table);

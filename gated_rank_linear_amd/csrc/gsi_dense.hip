@@ -399,39 +399,83 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// Precompute reduction: rows [0, m_img) are M, summed over sw chunks of the partials at pw (chunk
-// stride cw floats) and rounded to TC; rows [m_img, m_img + n) are V^T V, summed over sd chunks of
-// the partials at pd (chunk stride cd), stored to Dl as float32 with I subtracted. Four columns
-// per thread (n a multiple of 4), chunks added in order.
+// Precompute reduction. Blocks [0, nb_img): rows of M, one thread per four columns, summing the
+// sw chunks at pw (chunk stride cw floats) into running sum z mod 8 (eight loads in flight), the
+// eight sums added in a fixed tree, rounded to TC. Blocks from nb_img on: rows of V^T V (n x n),
+// eight threads per four columns, thread u summing chunks u, u + 8, ... of the sd chunks at pd
+// (chunk stride cd), the eight threads' sums added in a fixed butterfly; stored to Dl as float32
+// with I subtracted. Results do not depend on timing.
 template <typename TC>
 __global__ __launch_bounds__(256) void precompute_reduce_kernel(const float* __restrict__ pw, int sw, long long cw,
                                                                 const float* __restrict__ pd, int sd, long long cd,
                                                                 int m_img, int n, void* __restrict__ M,
-                                                                float* __restrict__ Dl) {
-  const int m = m_img + n;
-  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
-  if (q >= (long long)m * (n / 4)) return;
-  const int mm = (int)(q / (n / 4)), n4 = (int)(q % (n / 4)) * 4;
-  const bool img = mm < m_img;
-  const int r = img ? mm : mm - m_img;
-  const float4* pp = reinterpret_cast<const float4*>((img ? pw : pd) + (long long)r * n + n4);
-  const long long stride = (img ? cw : cd) / 4;
-  const int splits = img ? sw : sd;
-  float4 v = pp[0];
-  for (int z = 1; z < splits; ++z) {
-    const float4 w = pp[z * stride];
-    v.x += w.x;
-    v.y += w.y;
-    v.z += w.z;
-    v.w += w.w;
+                                                                float* __restrict__ Dl, int nb_img) {
+  if ((int)blockIdx.x < nb_img) {
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+    if (q >= (long long)m_img * (n / 4)) return;
+    const int r = (int)(q / (n / 4)), n4 = (int)(q % (n / 4)) * 4;
+    const float4* pp = reinterpret_cast<const float4*>(pw + (long long)r * n + n4);
+    const long long stride = cw / 4;
+    float a[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u][0] = a[u][1] = a[u][2] = a[u][3] = 0.f;
+    int z = 0;
+    for (; z + 8 <= sw; z += 8) {
+      float4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = pp[(long long)(z + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a[u][0] += w[u].x;
+        a[u][1] += w[u].y;
+        a[u][2] += w[u].z;
+        a[u][3] += w[u].w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // the last sw mod 8 chunks (z is a multiple of 8 here)
+      if (z + u < sw) {
+        const float4 w = pp[(long long)(z + u) * stride];
+        a[u][0] += w.x;
+        a[u][1] += w.y;
+        a[u][2] += w.z;
+        a[u][3] += w.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      st_from_f32<TC>(M, (long long)r * n + n4 + e,
+                      ((a[0][e] + a[1][e]) + (a[2][e] + a[3][e])) + ((a[4][e] + a[5][e]) + (a[6][e] + a[7][e])));
+    return;
   }
-  float vv[4] = {v.x, v.y, v.z, v.w};
-  if (img) {
+  const long long q8 = (long long)(blockIdx.x - nb_img) * 256 + threadIdx.x;
+  const long long q = q8 >> 3;  // group of 4 columns of V^T V
+  const int u = (int)(q8 & 7);
+  const bool valid = q < (long long)n * (n / 4);
+  const int r = valid ? (int)(q / (n / 4)) : 0, n4 = valid ? (int)(q % (n / 4)) * 4 : 0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const float4* pp = reinterpret_cast<const float4*>(pd + (long long)r * n + n4);
+    const long long stride = cd / 4;
+    for (int z = u; z < sd; z += 8) {
+      const float4 w = pp[(long long)z * stride];
+      acc[0] += w.x;
+      acc[1] += w.y;
+      acc[2] += w.z;
+      acc[3] += w.w;
+    }
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st_from_f32<TC>(M, (long long)r * n + n4 + e, vv[e]);
-  } else {
+  for (int e = 0; e < 4; ++e) {  // the 8 lanes of a group are adjacent: butterfly over lane bits 0..2
+    float v = acc[e];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    acc[e] = v;
+  }
+  if (valid && u == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Dl[(long long)r * n + n4 + e] = vv[e] - (r == n4 + e ? 1.0f : 0.0f);
+    for (int e = 0; e < 4; ++e) Dl[(long long)r * n + n4 + e] = acc[e] - (r == n4 + e ? 1.0f : 0.0f);
   }
 }
 
@@ -1242,12 +1286,13 @@ int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* 
       cd = (long long)k * k;
       sd = pl.sd;
     }
-    const long long groups = (long long)(d_out + k) * (k / 4);
-    const unsigned nb = (unsigned)((groups + 255) / 256);
+    const int nb_img = (int)(((long long)d_out * (k / 4) + 255) / 256);
+    const int nb_gram = (int)(((long long)k * (k / 4) * 8 + 255) / 256);
+    const unsigned nb = (unsigned)(nb_img + nb_gram);
     if (dtype == GSI_BF16)
-      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl);
+      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, nb_img);
     else
-      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl);
+      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, nb_img);
     return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
   }
   const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
