@@ -152,6 +152,9 @@ def batch1(args, cfg, g, torch, np, light: bool = False) -> dict:
     wc = max(g.gsi_layer_create_workspace_bytes(g.dtype_code(W.dtype), si.d_out, si.d, cfg.k)
              for si, (W, _) in zip(sites, keep))
     ws_create = torch.empty(wc, dtype=torch.uint8, device="cuda") if wc else None
+    # one untimed pass first: the runtime loads each kernel's code on its first launch
+    for (W, V), (M, aux) in zip(keep, bufs):
+        g.gsi_layer_create(W, V, M, aux, ws_create).destroy()
     # every layer's precompute enqueued back to back, as a model load would run it
     torch.cuda.synchronize()
     ev0.record()

@@ -621,10 +621,14 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __res
 // Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): MT x 256
 // output tile per block of 4 waves (MT = 16, 32, 64 or 128 rows), so A (the weight, d_out x d)
 // streams from memory once per 256 columns. Wave w owns columns 64 w .. 64 w + 63. A 64-column
-// K step is NB operand blocks of 1 KB (A: 2 sub-steps x MT / 16 row tiles; B: 2 x 16 column
-// tiles), copied straight into LDS in MFMA operand order, three stages in flight. Every wave
-// issues the same number of copies per step: when NB is not a multiple of 4 the spare copies
-// repeat the first blocks (same data to the same place).
+// K step is NB operand blocks of 1 KB, each holding 8 rows x 128 bytes (A: MT / 8 blocks; B: 32),
+// copied straight into LDS, three stages in flight. Eight consecutive lanes of a copy read one
+// row's whole 128-byte segment (one cache line), with the 16-byte chunks permuted within the
+// row: row r of an operand sits at block r / 8, row slot (r mod 8) xor (block parity), chunk
+// slot c xor (r mod 8). With that swizzle the MFMA operand reads (lane l: row l mod 16 of a tile,
+// chunk 4 u + l / 16 of sub-step u) hit 16 distinct 16-byte bank groups in every 16 lanes.
+// Every wave issues the same number of copies per step: when NB is not a multiple of 4 the spare
+// copies repeat the first blocks (same data to the same place).
 // Split K: block z covers K columns [z k_chunk, (z + 1) k_chunk) (k_chunk a multiple of 64) and,
 // when `part` is given, stores its raw float32 sums to part[z][m][n] for a reduction in chunk
 // order; otherwise (k_chunk >= kdim) it writes C.
@@ -644,9 +648,9 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
   const int m0 = blockIdx.x * MT, n0 = blockIdx.y * 256;
   if (m0 >= mv) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // copy t of this wave fills operand block qd = (wave + 4 t) mod NB: qd < NA is A sub-step
-  // qd / RT, row tile qd mod RT; qd >= NA is B sub-step (qd - NA) / 16, column tile
-  // (qd - NA) mod 16. Lane l reads row + (l mod 16), elements 8 (l / 16) .. + 7 of the sub-step.
+  // copy t of this wave fills operand block qd = (wave + 4 t) mod NB (qd < NA: A rows
+  // 8 qd .. 8 qd + 7; else B rows 8 (qd - NA) ..). Lane l fills row slot l / 8, chunk slot l mod 8:
+  // row 8 q + ((l / 8) xor (q mod 2)) of the operand, 16-byte chunk (l mod 8) xor (row mod 8).
   // Rows of A from m_split on come from A2 (row m_split of the product is row 0 of A2).
   const T* src[CPW];
   int dst[CPW];
@@ -654,20 +658,27 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
   for (int t = 0; t < CPW; ++t) {
     const int q = wave + 4 * t;
     const int qd = q < NB ? q : q - NB;
-    const int ko = 8 * (lane >> 4);
+    const int qo = qd < NA ? qd : qd - NA;
+    const int r = 8 * qo + ((lane >> 3) ^ (qo & 1));
+    const int ko = 8 * ((lane & 7) ^ (r & 7));
     dst[t] = qd * 64;
     if (qd < NA) {
-      const int mm = m0 + 16 * (qd % RT) + (lane & 15);
+      const int mm = m0 + r;
       const long long row = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) : 0;
       const T* abase = row < m_split ? reinterpret_cast<const T*>(A) + row * lda
                                      : reinterpret_cast<const T*>(A2) + (row - m_split) * lda;
-      src[t] = abase + 32 * (qd / RT) + ko;
+      src[t] = abase + ko;
     } else {
-      const int qb = qd - NA;
-      const long long row = n0 + 16 * (qb & 15) + (lane & 15);
-      src[t] = reinterpret_cast<const T*>(B) + row * ldb + 32 * (qb >> 4) + ko;
+      const long long row = n0 + r;
+      src[t] = reinterpret_cast<const T*>(B) + row * ldb + ko;
     }
   }
+  // LDS place of this lane's operand fragment (row l mod 16 of a 16-row tile, chunk 4 u + l / 16)
+  // relative to the tile's first block: independent of the tile
+  int rd[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    rd[u] = ((lane >> 3) & 1) * 64 + 8 * ((lane & 7) ^ ((lane >> 3) & 1)) + ((4 * u + (lane >> 4)) ^ (lane & 7));
   mf32x4 acc[RT][4];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -682,9 +693,9 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
   do {                                                                                                 \
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
       mu32x4 af[RT], bf[4];                                                                            \
-      _Pragma("unroll") for (int i = 0; i < RT; ++i) af[i] = ((const dlu32x4*)(STAGE))[(u * RT + i) * 64 + lane]; \
+      _Pragma("unroll") for (int i = 0; i < RT; ++i) af[i] = ((const dlu32x4*)(STAGE))[2 * i * 64 + rd[u]]; \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-        bf[j] = ((const dlu32x4*)(STAGE))[(NA + u * 16 + wave * 4 + j) * 64 + lane];                  \
+        bf[j] = ((const dlu32x4*)(STAGE))[(NA + 2 * (wave * 4 + j)) * 64 + rd[u]];                    \
       _Pragma("unroll") for (int i = 0; i < RT; ++i)                                                   \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
     }                                                                                                  \
