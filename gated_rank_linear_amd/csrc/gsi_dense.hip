@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_lds_kernel(const void* __res
 
 // ---------------------------------------------------------------------------------------------
 // Matrix-core NT GEMM for a short, wide B (n a multiple of 256, the rank k of M = W V): MT x 256
-// output tile per block of 4 waves (MT = 16, 32, 64 or 128 rows), so A (the weight, d_out x d)
+// output tile per block of 4 waves (MT = 16, 32 or 64 rows), so A (the weight, d_out x d)
 // streams from memory once per 256 columns. Wave w owns columns 64 w .. 64 w + 63. A 64-column
 // K step is NB operand blocks of 1 KB, each holding 8 rows x 128 bytes (A: MT / 8 blocks; B: 32),
 // copied straight into LDS, three stages in flight. Eight consecutive lanes of a copy read one
@@ -689,16 +689,19 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
     _Pragma("unroll") for (int t = 0; t < CPW; ++t) __builtin_amdgcn_global_load_lds(                  \
         (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + dst[t]), 16, 0, 0);             \
   } while (0)
+// both sub-steps' operand fragments are read before the first product, so the LDS latency is
+// paid once per step
 #define GSI_WCOMPUTE(STAGE)                                                                            \
   do {                                                                                                 \
+    mu32x4 af[2][RT], bf[2][4];                                                                        \
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
-      mu32x4 af[RT], bf[4];                                                                            \
-      _Pragma("unroll") for (int i = 0; i < RT; ++i) af[i] = ((const dlu32x4*)(STAGE))[2 * i * 64 + rd[u]]; \
+      _Pragma("unroll") for (int i = 0; i < RT; ++i) af[u][i] = ((const dlu32x4*)(STAGE))[2 * i * 64 + rd[u]]; \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-        bf[j] = ((const dlu32x4*)(STAGE))[(NA + 2 * (wave * 4 + j)) * 64 + rd[u]];                    \
-      _Pragma("unroll") for (int i = 0; i < RT; ++i)                                                   \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
+        bf[u][j] = ((const dlu32x4*)(STAGE))[(NA + 2 * (wave * 4 + j)) * 64 + rd[u]];                 \
     }                                                                                                  \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                      \
+      _Pragma("unroll") for (int i = 0; i < RT; ++i)                                                   \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[u][i], bf[u][j], acc[i][j]); \
   } while (0)
 // every step issues exactly CPW copies per wave (past the last stage they re-read the last K step
 // into a stage nobody reads again), so waiting until at most CPW remain completes the current one
@@ -752,6 +755,105 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
         if (sub_identity && mm == nn) v -= 1.0f;
         st_from_f32<TC>(C, crow * ldc + nn, v);
       }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Split-K partial products of the create-time precompute ([W; V^T] (V^T)^T and V^T V): a
+// 128 x 256 output tile per block of 8 waves, two waves per SIMD; wave w owns rows
+// 64 (w / 4) .. + 63 and columns 64 (w mod 4) .. + 63 of the tile (64 accumulator registers per
+// lane). Copies, operand blocks, swizzle and stages as in gemm_nt_wide_kernel (48 blocks of 1 KB
+// per 64-column step, 6 copies per wave). Block z covers K columns [z k_chunk, (z + 1) k_chunk)
+// and stores its raw float32 sums to part[z][m][n]; rows from m_split on come from A2.
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(512) void gemm_nt_wide8_kernel(const void* __restrict__ A, const void* __restrict__ A2,
+                                                            int m_split, long long lda,
+                                                            const void* __restrict__ B, long long ldb, int m, int n,
+                                                            int kdim, int k_chunk, float* __restrict__ part) {
+  constexpr int NA = 16, NB = NA + 32, CPW = NB / 8;
+  __shared__ mu32x4 st0[NB * 64], st1[NB * 64], st2[NB * 64];
+  const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 256;
+  if (m0 >= m) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 2, wc = wave & 3;
+  const T* src[CPW];
+#pragma unroll
+  for (int t = 0; t < CPW; ++t) {
+    const int qd = wave + 8 * t;
+    const int qo = qd < NA ? qd : qd - NA;
+    const int r = 8 * qo + ((lane >> 3) ^ (qo & 1));
+    const int ko = 8 * ((lane & 7) ^ (r & 7));
+    if (qd < NA) {
+      const int mm = m0 + r;
+      const long long row = mm < m ? mm : 0;
+      const T* abase = row < m_split ? reinterpret_cast<const T*>(A) + row * lda
+                                     : reinterpret_cast<const T*>(A2) + (row - m_split) * lda;
+      src[t] = abase + ko;
+    } else {
+      src[t] = reinterpret_cast<const T*>(B) + (long long)(n0 + r) * ldb + ko;
+    }
+  }
+  int rd[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    rd[u] = ((lane >> 3) & 1) * 64 + 8 * ((lane & 7) ^ ((lane >> 3) & 1)) + ((4 * u + (lane >> 4)) ^ (lane & 7));
+  mf32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+#define GSI_W8ISSUE(STAGE, K0)                                                                         \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < CPW; ++t) __builtin_amdgcn_global_load_lds(                  \
+        (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + (wave + 8 * t) * 64), 16, 0, 0); \
+  } while (0)
+#define GSI_W8COMPUTE(STAGE)                                                                           \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
+      mu32x4 af[4], bf[4];                                                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+        af[i] = ((const dlu32x4*)(STAGE))[2 * (4 * wr + i) * 64 + rd[u]];                             \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
+        bf[j] = ((const dlu32x4*)(STAGE))[(NA + 2 * (4 * wc + j)) * 64 + rd[u]];                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
+    }                                                                                                  \
+  } while (0)
+// every step issues exactly CPW copies per wave (past the last stage they re-read the last K step
+// into a stage nobody reads again), so waiting until at most CPW remain completes the current one
+#define GSI_W8STEP(CUR, FUT, ST)                                                                        \
+  do {                                                                                                 \
+    dwait_vmcnt<CPW>();                                                                                \
+    dlds_barrier();                                                                                    \
+    GSI_W8ISSUE(FUT, kb + min((ST) + 2, nk - 1) * 64);                                                 \
+    GSI_W8COMPUTE(CUR);                                                                                \
+  } while (0)
+  const int kb = (int)blockIdx.z * k_chunk;
+  const int nk = (min(kdim, kb + k_chunk) - kb) / 64;  // >= 1: the launch checks the split
+  GSI_W8ISSUE(st0, kb);
+  GSI_W8ISSUE(st1, kb + min(1, nk - 1) * 64);
+  int s0 = 0;
+  for (; s0 + 3 <= nk; s0 += 3) {
+    GSI_W8STEP(st0, st2, s0);
+    GSI_W8STEP(st1, st0, s0 + 1);
+    GSI_W8STEP(st2, st1, s0 + 2);
+  }
+  if (s0 < nk) GSI_W8STEP(st0, st2, s0);
+  if (s0 + 1 < nk) GSI_W8STEP(st1, st0, s0 + 1);
+  dwait_vmcnt<0>();  // no copy may land in LDS after the block ends
+#undef GSI_W8STEP
+#undef GSI_W8COMPUTE
+#undef GSI_W8ISSUE
+  float* pz = part + (long long)blockIdx.z * m * n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
+      if (mm >= m) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pz[(long long)mm * n + n0 + wc * 64 + j * 16 + (lane & 15)] = acc[i][j][r];
     }
 }
 
@@ -824,8 +926,7 @@ static void* pick_wide_c(int c_type) {
 
 template <typename T>
 static void* pick_wide(int mt, int c_type) {
-  return mt == 128 ? pick_wide_c<T, 128>(c_type)
-         : mt == 64 ? pick_wide_c<T, 64>(c_type)
+  return mt == 64 ? pick_wide_c<T, 64>(c_type)
          : mt == 32 ? pick_wide_c<T, 32>(c_type)
                     : pick_wide_c<T, 16>(c_type);
 }
@@ -1262,17 +1363,14 @@ size_t precompute_ws_bytes(int dtype, int d_out, int d, int k) {
 
 static int launch_wide_partials(int dtype, const void* A, const void* A2, int m_split, const void* B, int m, int n,
                                 int kdim, int splits, float* part, hipStream_t s) {
-  void* fn = dtype == GSI_BF16 ? pick_wide<bf16_t>(128, GSI_F32) : pick_wide<f16_t>(128, GSI_F32);
-  if (!fn) return GSI_ERR_DTYPE;
+  void* fn = dtype == GSI_BF16 ? (void*)gemm_nt_wide8_kernel<bf16_t> : (void*)gemm_nt_wide8_kernel<f16_t>;
   int k_chunk = kdim / splits;
-  long long lda = kdim, ldb = kdim, ldc = n;
-  const int* no_idx = nullptr;
-  void* C = part;
-  int sub = 0;
+  // every block needs at least one whole 64-column step of K, and n whole 256-column tiles
+  if (splits < 1 || kdim % splits != 0 || k_chunk % 64 != 0 || k_chunk < 64 || n % 256 != 0) return GSI_ERR_SHAPE;
+  long long lda = kdim, ldb = kdim;
   dim3 grid((m + 127) / 128, n / 256, splits);
-  void* args[] = {&A, &lda, &no_idx, &B, &ldb, &C, &ldc, &no_idx, &m, &n, &kdim, &no_idx, &sub, &k_chunk, &part,
-                  &A2, &m_split};
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  void* args[] = {&A, &A2, &m_split, &lda, &B, &ldb, &m, &n, &kdim, &k_chunk, &part};
+  return hipLaunchKernel(fn, grid, dim3(512), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 // With the workspace: the split products above, then one reduction that rounds M and subtracts
