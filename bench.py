@@ -10,8 +10,9 @@ HBM; the timed region is `--steps` tokens after `--warmup` tokens. The roofline 
 the decode kernel against the 8 TB/s HBM peak using the algorithmic bytes of the realised gates
 (per token and site: V_k, plus M, plus W when the gate is slow), measured with HIP events on the
 kernel's stream. The CPU baseline times the fp64 oracle on a bounded sample (see --cpu-seconds).
-The line also carries the create-time precompute (M = W V_k and V_k^T V_k - I) at k = 256 and
-at k = 512 as matrix-core TFLOP/s, and the bandwidth of an in-repo streaming-read kernel.
+The line also carries the create-time precompute (M = W V_k, V_k^T V_k - I and, for 16-bit layers,
+(V_k (V_k^T V_k - I))^T) at k = 256 and at k = 512 as matrix-core TFLOP/s, and the bandwidth of an
+in-repo streaming-read kernel.
 
 `--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
 batched path and prints its own line (tokens/s and algorithmic GB/s).
@@ -147,7 +148,9 @@ def batch1(args, cfg, g, torch, np, light: bool = False) -> dict:
         bufs.append((torch.empty((si.d_out, cfg.k), dtype=W.dtype, device=W.device),
                      torch.empty(nb, dtype=torch.uint8, device=W.device)))
         keep.append((W, V))
-    pre_flop = sum(2.0 * si.d_out * si.d * cfg.k + 2.0 * cfg.k * cfg.k * si.d for si in sites)
+    # M = W V, V^T V, and for 16-bit layers (V (V^T V - I))^T (the batched gate's second projection)
+    pre_flop = sum(2.0 * si.d_out * si.d * cfg.k + 2.0 * cfg.k * cfg.k * si.d * (1 if cfg.dtype == "f32" else 2)
+                   for si in sites)
     # one create workspace for all layers (the creates run one after another on the stream)
     wc = max(g.gsi_layer_create_workspace_bytes(g.dtype_code(W.dtype), si.d_out, si.d, cfg.k)
              for si, (W, _) in zip(sites, keep))
@@ -595,7 +598,7 @@ def synth_weight(cfg, si):
 
 
 def precompute_rank512(g, torch, cfg, sites, keep):
-    """The create-time precompute (V^T, M = W V, V^T V - I) at rank k = 512 over the same weights:
+    """The create-time precompute (V^T, M = W V, V^T V - I, (V (V^T V - I))^T) at rank k = 512 over the same weights:
     the shapes of the T = 64 GPT-J-shaped workload, whose precompute is the one matrix-core bound
     step of the method. V is a seeded Gaussian matrix scaled by 1/sqrt(d) (orthonormality does not
     change the work). Only the kernels are timed."""
@@ -610,7 +613,7 @@ def precompute_rank512(g, torch, cfg, sites, keep):
         nb = g.gsi_layer_aux_bytes(g.dtype_code(W.dtype), si.d_out, si.d, k)
         bufs.append((torch.empty((si.d_out, k), dtype=W.dtype, device="cuda"),
                      torch.empty(nb, dtype=torch.uint8, device="cuda")))
-        flop += 2.0 * si.d_out * si.d * k + 2.0 * k * k * si.d
+        flop += 2.0 * si.d_out * si.d * k + 2.0 * k * k * si.d * 2
     wc = max(g.gsi_layer_create_workspace_bytes(g.dtype_code(W.dtype), si.d_out, si.d, k)
              for si, (W, _) in zip(sites, keep))
     ws_create = torch.empty(wc, dtype=torch.uint8, device="cuda") if wc else None

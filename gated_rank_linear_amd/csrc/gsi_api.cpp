@@ -1,6 +1,7 @@
 // C ABI of libgsi (declared in include/gsi.h): argument validation, handles, and enqueueing of
 // the HIP kernels. Every argument check runs before the first HIP call, so an invalid call
 // enqueues nothing and never touches the device.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
@@ -44,11 +45,16 @@ int check_eps(float eps) {
 int hip_rc(hipError_t e) { return e == hipSuccess ? GSI_OK : GSI_ERR_HIP; }
 
 // aux = [V^T (k x d, weight dtype)] [V^T V - I (k x k, float32)] [decode plan rows (kMaxBlocks)]
+//       [(V (V^T V - I))^T (k x d, weight dtype; 16-bit layers only)]
 // (a dense layer, k = 0, holds the plan rows only)
 size_t aux_vt_off(int, int, int) { return 0; }
 size_t aux_dl_off(int dtype, int d, int k) { return align256((size_t)k * d * dtype_size(dtype)); }
 size_t aux_plan_off(int dtype, int d, int k) { return aux_dl_off(dtype, d, k) + align256((size_t)k * k * 4); }
-size_t aux_bytes(int dtype, int d, int k) { return aux_plan_off(dtype, d, k) + sizeof(PlanRow) * kMaxBlocks; }
+size_t aux_vdt_off(int dtype, int d, int k) { return align256(aux_plan_off(dtype, d, k) + sizeof(PlanRow) * kMaxBlocks); }
+bool has_vdt(int dtype, int k) { return dtype != GSI_F32 && k > 0; }
+size_t aux_bytes(int dtype, int d, int k) {
+  return aux_vdt_off(dtype, d, k) + (has_vdt(dtype, k) ? align256((size_t)k * d * dtype_size(dtype)) : 0);
+}
 
 // The decode kernel's grid, one answer per (device, dtype, input window class): the occupancy
 // query behind it costs tens of microseconds, once per layer creation otherwise.
@@ -90,6 +96,19 @@ BatchedWs batched_part(void* ws, int k, int T, int d_out) {
 int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps, void* Y,
                 long long y_ld, uint8_t* gate, int gate_ld, float* rho, void* ws, int d_out_ws, hipStream_t s) {
   BatchedWs w = batched_part(ws, L.k, T, d_out_ws);
+  if (batched_split(dtype, L, std::min(T, 64)).zy > 0) {
+    // two launches per chunk of at most 64 tokens
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      const int n = std::min(64, T - t0);
+      const BatchedSplit sp = batched_split(dtype, L, n);
+      const int rc = launch_batched_site(dtype, L, sp, (const char*)X + (size_t)t0 * x_ld * dtype_size(dtype), x_ld,
+                                         n, eps, (char*)Y + (size_t)t0 * y_ld * dtype_size(dtype), y_ld,
+                                         gate + (size_t)t0 * gate_ld, gate_ld, rho ? rho + (size_t)t0 * gate_ld : nullptr,
+                                         w, s);
+      if (rc != GSI_OK) return rc;
+    }
+    return GSI_OK;
+  }
   int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
   if (rc != GSI_OK) return rc;
   if (L.mode == kSiteDense)  // every token: y = W x
@@ -194,6 +213,7 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
   L->desc.M = M;
   L->desc.Dl = Dl;
   L->desc.W = W;
+  L->desc.VDt = has_vdt(dtype, k) ? (char*)aux + aux_vdt_off(dtype, d, k) : nullptr;
   L->desc.d = d;
   L->desc.d_out = d_out;
   L->desc.k = k;
@@ -204,9 +224,11 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
     delete L;
     return rc;
   }
-  // V^T (k x d) and the decode plan, then M = W V = W (V^T)^T and V^T V - I   [GSI §2.1]
+  // V^T (k x d) and the decode plan, then M = W V = W (V^T)^T and V^T V - I   [GSI §2.1]; for the
+  // batched gate also (V (V^T V - I))^T = (V^T V - I) V^T, row j of it = sum_l D[j][l] V[:, l]
   if ((rc = launch_transpose(dtype, V, Vt, d, k, L->desc, L->P, L->plan, s)) != GSI_OK ||
-      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK) {
+      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK ||
+      (L->desc.VDt && (rc = launch_vdt(dtype, Dl, V, (void*)L->desc.VDt, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK)) {
     delete L;
     return rc;
   }
@@ -235,6 +257,7 @@ int gsi_layer_create_dense(gsi_layer** out, int dtype, int d_out, int d, const v
   L->desc.M = nullptr;
   L->desc.Dl = nullptr;
   L->desc.W = W;
+  L->desc.VDt = nullptr;
   L->desc.d = d;
   L->desc.d_out = d_out;
   L->desc.k = 0;

@@ -262,20 +262,48 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
 // n0 + 16 w, so every element of B is loaded once per block; each wave runs only the
 // NRT = ceil(mv / 16) row tiles that hold valid rows (mv is uniform, read once). The rows of A
 // are staged once per block through LDS. K is split over blockIdx.z; the raw float32 sums of a
-// chunk go to part[z][mm][nn] (rows mm < mv), added later in chunk order. Per sub-chunk of 256 K
-// columns the block copies its A rows (mv valid, the rest zero) into LDS, a float32 A split into
-// bf16 high and low parts (|a - hi - lo| <= 2^-18 |a|), stored in the A-operand order of
+// chunk go to part[z][mm][nn] (rows mm < mv; row o_idx[mm] when an output list is given), added
+// later in chunk order (with `coherent`, by device-scope stores another block can read without a
+// cache flush). Per sub-chunk of 256 K columns the block copies its A rows (mv valid, the
+// rest zero) into LDS, a float32 A split into high and low parts in B's 16-bit type (bf16:
+// |a - hi - lo| <= 2^-18 |a|; f16: 2^-22 |a| within its normal range), stored in the A-operand order of
 // v_mfma_f32_16x16x32_{bf16,f16} (row tile t, step s, lane l at ((t * 8 + s) * 64 + l)), so every
 // element is read from global memory (and split) once per block instead of once per wave and
 // every LDS read is one conflict-free 16-byte load; the eight steps of B of a sub-chunk are
-// loaded before its products, and the next sub-chunk's before this one's products.
-template <typename TA, typename TB, int NRT>
+// loaded before its products, and the next sub-chunk's A fragments (into registers) and B steps
+// before this one's products.
+// B steps of one 256-column sub-chunk for this lane (row nn of B, the lane's 8-element K groups);
+// steps outside [kb, ke) read column kb and are zeroed
+template <typename TB>
+__device__ __forceinline__ void skinny_load_b(const TB* __restrict__ B, long long ldb, int n, int kb, int ke, int k0,
+                                              mu32x4 (&bv)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nn = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const bool bok = nn < n;
+  const long long brow = bok ? (long long)nn * ldb : 0;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int kk = k0 + 32 * st + 8 * (lane >> 4);
+    const bool kin = kk < ke;  // K bounds are multiples of 8: a chunk is all in or all out
+    const mu32x4 w = reinterpret_cast<const mu32x4*>(B + brow + (kin ? kk : kb))[0];
+    bv[st] = (bok && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename TA, typename TB, int NRT, bool kPre = false, int kPreB = 0>
 __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, long long lda,
                                                     const int* __restrict__ a_idx, const TB* __restrict__ B,
                                                     long long ldb, int mv, int n, int kb, int ke,
                                                     float* __restrict__ part, mu32x4* __restrict__ lds_hi,
-                                                    mu32x4* __restrict__ lds_lo) {
-  constexpr bool kSplit = sizeof(TA) == 4;
+                                                    mu32x4* __restrict__ lds_lo, const int* __restrict__ o_idx,
+                                                    bool coherent, const TA* __restrict__ A_lo, mu32x4 (&pb0)[8],
+                                                    mu32x4 (&pb1)[8]) {
+  // kPreB (16-bit A only): the caller has already loaded the first kPreB sub-chunks' B steps into
+  // pb0 (and pb1) with skinny_load_b
+  // kF32: A is float32 and is split here; kPre: A arrives split, high parts at A and low parts at
+  // A_lo (16-bit, B's type); either way each step takes two products
+  constexpr bool kF32 = sizeof(TA) == 4;
+  constexpr bool kSplit = kF32 || kPre;
   constexpr int kSteps = 8;  // 32-column steps per sub-chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -285,42 +313,81 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
   mf32x4 acc[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t] = mf32x4{0.f, 0.f, 0.f, 0.f};
-  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) {
+  static_assert(kSteps == 8, "skinny_load_b loads eight steps");
+  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) { skinny_load_b(B, ldb, n, kb, ke, k0, bv); };
+  // A fragments of a sub-chunk: thread tid takes fragments f = tid + 256 i (i < 2 NRT); they are
+  // loaded into registers one sub-chunk ahead and written to LDS (split, for a float32 A) at the
+  // start of the sub-chunk that uses them
+  constexpr int NF = NRT * kSteps * 64 / 256;
+  constexpr int AW = kSplit ? 2 : 1;  // 16-byte loads per fragment
+  mu32x4 areg[NF][AW];
+  // each fragment's A row is the same in every sub-chunk: its offset is looked up once (the list
+  // may sit in LDS, and a load through a generic pointer would make every later wait drain all
+  // memory loads in flight)
+  // 16-bit A is read coalesced: element e = tid + 256 i of a sub-chunk is row e / 32, 16-byte
+  // chunk e mod 32 (32 consecutive threads read one row's 512 bytes) and is written to its place
+  // in the A-operand order; a float32 A is read per fragment
+  auto a_row_of = [&](int e) { return kF32 ? 16 * (e >> 9) + (e & 15) : e >> 5; };
+  auto a_lds_of = [&](int e) {
+    return kF32 ? e : (((e >> 9) * kSteps + ((e & 31) >> 2)) * 64 + ((e >> 5) & 15) + 16 * (e & 3));
+  };
+  long long arow[NF];
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int kk = k0 + 32 * st + 8 * kq;
-      const bool kin = kk < ke;  // K bounds are multiples of 8: a chunk is all in or all out
-      const mu32x4 w = reinterpret_cast<const mu32x4*>(B + brow + (kin ? kk : kb))[0];
-      bv[st] = (bok && kin) ? w : mu32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < NF; ++i) {
+    const int mm = a_row_of(tid + 256 * i);
+    arow[i] = mm < mv ? (long long)(a_idx ? a_idx[mm] : mm) * lda : -1;
+  }
+  // output rows of this lane's results, looked up before any store is issued (a lookup after a
+  // store would wait for that store to complete)
+  int orow[NRT][4];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 16 * t + 4 * kq + r;
+      orow[t][r] = mm < mv ? (o_idx ? o_idx[mm] : mm) : -1;
+    }
+  auto load_a_into = [&](int k0, mu32x4(&areg)[NF][AW]) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int f = tid + 256 * i;
+      const int l = f & 63, st = (f >> 6) & (kSteps - 1);
+      const int kk = kF32 ? k0 + 32 * st + 8 * (l >> 4) : k0 + 8 * (f & 31);
+      const bool in = arow[i] >= 0 && kk < ke;
+      const long long row = in ? arow[i] + kk : 0;
+      const mu32x4* pa = reinterpret_cast<const mu32x4*>(A + row);
+      if constexpr (kPre) {
+        const mu32x4 vh = pa[0];
+        const mu32x4 vl = reinterpret_cast<const mu32x4*>(A_lo + row)[0];
+        areg[i][0] = in ? vh : mu32x4{0u, 0u, 0u, 0u};
+        areg[i][1] = in ? vl : mu32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int h = 0; h < AW; ++h) {
+          const mu32x4 v = pa[h];
+          areg[i][h] = in ? v : mu32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
   };
-  mu32x4 bcur[kSteps], bnxt[kSteps];
-  load_b(kb, bcur);
-  for (int k0 = kb; k0 < ke; k0 += 32 * kSteps) {
-    __syncthreads();  // the previous sub-chunk's A fragments are no longer read
-    // stage A: NRT * 8 * 64 fragments of 8 elements
-    for (int f = tid; f < NRT * kSteps * 64; f += 256) {
-      const int l = f & 63, st = (f >> 6) & (kSteps - 1), t = f >> 9;
-      const int mm = 16 * t + (l & 15);
-      const int kk = k0 + 32 * st + 8 * (l >> 4);
-      if constexpr (kSplit) {
-        float v[8];
-        if (mm < mv && kk < ke) {
-          const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
-          const mu32x4* pa = reinterpret_cast<const mu32x4*>(A + row + kk);
-          const mu32x4 r0 = pa[0], r1 = pa[1];
-          const unsigned raw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  auto load_a = [&](int k0) { load_a_into(k0, areg); };
+  auto store_a_from = [&](const mu32x4(&areg)[NF][AW]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(raw[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        }
+    for (int i = 0; i < NF; ++i) {
+      const int f = a_lds_of(tid + 256 * i);
+      if constexpr (kPre) {
+        lds_hi[f] = areg[i][0];
+        lds_lo[f] = areg[i][1];
+      } else if constexpr (kF32) {
+        const unsigned raw[8] = {areg[i][0].x, areg[i][0].y, areg[i][0].z, areg[i][0].w,
+                                 areg[i][AW - 1].x, areg[i][AW - 1].y, areg[i][AW - 1].z, areg[i][AW - 1].w};
         unsigned short h[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const bf16_t hb = from_f32<bf16_t>(v[e]);
-          const bf16_t lb = from_f32<bf16_t>(v[e] - to_f32(hb));
+          // split in B's own 16-bit type, the type the matrix-core product reads both operands in
+          const float v = __uint_as_float(raw[e]);
+          const TB hb = from_f32<TB>(v);
+          const TB lb = from_f32<TB>(v - to_f32(hb));
           h[e] = hb.b;
           lo[e] = lb.b;
         }
@@ -329,25 +396,89 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
         lds_lo[f] = mu32x4{lo[0] | ((unsigned)lo[1] << 16), lo[2] | ((unsigned)lo[3] << 16),
                            lo[4] | ((unsigned)lo[5] << 16), lo[6] | ((unsigned)lo[7] << 16)};
       } else {
-        mu32x4 v = mu32x4{0u, 0u, 0u, 0u};
-        if (mm < mv && kk < ke) {
-          const long long row = (long long)(a_idx ? a_idx[mm] : mm) * lda;
-          v = reinterpret_cast<const mu32x4*>(A + row + kk)[0];
-        }
-        lds_hi[f] = v;
+        lds_hi[f] = areg[i][0];
       }
     }
-    __syncthreads();
-    if (k0 + 32 * kSteps < ke) load_b(k0 + 32 * kSteps, bnxt);  // uniform
+  };
+  auto store_a = [&]() { store_a_from(areg); };
+  // per step the high parts of every tile, then the low parts: consecutive products never use the
+  // same accumulator
+  auto products = [&](const mu32x4(&bv)[kSteps]) {
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
 #pragma unroll
-      for (int t = 0; t < NRT; ++t) {
-        const int f = (t * kSteps + st) * 64 + lane;
-        acc[t] = mfma_op<TB>::run(lds_hi[f], bcur[st], acc[t]);
-        if constexpr (kSplit) acc[t] = mfma_op<TB>::run(lds_lo[f], bcur[st], acc[t]);
+      for (int t = 0; t < NRT; ++t) acc[t] = mfma_op<TB>::run(lds_hi[(t * kSteps + st) * 64 + lane], bv[st], acc[t]);
+      if constexpr (kSplit) {
+#pragma unroll
+        for (int t = 0; t < NRT; ++t) acc[t] = mfma_op<TB>::run(lds_lo[(t * kSteps + st) * 64 + lane], bv[st], acc[t]);
       }
     }
+  };
+  constexpr int S = 32 * kSteps;
+  // two sub-chunks ahead only while the registers allow it (one or two row tiles of 16-bit A)
+  constexpr bool kDeep = !kSplit && NRT <= 2;
+  if constexpr (kDeep) {
+    // 16-bit A: two sub-chunks of A and B in flight ahead of the products. Three register sets,
+    // named in a loop unrolled by three; loads past the chunk read its first columns and are
+    // zeroed, so every step issues the same loads.
+    mu32x4 a0[NF][AW], a1[NF][AW], a2[NF][AW], b2[kSteps];
+    mu32x4(&b0)[kSteps] = pb0;
+    mu32x4(&b1)[kSteps] = pb1;
+    if constexpr (kPreB < 1) load_b(kb, b0);
+    load_a_into(kb, a0);
+    if constexpr (kPreB < 2) load_b(kb + S, b1);
+    load_a_into(kb + S, a1);
+#define GSI_SKSTEP(KC, ACUR, BCUR, ANX, BNX)                                                              \
+  do {                                                                                                   \
+    __syncthreads();                                                                                     \
+    store_a_from(ACUR);                                                                                  \
+    __syncthreads();                                                                                     \
+    load_a_into((KC) + 2 * S, ANX);                                                                      \
+    load_b((KC) + 2 * S, BNX);                                                                           \
+    products(BCUR);                                                                                      \
+  } while (0)
+    for (int k0 = kb;; k0 += 3 * S) {
+      GSI_SKSTEP(k0, a0, b0, a2, b2);
+      if (k0 + S >= ke) break;
+      GSI_SKSTEP(k0 + S, a1, b1, a0, b0);
+      if (k0 + 2 * S >= ke) break;
+      GSI_SKSTEP(k0 + 2 * S, a2, b2, a1, b1);
+      if (k0 + 3 * S >= ke) break;
+    }
+#undef GSI_SKSTEP
+  }
+  mu32x4 bcur[kSteps], bnxt[kSteps];
+  if constexpr (kPre) {
+    // A arrives split (the batched fast product, K of one or two sub-chunks): each sub-chunk's
+    // loads issued together, no registers held for the next one
+    for (int k0 = kb; k0 < ke; k0 += 32 * kSteps) {
+      load_a(k0);
+      load_b(k0, bcur);
+      __syncthreads();  // the previous sub-chunk's A fragments are no longer read
+      store_a();
+      __syncthreads();
+      products(bcur);
+    }
+  }
+  constexpr bool kNext = kF32 || (!kSplit && !kDeep);  // one sub-chunk ahead
+  if constexpr (kNext) {
+    if constexpr (kPreB >= 1) {
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) bcur[st] = pb0[st];
+    } else {
+      load_b(kb, bcur);
+    }
+    load_a(kb);
+  }
+  for (int k0 = kb; kNext && k0 < ke; k0 += 32 * kSteps) {
+    __syncthreads();  // the previous sub-chunk's A fragments are no longer read
+    store_a();
+    __syncthreads();
+    if (k0 + 32 * kSteps < ke) {  // uniform: the next sub-chunk's A and B in flight during the products
+      load_a(k0 + 32 * kSteps);
+      load_b(k0 + 32 * kSteps, bnxt);
+    }
+    products(bcur);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) bcur[st] = bnxt[st];
   }
@@ -355,8 +486,13 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
   for (int t = 0; t < NRT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int mm = 16 * t + 4 * kq + r;
-      if (mm < mv && bok) part[(long long)mm * n + nn] = acc[t][r];
+      if (orow[t][r] >= 0 && bok) {
+        float* q = part + (long long)orow[t][r] * n + nn;
+        if (coherent)  // read by another block of the same launch
+          __hip_atomic_store(q, acc[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *q = acc[t][r];
+      }
     }
 }
 
@@ -374,11 +510,12 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_staged_kernel(const void* 
   float* pz = part + (long long)blockIdx.z * m * n;
   const TA* a = reinterpret_cast<const TA*>(A);
   const TB* b = reinterpret_cast<const TB*>(B);
+  mu32x4 b0[8], b1[8];  // loaded inside (no early B loads here)
   switch ((mv + 15) >> 4) {  // uniform
-    case 1: skinny_staged_tiles<TA, TB, 1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    case 2: skinny_staged_tiles<TA, TB, 2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    case 3: skinny_staged_tiles<TA, TB, 3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
-    default: skinny_staged_tiles<TA, TB, 4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo); break;
+    case 1: skinny_staged_tiles<TA, TB, 1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
+    case 2: skinny_staged_tiles<TA, TB, 2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
+    case 3: skinny_staged_tiles<TA, TB, 3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
+    default: skinny_staged_tiles<TA, TB, 4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
   }
 }
 
@@ -1353,12 +1490,31 @@ static PrecomputePlan precompute_plan(int dtype, int d_out, int d, int k) {
 
 int precompute_splits(int dtype, int d_out, int d, int k) { return precompute_plan(dtype, d_out, d, k).sm; }
 
+// the (V^T V - I) V^T product on matrix cores: D split into 16-bit high and low rows, one
+// product for both ([D_hi; D_lo] against V's rows, float32 sums), then their sum in that order
+static bool vdt_on_mfma(int dtype, int d, int k) { return dtype != GSI_F32 && d % 256 == 0 && k % 64 == 0 && k >= 64; }
+static size_t vdt_ws_bytes(int dtype, int d, int k) {
+  if (!vdt_on_mfma(dtype, d, k)) return 0;
+  return align256((size_t)2 * k * d * 4) + align256((size_t)2 * k * k * 2);
+}
+
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k) {
   const PrecomputePlan pl = precompute_plan(dtype, d_out, d, k);
   if (pl.sm == 0) return 0;
   const size_t img = (size_t)pl.sm * (pl.fused ? d_out + k : d_out) * k * 4;
   const size_t gram = pl.fused ? 0 : (size_t)pl.sd * k * k * 4;
-  return (img + 255) / 256 * 256 + (gram + 255) / 256 * 256;
+  return std::max((img + 255) / 256 * 256 + (gram + 255) / 256 * 256, vdt_ws_bytes(dtype, d, k));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ D, long long n, T* __restrict__ hi,
+                                                         T* __restrict__ lo) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const float v = D[i];
+    const T h = from_f32<T>(v);
+    hi[i] = h;
+    lo[i] = from_f32<T>(v - to_f32(h));
+  }
 }
 
 static int launch_wide_partials(int dtype, const void* A, const void* A2, int m_split, const void* B, int m, int n,
@@ -1407,6 +1563,32 @@ int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* 
   const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
   if (rc != GSI_OK) return rc;
   return launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s);
+}
+
+int launch_vdt(int dtype, const float* Dl, const void* V, void* VDt, int d, int k, void* ws, size_t ws_bytes,
+               hipStream_t s) {
+  if (ws && vdt_on_mfma(dtype, d, k) && vdt_ws_bytes(dtype, d, k) <= ws_bytes) {
+    float* part = (float*)ws;  // [2k][d]: rows D_hi V^T, then D_lo V^T
+    char* dh = (char*)ws + align256((size_t)2 * k * d * 4);
+    char* dl = dh + (size_t)k * k * 2;
+    const long long kk = (long long)k * k;
+    const unsigned sb = (unsigned)std::min<long long>(1024, (kk + 255) / 256);
+    if (dtype == GSI_BF16)
+      split_rows_kernel<bf16_t><<<sb, 256, 0, s>>>(Dl, kk, (bf16_t*)dh, (bf16_t*)dl);
+    else
+      split_rows_kernel<f16_t><<<sb, 256, 0, s>>>(Dl, kk, (f16_t*)dh, (f16_t*)dl);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+    int rc = launch_wide_partials(dtype, dh, dl, k, V, 2 * k, d, k, 1, part, s);
+    if (rc != GSI_OK) return rc;
+    const int nb = (int)(((long long)k * (d / 4) + 255) / 256);
+    if (dtype == GSI_BF16)
+      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(part, 2, (long long)k * d, nullptr, 0, 0, k, d, VDt, nullptr, nb);
+    else
+      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(part, 2, (long long)k * d, nullptr, 0, 0, k, d, VDt, nullptr, nb);
+    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+  }
+  // row j of (V (V^T V - I))^T = sum_l D[j][l] V[:, l]: D against V's rows
+  return launch_gemm_nt(GSI_F32, dtype, dtype, Dl, k, nullptr, V, k, VDt, d, nullptr, k, d, k, nullptr, 0, s);
 }
 
 int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long long lda, const int* a_idx,
@@ -1598,13 +1780,21 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
   if (threadIdx.x == 0) { counts[0] = base[0]; counts[1] = base[1]; }
 }
 
+static size_t proj_bytes(int k, int T) {
+  const size_t t = (size_t)std::min(T, 64);
+  return align256((size_t)(kMaxK / 16) * t * 2 * 4) + align256((size_t)kMaxProjChunks * t * 4);
+}
 size_t batched_ws_bytes(int k, int T, int d_out) {
-  return 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
-         2 * align256(split_part_elems(T, d_out) * 4);
+  return kBatchedCounters * 4 + 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
+         2 * align256(split_part_elems(T, d_out) * 4) + proj_bytes(k, T);
 }
 BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   char* p = (char*)base;
   BatchedWs w;
+  // the counters first, at an offset and size that do not depend on the site's shape: they must
+  // stay zero between calls whatever else the workspace was carved into
+  w.cnt = (int*)p;
+  p += kBatchedCounters * 4;
   w.part_elems = split_part_elems(T, d_out);
   w.G = (float*)p; p += align256((size_t)T * k * 4);
   w.H = (float*)p; p += align256((size_t)T * k * 4);
@@ -1615,6 +1805,10 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   w.part = w.part_elems ? (float*)p : nullptr;
   p += align256(w.part_elems * 4);
   w.part2 = w.part_elems ? (float*)p : nullptr;
+  p += align256(w.part_elems * 4);
+  const size_t t = (size_t)std::min(T, 64);
+  w.gq = (float*)p; p += align256((size_t)(kMaxK / 16) * t * 2 * 4);
+  w.nx2p = (float*)p;
   return w;
 }
 
@@ -1662,6 +1856,390 @@ int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long 
   compact_kernel<<<1, 1024, 0, s>>>(gate, gate_ld, T, w.fast_idx, w.slow_idx, w.counts);
   if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
   return GSI_OK;
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// Batched path in two launches per site and chunk of at most 64 tokens (16-bit weights).
+//
+// bproj_kernel: [G | H] = X [V_k | V_k (V_k^T V_k - I)] on matrix cores, h = (V^T V - I) g being
+// the second half [GSI §2.2: the residual norm from g and the stored basis]. Block (c, tt): the
+// 16 columns 16 c .. of g and of h for the tokens 16 tt .. 16 tt + 15, over all of x's K; its NW
+// waves take every NW-th 32-column sub-step and their partial tiles are added in wave order
+// through LDS. Wave 0 stores g split into high and low parts in the weight dtype and, per token,
+// the tile's sums of g^2 and g h (fixed butterfly) to gq[t][c][0..1]; blocks of column tile 0
+// also store |x|^2 per token.
+// ---------------------------------------------------------------------------------------------
+struct BProjArgs {
+  const void* X;
+  long long x_ld;
+  int ntok, d, k, with_h;
+  const void* Vt;
+  const void* VDt;
+  float* nx2p;  // [ntok][kMaxProjChunks] (chunk 0 only)
+  void* Ghi;    // [ntok][k] high parts of g in the weight dtype
+  void* Glo;    // [ntok][k] low parts: g - Ghi rounded to the weight dtype
+  float* gq;    // [ntok][kMaxK / 16][2]
+};
+
+template <typename T>
+__device__ __forceinline__ float sumsq8(mu32x4 q) {
+  const T* e = reinterpret_cast<const T*>(&q);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = __builtin_fmaf(to_f32(e[i]), to_f32(e[i]), s);
+  return s;
+}
+
+template <typename T, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void bproj_kernel(BProjArgs p) {
+  __shared__ float red[NW][2][256];
+  __shared__ float redx[NW][16];
+  const int c = blockIdx.x, tt = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tok = 16 * tt + (lane & 15);
+  const bool tok_ok = tok < p.ntok;
+  const T* xrow = reinterpret_cast<const T*>(p.X) + (long long)(tok_ok ? tok : 0) * p.x_ld;
+  const T* vrow = reinterpret_cast<const T*>(p.Vt) + (long long)(16 * c + (lane & 15)) * p.d;
+  const T* hrow = p.with_h ? reinterpret_cast<const T*>(p.VDt) + (long long)(16 * c + (lane & 15)) * p.d : vrow;
+  const int ko = 8 * (lane >> 4);
+  const bool want_x2 = c == 0;
+  const int nsub = p.d / 32;
+  // U sub-steps per batch, every load of a batch issued before any is used: a memory round trip
+  // costs microseconds under load, so the number of batches, not the bytes, sets the time
+  mf32x4 ag = mf32x4{0.f, 0.f, 0.f, 0.f}, ah = ag;
+  float sx = 0.f;
+  const mu32x4 zero = mu32x4{0u, 0u, 0u, 0u};
+  const int nb = (nsub + NW * U - 1) / (NW * U);
+  for (int b = 0; b < nb; ++b) {
+    mu32x4 x[U], v[U], h[U];
+    // batch b: sub-steps w + NW (U b + u); past the end a load reads sub-step 0 and is zeroed
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sub = w + NW * (U * b + u);
+      const bool in = sub < nsub;  // uniform in the wave
+      const int kk = (in ? 32 * sub : 0) + ko;
+      const mu32x4 xv = *reinterpret_cast<const mu32x4*>(xrow + kk);
+      const mu32x4 vv = *reinterpret_cast<const mu32x4*>(vrow + kk);
+      const mu32x4 hv = *reinterpret_cast<const mu32x4*>(hrow + kk);
+      x[u] = (in && tok_ok) ? xv : zero;
+      v[u] = in ? vv : zero;
+      h[u] = in ? hv : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ag = mfma_op<T>::run(x[u], v[u], ag);
+      if (p.with_h) ah = mfma_op<T>::run(x[u], h[u], ah);
+      if (want_x2) sx += sumsq8<T>(x[u]);
+    }
+  }
+  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold token l mod 16's four K groups
+  sx += __shfl_xor(sx, 16, 64);
+  sx += __shfl_xor(sx, 32, 64);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    red[w][0][r * 64 + lane] = ag[r];
+    red[w][1][r * 64 + lane] = ah[r];
+  }
+  if (lane < 16) redx[w][lane] = sx;
+  __syncthreads();
+  if (w != 0) return;
+  const int k = p.k;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float g = 0.f, h = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      g += red[ww][0][r * 64 + lane];
+      h += red[ww][1][r * 64 + lane];
+    }
+    // this lane: token 16 tt + 4 (lane / 16) + r, column 16 c + lane mod 16
+    const int t = 16 * tt + 4 * (lane >> 4) + r;
+    const bool ok = t < p.ntok;
+    if (ok) {
+      // g split once here for the fast product's matrix-core passes (|g - hi - lo| <= 2^-18 |g|
+      // for bf16)
+      const T hi = from_f32<T>(g);
+      const T lo = from_f32<T>(g - to_f32(hi));
+      reinterpret_cast<T*>(p.Ghi)[(long long)t * k + 16 * c + (lane & 15)] = hi;
+      reinterpret_cast<T*>(p.Glo)[(long long)t * k + 16 * c + (lane & 15)] = lo;
+    }
+    float gg = g * g, gh = g * h;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      gg += __shfl_xor(gg, o, 64);
+      gh += __shfl_xor(gh, o, 64);
+    }
+    if (ok && (lane & 15) == 0) {
+      p.gq[((long long)t * (kMaxK / 16) + c) * 2 + 0] = gg;
+      p.gq[((long long)t * (kMaxK / 16) + c) * 2 + 1] = gh;
+    }
+  }
+  if (want_x2 && lane < 16 && tok_ok) {
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += redx[ww][lane];
+    p.nx2p[(long long)tok * kMaxProjChunks] = v;
+  }
+}
+
+// Cross-block hand-off inside one launch without cache flushes: partial sums are written with
+// device-scope stores (coherent across the XCDs' L2s), every wave waits until its stores have
+// completed, then one thread counts the block in; the block that counts last reads the partial
+// sums with device-scope loads and resets the counter for the next launch.
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool arrive_last(int* cnt, int total, int* s_last) {
+  dwait_vmcnt<0>();  // this wave's device-scope stores are complete
+  __syncthreads();   // ... and every other wave's
+  if (threadIdx.x == 0)
+    *s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+  __syncthreads();
+  return *s_last;
+}
+
+// ---------------------------------------------------------------------------------------------
+// bprod_kernel: gate and both products of one site for the chunk's tokens. Every block first
+// forms the gate of every token from the projection's pieces, in one fixed order (nr2 =
+// (|x|^2 - |g|^2) + g^T h, fast iff nr2 < fl(eps^2) |x|^2 [GSI §2.2]), so all blocks agree, and
+// lists the fast and slow tokens in token order in LDS; block (0, 0) stores the gate bits and
+// rho. Block (b, z) then owns output rows 64 b .. 64 b + 63 and K chunk z: y = M g over the fast
+// tokens (g as its two 16-bit parts, two matrix-core passes; K columns of M in [z kcm, ..)) and y = W x over the slow tokens (K columns of W in
+// [z kcw, ..)), both on the staged skinny tiles, raw float32 sums to Py[z][t][row]. The last
+// block of a row tile adds the chunks in chunk order and stores y rows in the weight dtype.
+// A static-projection site lists every token as fast, a dense site every token as slow.
+// ---------------------------------------------------------------------------------------------
+struct BProdArgs {
+  const void* X;
+  long long x_ld;
+  int ntok, d, d_out, k, mode;
+  float eps;
+  const void* Ghi;    // [ntok][k] g, high and low parts in the weight dtype
+  const void* Glo;
+  const float* gq;    // [ntok][kMaxK / 16][2]
+  const float* nx2p;  // [ntok][kMaxProjChunks]
+  int zp;
+  const void* M;
+  const void* W;
+  int kcm, kcw;
+  float* Py;  // [Zy][ntok][d_out]
+  int* cnt;   // [d_out / 64], zero between launches
+  void* Y;
+  long long y_ld;
+  uint8_t* gate;
+  int gate_ld;
+  float* rho;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
+  __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[4 * 8 * 64];
+  __shared__ int s_fast[64], s_slow[64];
+  __shared__ int s_n[2], s_last;
+  const int z = blockIdx.z, nz = gridDim.z;
+  // the slow product's first sub-chunk of W is requested before the gate is known: it
+  // arrives while the gate and the fast product run (a site with no slow token wastes it)
+  const T* wt = reinterpret_cast<const T*>(p.W);
+  const int kbw = z * p.kcw, kew = min(p.d, kbw + p.kcw);
+  mu32x4 wb0[8], wb1[8];  // wb1 is loaded by the slow pass itself (registers)
+  skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0);
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    bool fast = false;
+    float r = __builtin_nanf("");
+    if (t < p.ntok) {
+      if (p.mode == kSiteGated) {
+        // this token's pieces are contiguous: all loaded at once, then added in a fixed order
+        float4 xv[kMaxProjChunks / 4], qv[kMaxK / 32];
+        const float4* xp = reinterpret_cast<const float4*>(p.nx2p + (long long)t * kMaxProjChunks);
+        const float4* qp = reinterpret_cast<const float4*>(p.gq + (long long)t * (kMaxK / 16) * 2);
+#pragma unroll
+        for (int i = 0; i < kMaxProjChunks / 4; ++i) xv[i] = xp[i];
+#pragma unroll
+        for (int i = 0; i < kMaxK / 32; ++i)
+          if (i < p.k / 32 + 1) qv[i] = qp[i];
+        float nx2 = 0.f, gg = 0.f, q = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxProjChunks; ++i) {
+          const float v = i % 4 == 0 ? xv[i / 4].x : i % 4 == 1 ? xv[i / 4].y : i % 4 == 2 ? xv[i / 4].z : xv[i / 4].w;
+          if (i < p.zp) nx2 += v;
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxK / 16; ++c) {
+          const float4 v = qv[c / 2];
+          if (c < p.k / 16) {
+            gg += c % 2 == 0 ? v.x : v.z;
+            q += c % 2 == 0 ? v.y : v.w;
+          }
+        }
+        const float nr2 = (nx2 - gg) + q;
+        const float thr = p.eps * p.eps;
+        fast = nr2 < thr * nx2;
+        r = sqrtf(fmaxf(nr2, 0.f) / nx2);
+      } else {
+        fast = p.mode == kSiteStatic;
+      }
+    }
+    const bool valid = t < p.ntok;
+    const u64 mf = __ballot(valid && fast), ms = __ballot(valid && !fast);
+    const u64 below = t ? (~0ull >> (64 - t)) : 0ull;
+    if (valid && fast) s_fast[__popcll(mf & below)] = t;
+    if (valid && !fast) s_slow[__popcll(ms & below)] = t;
+    if (t == 0) {
+      s_n[0] = __popcll(mf);
+      s_n[1] = __popcll(ms);
+    }
+    if (blockIdx.x == 0 && z == 0 && valid) {
+      p.gate[(long long)t * p.gate_ld] = fast ? 0 : 1;
+      if (p.rho) p.rho[(long long)t * p.gate_ld] = r;
+    }
+  }
+  __syncthreads();
+  const int nf = s_n[0], ns = s_n[1];
+  float* pz = p.Py + (long long)z * p.ntok * p.d_out;
+  if (nf > 0) {  // fast tokens: y = M g     [GSI §2.2]
+    const int kb = z * p.kcm, ke = min(p.k, kb + p.kcm);
+    const T* gh = reinterpret_cast<const T*>(p.Ghi);
+    const T* gl = reinterpret_cast<const T*>(p.Glo);
+    const T* m = reinterpret_cast<const T*>(p.M);
+    switch ((nf + 15) >> 4) {
+      case 1: skinny_staged_tiles<T, T, 1, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
+      case 2: skinny_staged_tiles<T, T, 2, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
+      case 3: skinny_staged_tiles<T, T, 3, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
+      default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
+    }
+  }
+  if (ns > 0) {  // slow tokens: y = W x     [GSI §2.2]
+    const T* xa = reinterpret_cast<const T*>(p.X);
+    __syncthreads();  // the fast pass's staged tokens are no longer read
+    switch ((ns + 15) >> 4) {
+      case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
+      case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
+      case 3: skinny_staged_tiles<T, T, 3, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
+      default: skinny_staged_tiles<T, T, 4, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
+    }
+  }
+  if (!arrive_last(&p.cnt[blockIdx.x], nz, &s_last)) return;
+  // the last block of the row tile: thread i takes rows 64 b + 4 (i mod 16) .. + 3 of tokens
+  // i / 16 + 16 s, summing the chunks in chunk order
+  const int row = blockIdx.x * 64 + 4 * (threadIdx.x & 15);
+  // the four tokens' chunk values all in flight at once, then added in chunk order
+  // one device-scope acquire, then ordinary 16-byte loads (fewer loads than device-scope 4-byte
+  // ones, all in flight at once)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  float4 pv[4][kMaxProdChunks];
+#pragma unroll
+  for (int sg = 0; sg < 4; ++sg) {
+    const int t = (threadIdx.x >> 4) + 16 * sg;
+#pragma unroll
+    for (int zz = 0; zz < kMaxProdChunks; ++zz)
+      if (zz < nz && t < p.ntok)
+        pv[sg][zz] = *reinterpret_cast<const float4*>(p.Py + ((long long)zz * p.ntok + t) * p.d_out + row);
+  }
+#pragma unroll
+  for (int sg = 0; sg < 4; ++sg) {
+    const int t = (threadIdx.x >> 4) + 16 * sg;
+    if (t >= p.ntok) continue;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int zz = 0; zz < kMaxProdChunks; ++zz) {
+      if (zz < nz) {
+        a[0] += pv[sg][zz].x;
+        a[1] += pv[sg][zz].y;
+        a[2] += pv[sg][zz].z;
+        a[3] += pv[sg][zz].w;
+      }
+    }
+    T* yr = reinterpret_cast<T*>(p.Y) + (long long)t * p.y_ld + row;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yr[e] = from_f32<T>(a[e]);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&p.cnt[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
+  BatchedSplit sp{0, 0, 0, 0, 0};
+  if (dtype == GSI_F32 || ntok < 1 || ntok > 64) return sp;
+  if (L.d % 32 != 0 || L.d_out % 64 != 0 || L.k % 16 != 0 || L.k > kMaxK) return sp;
+  if (kMaxK / 16 + L.d_out / 64 > kBatchedCounters) return sp;
+  if (L.mode != kSiteDense && (L.k == 0 || !L.VDt)) return sp;
+  sp.zp = 1;  // the projection covers all of K in one block
+  sp.kc = L.d;
+  // products: about 256 to 512 blocks of 64 output rows, at most kMaxProdChunks chunks of K;
+  // every chunk of K (of W and of M) non-empty
+  const int nrt = L.d_out / 64;
+  int zy = std::max(1, std::min(kMaxProdChunks, 512 / nrt));
+  for (;; --zy) {
+    const int kcw = ((L.d + zy - 1) / zy + 7) / 8 * 8;
+    const int kcm = L.mode == kSiteDense ? 8 : ((L.k + zy - 1) / zy + 7) / 8 * 8;
+    const bool ok = (long long)(zy - 1) * kcw < L.d && (L.mode == kSiteDense || (long long)(zy - 1) * kcm < L.k);
+    if (ok || zy == 1) {
+      sp.zy = zy;
+      sp.kcw = kcw;
+      sp.kcm = kcm;
+      break;
+    }
+  }
+  return sp;
+}
+
+int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, const void* X, long long x_ld,
+                        int ntok, float eps, void* Y, long long y_ld, uint8_t* gate, int gate_ld, float* rho,
+                        const BatchedWs& w, hipStream_t s) {
+  if (L.mode != kSiteDense) {
+    BProjArgs a;
+    a.X = X;
+    a.x_ld = x_ld;
+    a.ntok = ntok;
+    a.d = L.d;
+    a.k = L.k;
+    a.with_h = L.mode == kSiteGated;
+    a.Vt = L.Vt;
+    a.VDt = L.VDt;
+    a.nx2p = w.nx2p;
+    a.Ghi = w.G;  // the float32 G region holds both 16-bit halves
+    a.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
+    a.gq = w.gq;
+    dim3 grid(L.k / 16, (ntok + 15) / 16);
+    // 8 waves with 16 sub-steps each in one batch (d <= 4096), or 16 waves in batches of 8
+    const bool wide = L.d >= 8192;
+    void* fn = dtype == GSI_BF16 ? (wide ? (void*)bproj_kernel<bf16_t, 16, 8> : (void*)bproj_kernel<bf16_t, 8, 16>)
+                                 : (wide ? (void*)bproj_kernel<f16_t, 16, 8> : (void*)bproj_kernel<f16_t, 8, 16>);
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, grid, dim3(wide ? 1024 : 512), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+  }
+  BProdArgs b;
+  b.X = X;
+  b.x_ld = x_ld;
+  b.ntok = ntok;
+  b.d = L.d;
+  b.d_out = L.d_out;
+  b.k = L.k;
+  b.mode = L.mode;
+  b.eps = eps;
+  b.Ghi = w.G;
+  b.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
+  b.gq = w.gq;
+  b.nx2p = w.nx2p;
+  b.zp = 1;
+  b.M = L.M;
+  b.W = L.W;
+  b.kcm = sp.kcm;
+  b.kcw = sp.kcw;
+  b.Py = w.part;
+  b.cnt = w.cnt + kMaxK / 16;
+  b.Y = Y;
+  b.y_ld = y_ld;
+  b.gate = gate;
+  b.gate_ld = gate_ld;
+  b.rho = rho;
+  dim3 grid(L.d_out / 64, 1, sp.zy);
+  if (dtype == GSI_BF16)
+    bprod_kernel<bf16_t><<<grid, 256, 0, s>>>(b);
+  else
+    bprod_kernel<f16_t><<<grid, 256, 0, s>>>(b);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 }  // namespace gsi

@@ -152,6 +152,10 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k);
 int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
                       void* ws, size_t ws_bytes, hipStream_t s);
+// VDt[k, d] = (V (V^T V - I))^T from Dl = V^T V - I and V (d x k), in the weight dtype; matrix
+// cores with a workspace of precompute_ws_bytes()
+int launch_vdt(int dtype, const float* Dl, const void* V, void* VDt, int d, int k, void* ws, size_t ws_bytes,
+               hipStream_t s);
 // dst[k, d] = transpose(src[d, k]); with `plan` (P <= 256 entries), also the decode plan rows of
 // the layer described by desc
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, const LayerDesc& desc, int P,
@@ -171,6 +175,18 @@ struct BatchedWs {
   float* part;   // [kMaxSplit, T, d_out] split-K partial sums of the fast product (and the projection)
   float* part2;  // [kMaxSplit, T, d_out] split-K partial sums of the slow product
   long long part_elems;
+  // two-launch path (chunks of at most 64 tokens)
+  float* gq;     // [64][kMaxK / 16][2] per token and column tile: sum g^2, sum g h
+  float* nx2p;   // [64][kMaxProjChunks] per token, chunk sums of |x|^2
+  int* cnt;      // [kBatchedCounters] arrival counters (projection tiles, then row tiles), zero between launches
+};
+constexpr int kMaxProjChunks = 16;
+constexpr int kMaxProdChunks = 4;  // K chunks of the two-launch path's products
+constexpr int kBatchedCounters = 4096;  // arrival counters of the two-launch path (16 KB)
+// K chunks of the two-launch batched path of one site (zp == 0 and zy == 0: not applicable)
+struct BatchedSplit {
+  int zp, kc;         // projection: chunks of x's K and their width
+  int zy, kcw, kcm;   // products: chunks of K and their widths over W and over M
 };
 constexpr int kMaxSplit = 8;  // K chunks of a split product
 // partial-sum elements the batched path may use (none when every call runs one token)
@@ -190,5 +206,10 @@ int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int
                    const int* cb, const int* ib, int m, int n, void* C, long long ldc, hipStream_t s);
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s);
+BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok);
+// projection (with the gate pieces) and products of one site over ntok <= 64 tokens
+int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, const void* X, long long x_ld,
+                        int ntok, float eps, void* Y, long long y_ld, uint8_t* gate, int gate_ld, float* rho,
+                        const BatchedWs& w, hipStream_t s);
 
 }  // namespace gsi

@@ -30,6 +30,7 @@ struct LayerDesc {
   const void* M;      // [d_out, k]
   const float* Dl;    // [k, k] = V^T V - I
   const void* W;      // [d_out, d]
+  const void* VDt;    // [k, d] = (V (V^T V - I))^T in the weight dtype (16-bit layers; batched gate)
   int d, d_out, k, mode;
   long long x_off, y_off;  // column offsets into stacked X / Y rows
 };
