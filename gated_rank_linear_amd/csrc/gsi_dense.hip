@@ -274,13 +274,17 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
 // before this one's products.
 // B steps of one 256-column sub-chunk for this lane (row nn of B, the lane's 8-element K groups);
 // steps outside [kb, ke) read column kb and are zeroed
+// With B2, column tile b of C takes its first 32 columns from rows 32 b .. of B and the next 32
+// from the same rows of B2 (waves 0-1 and 2-3).
 template <typename TB>
 __device__ __forceinline__ void skinny_load_b(const TB* __restrict__ B, long long ldb, int n, int kb, int ke, int k0,
-                                              mu32x4 (&bv)[8]) {
+                                              mu32x4 (&bv)[8], const TB* __restrict__ B2 = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nn = blockIdx.x * 64 + wave * 16 + (lane & 15);
   const bool bok = nn < n;
-  const long long brow = bok ? (long long)nn * ldb : 0;
+  const int brow_i = B2 ? blockIdx.x * 32 + (wave & 1) * 16 + (lane & 15) : nn;
+  if (B2 && wave >= 2) B = B2;
+  const long long brow = bok ? (long long)brow_i * ldb : 0;
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
     const int kk = k0 + 32 * st + 8 * (lane >> 4);
@@ -297,7 +301,10 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
                                                     float* __restrict__ part, mu32x4* __restrict__ lds_hi,
                                                     mu32x4* __restrict__ lds_lo, const int* __restrict__ o_idx,
                                                     bool coherent, const TA* __restrict__ A_lo, mu32x4 (&pb0)[8],
-                                                    mu32x4 (&pb1)[8]) {
+                                                    mu32x4 (&pb1)[8], const TB* __restrict__ B2 = nullptr,
+                                                    float* __restrict__ x2out = nullptr) {
+  // B2: second row source (skinny_load_b); x2out (16-bit A): each A row's sum of squares over
+  // [kb, ke) to x2out[row * kMaxProjChunks]
   // kPreB (16-bit A only): the caller has already loaded the first kPreB sub-chunks' B steps into
   // pb0 (and pb1) with skinny_load_b
   // kF32: A is float32 and is split here; kPre: A arrives split, high parts at A and low parts at
@@ -314,7 +321,7 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t] = mf32x4{0.f, 0.f, 0.f, 0.f};
   static_assert(kSteps == 8, "skinny_load_b loads eight steps");
-  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) { skinny_load_b(B, ldb, n, kb, ke, k0, bv); };
+  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) { skinny_load_b(B, ldb, n, kb, ke, k0, bv, B2); };
   // A fragments of a sub-chunk: thread tid takes fragments f = tid + 256 i (i < 2 NRT); they are
   // loaded into registers one sub-chunk ahead and written to LDS (split, for a float32 A) at the
   // start of the sub-chunk that uses them
@@ -371,7 +378,25 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
     }
   };
   auto load_a = [&](int k0) { load_a_into(k0, areg); };
+  // rows (tid / 32) + 8 i: their sums of squares, complete in lane tid mod 32 == 0
+  float xs[NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) xs[i] = 0.f;
   auto store_a_from = [&](const mu32x4(&areg)[NF][AW]) {
+    if constexpr (!kSplit) {
+      if (x2out) {  // uniform
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          float v = 0.f;
+          const TA* e = reinterpret_cast<const TA*>(&areg[i][0]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v = __builtin_fmaf(to_f32(e[j]), to_f32(e[j]), v);
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+          xs[i] += v;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const int f = a_lds_of(tid + 256 * i);
@@ -494,6 +519,15 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
           *q = acc[t][r];
       }
     }
+  if constexpr (!kSplit) {
+    if (x2out && (tid & 31) == 0) {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const int mm = (tid >> 5) + 8 * i;
+        if (mm < mv) x2out[(long long)mm * kMaxProjChunks] = xs[i];
+      }
+    }
+  }
 }
 
 template <typename TA, typename TB>
@@ -1782,7 +1816,8 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
 
 static size_t proj_bytes(int k, int T) {
   const size_t t = (size_t)std::min(T, 64);
-  return align256((size_t)(kMaxK / 16) * t * 2 * 4) + align256((size_t)kMaxProjChunks * t * 4);
+  return align256((size_t)kMaxProjChunks * t * 2 * k * 4) + align256((size_t)(kMaxK / 16) * t * 2 * 4) +
+         align256((size_t)kMaxProjChunks * t * 4);
 }
 size_t batched_ws_bytes(int k, int T, int d_out) {
   return kBatchedCounters * 4 + 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
@@ -1807,6 +1842,7 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   w.part2 = w.part_elems ? (float*)p : nullptr;
   p += align256(w.part_elems * 4);
   const size_t t = (size_t)std::min(T, 64);
+  w.Pp = (float*)p; p += align256((size_t)kMaxProjChunks * t * 2 * k * 4);
   w.gq = (float*)p; p += align256((size_t)(kMaxK / 16) * t * 2 * 4);
   w.nx2p = (float*)p;
   return w;
@@ -1859,130 +1895,6 @@ int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long 
 }
 
 
-// ---------------------------------------------------------------------------------------------
-// Batched path in two launches per site and chunk of at most 64 tokens (16-bit weights).
-//
-// bproj_kernel: [G | H] = X [V_k | V_k (V_k^T V_k - I)] on matrix cores, h = (V^T V - I) g being
-// the second half [GSI §2.2: the residual norm from g and the stored basis]. Block (c, tt): the
-// 16 columns 16 c .. of g and of h for the tokens 16 tt .. 16 tt + 15, over all of x's K; its NW
-// waves take every NW-th 32-column sub-step and their partial tiles are added in wave order
-// through LDS. Wave 0 stores g split into high and low parts in the weight dtype and, per token,
-// the tile's sums of g^2 and g h (fixed butterfly) to gq[t][c][0..1]; blocks of column tile 0
-// also store |x|^2 per token.
-// ---------------------------------------------------------------------------------------------
-struct BProjArgs {
-  const void* X;
-  long long x_ld;
-  int ntok, d, k, with_h;
-  const void* Vt;
-  const void* VDt;
-  float* nx2p;  // [ntok][kMaxProjChunks] (chunk 0 only)
-  void* Ghi;    // [ntok][k] high parts of g in the weight dtype
-  void* Glo;    // [ntok][k] low parts: g - Ghi rounded to the weight dtype
-  float* gq;    // [ntok][kMaxK / 16][2]
-};
-
-template <typename T>
-__device__ __forceinline__ float sumsq8(mu32x4 q) {
-  const T* e = reinterpret_cast<const T*>(&q);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = __builtin_fmaf(to_f32(e[i]), to_f32(e[i]), s);
-  return s;
-}
-
-template <typename T, int NW, int U>
-__global__ __launch_bounds__(64 * NW) void bproj_kernel(BProjArgs p) {
-  __shared__ float red[NW][2][256];
-  __shared__ float redx[NW][16];
-  const int c = blockIdx.x, tt = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tok = 16 * tt + (lane & 15);
-  const bool tok_ok = tok < p.ntok;
-  const T* xrow = reinterpret_cast<const T*>(p.X) + (long long)(tok_ok ? tok : 0) * p.x_ld;
-  const T* vrow = reinterpret_cast<const T*>(p.Vt) + (long long)(16 * c + (lane & 15)) * p.d;
-  const T* hrow = p.with_h ? reinterpret_cast<const T*>(p.VDt) + (long long)(16 * c + (lane & 15)) * p.d : vrow;
-  const int ko = 8 * (lane >> 4);
-  const bool want_x2 = c == 0;
-  const int nsub = p.d / 32;
-  // U sub-steps per batch, every load of a batch issued before any is used: a memory round trip
-  // costs microseconds under load, so the number of batches, not the bytes, sets the time
-  mf32x4 ag = mf32x4{0.f, 0.f, 0.f, 0.f}, ah = ag;
-  float sx = 0.f;
-  const mu32x4 zero = mu32x4{0u, 0u, 0u, 0u};
-  const int nb = (nsub + NW * U - 1) / (NW * U);
-  for (int b = 0; b < nb; ++b) {
-    mu32x4 x[U], v[U], h[U];
-    // batch b: sub-steps w + NW (U b + u); past the end a load reads sub-step 0 and is zeroed
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sub = w + NW * (U * b + u);
-      const bool in = sub < nsub;  // uniform in the wave
-      const int kk = (in ? 32 * sub : 0) + ko;
-      const mu32x4 xv = *reinterpret_cast<const mu32x4*>(xrow + kk);
-      const mu32x4 vv = *reinterpret_cast<const mu32x4*>(vrow + kk);
-      const mu32x4 hv = *reinterpret_cast<const mu32x4*>(hrow + kk);
-      x[u] = (in && tok_ok) ? xv : zero;
-      v[u] = in ? vv : zero;
-      h[u] = in ? hv : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ag = mfma_op<T>::run(x[u], v[u], ag);
-      if (p.with_h) ah = mfma_op<T>::run(x[u], h[u], ah);
-      if (want_x2) sx += sumsq8<T>(x[u]);
-    }
-  }
-  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold token l mod 16's four K groups
-  sx += __shfl_xor(sx, 16, 64);
-  sx += __shfl_xor(sx, 32, 64);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    red[w][0][r * 64 + lane] = ag[r];
-    red[w][1][r * 64 + lane] = ah[r];
-  }
-  if (lane < 16) redx[w][lane] = sx;
-  __syncthreads();
-  if (w != 0) return;
-  const int k = p.k;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float g = 0.f, h = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      g += red[ww][0][r * 64 + lane];
-      h += red[ww][1][r * 64 + lane];
-    }
-    // this lane: token 16 tt + 4 (lane / 16) + r, column 16 c + lane mod 16
-    const int t = 16 * tt + 4 * (lane >> 4) + r;
-    const bool ok = t < p.ntok;
-    if (ok) {
-      // g split once here for the fast product's matrix-core passes (|g - hi - lo| <= 2^-18 |g|
-      // for bf16)
-      const T hi = from_f32<T>(g);
-      const T lo = from_f32<T>(g - to_f32(hi));
-      reinterpret_cast<T*>(p.Ghi)[(long long)t * k + 16 * c + (lane & 15)] = hi;
-      reinterpret_cast<T*>(p.Glo)[(long long)t * k + 16 * c + (lane & 15)] = lo;
-    }
-    float gg = g * g, gh = g * h;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      gg += __shfl_xor(gg, o, 64);
-      gh += __shfl_xor(gh, o, 64);
-    }
-    if (ok && (lane & 15) == 0) {
-      p.gq[((long long)t * (kMaxK / 16) + c) * 2 + 0] = gg;
-      p.gq[((long long)t * (kMaxK / 16) + c) * 2 + 1] = gh;
-    }
-  }
-  if (want_x2 && lane < 16 && tok_ok) {
-    float v = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) v += redx[ww][lane];
-    p.nx2p[(long long)tok * kMaxProjChunks] = v;
-  }
-}
-
 // Cross-block hand-off inside one launch without cache flushes: partial sums are written with
 // device-scope stores (coherent across the XCDs' L2s), every wave waits until its stores have
 // completed, then one thread counts the block in; the block that counts last reads the partial
@@ -1997,6 +1909,118 @@ __device__ __forceinline__ bool arrive_last(int* cnt, int total, int* s_last) {
     *s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
   __syncthreads();
   return *s_last;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Batched path in two launches per site and chunk of at most 64 tokens (16-bit weights).
+//
+// bproj_kernel: [G | H] = X [V_k | V_k (V_k^T V_k - I)] on matrix cores, h = (V^T V - I) g being
+// the second half [GSI §2.2: the residual norm from g and the stored basis]. Block (b, z) streams
+// rows 32 b .. 32 b + 31 of V^T and of (V (V^T V - I))^T (the skinny tiles, x staged in LDS) over
+// K chunk z and stores the raw float32 sums for every token; blocks of tile 0 also store each
+// token's |x|^2 over the chunk. The last block of a tile to finish adds the chunks in chunk order,
+// stores g split into high and low parts in the weight dtype, and per token the tile's sums of
+// g^2 and g h.
+// ---------------------------------------------------------------------------------------------
+struct BProjArgs {
+  const void* X;
+  long long x_ld;
+  int ntok, d, k, with_h, kc;
+  const void* Vt;
+  const void* VDt;
+  float* Pp;    // [Zp][ntok][2 k]: tile b's 32 g then 32 h columns at 64 b
+  float* nx2p;  // [ntok][kMaxProjChunks]
+  void* Ghi;    // [ntok][k] high parts of g in the weight dtype
+  void* Glo;    // [ntok][k] low parts: g - Ghi rounded to the weight dtype
+  float* gq;    // [ntok][kMaxK / 16][2], tiles of 32 columns
+  int* cnt;     // [k / 32], zero between launches
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
+  __shared__ mu32x4 lds_a[4 * 8 * 64];
+  __shared__ int s_last;
+  const int b = blockIdx.x, z = blockIdx.z, nz = gridDim.z;
+  const int k2 = 2 * p.k;
+  const int kb = z * p.kc, ke = min(p.d, kb + p.kc);
+  float* pz = p.Pp + (long long)z * p.ntok * k2;
+  const T* x = reinterpret_cast<const T*>(p.X);
+  const T* vt = reinterpret_cast<const T*>(p.Vt);
+  const T* vd = p.with_h ? reinterpret_cast<const T*>(p.VDt) : vt;
+  float* x2 = b == 0 ? p.nx2p + z : nullptr;
+  mu32x4 b0[8], b1[8];
+  switch ((p.ntok + 15) >> 4) {  // uniform
+    case 1: skinny_staged_tiles<T, T, 1>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
+    case 2: skinny_staged_tiles<T, T, 2>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
+    case 3: skinny_staged_tiles<T, T, 3>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
+    default: skinny_staged_tiles<T, T, 4>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
+  }
+  if (!arrive_last(&p.cnt[b], nz, &s_last)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the tile's last block: thread (t, q) = (tid / 4, tid mod 4) takes columns 8 q .. 8 q + 7 of
+  // the tile's g and h for token t, summing the chunks in chunk order
+  const int t = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const bool ok = t < p.ntok;
+  float g[8], h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = h[e] = 0.f;
+  if (ok) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float4 v[kMaxProjChunks][2];
+#pragma unroll
+      for (int zz = 0; zz < kMaxProjChunks; ++zz) {
+        if (zz < nz) {
+          const float4* src = reinterpret_cast<const float4*>(p.Pp + ((long long)zz * p.ntok + t) * k2 + 64 * b +
+                                                              32 * half + 8 * q);
+          v[zz][0] = src[0];
+          v[zz][1] = src[1];
+        }
+      }
+      float* o = half ? h : g;
+#pragma unroll
+      for (int zz = 0; zz < kMaxProjChunks; ++zz) {
+        if (zz < nz) {
+          o[0] += v[zz][0].x; o[1] += v[zz][0].y; o[2] += v[zz][0].z; o[3] += v[zz][0].w;
+          o[4] += v[zz][1].x; o[5] += v[zz][1].y; o[6] += v[zz][1].z; o[7] += v[zz][1].w;
+        }
+      }
+    }
+  }
+  float gg = 0.f, gh = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    gg = __builtin_fmaf(g[e], g[e], gg);
+    gh = __builtin_fmaf(g[e], h[e], gh);
+  }
+  gg += __shfl_xor(gg, 1, 64);
+  gh += __shfl_xor(gh, 1, 64);
+  gg += __shfl_xor(gg, 2, 64);
+  gh += __shfl_xor(gh, 2, 64);
+  if (ok) {
+    // g split once here for the fast product's matrix-core passes (|g - hi - lo| <= 2^-18 |g|
+    // for bf16)
+    unsigned short hv[8], lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const T hi = from_f32<T>(g[e]);
+      const T lo = from_f32<T>(g[e] - to_f32(hi));
+      hv[e] = hi.b;
+      lv[e] = lo.b;
+    }
+    const long long off = (long long)t * p.k + 32 * b + 8 * q;
+    *reinterpret_cast<mu32x4*>(reinterpret_cast<T*>(p.Ghi) + off) =
+        mu32x4{hv[0] | ((unsigned)hv[1] << 16), hv[2] | ((unsigned)hv[3] << 16), hv[4] | ((unsigned)hv[5] << 16),
+               hv[6] | ((unsigned)hv[7] << 16)};
+    *reinterpret_cast<mu32x4*>(reinterpret_cast<T*>(p.Glo) + off) =
+        mu32x4{lv[0] | ((unsigned)lv[1] << 16), lv[2] | ((unsigned)lv[3] << 16), lv[4] | ((unsigned)lv[5] << 16),
+               lv[6] | ((unsigned)lv[7] << 16)};
+    if (q == 0) {
+      p.gq[((long long)t * (kMaxK / 16) + b) * 2 + 0] = gg;
+      p.gq[((long long)t * (kMaxK / 16) + b) * 2 + 1] = gh;
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&p.cnt[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2051,14 +2075,15 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
     if (t < p.ntok) {
       if (p.mode == kSiteGated) {
         // this token's pieces are contiguous: all loaded at once, then added in a fixed order
-        float4 xv[kMaxProjChunks / 4], qv[kMaxK / 32];
+        // tiles of 32 columns: k / 32 (g^2, g h) pairs
+        float4 xv[kMaxProjChunks / 4], qv[kMaxK / 64];
         const float4* xp = reinterpret_cast<const float4*>(p.nx2p + (long long)t * kMaxProjChunks);
         const float4* qp = reinterpret_cast<const float4*>(p.gq + (long long)t * (kMaxK / 16) * 2);
 #pragma unroll
         for (int i = 0; i < kMaxProjChunks / 4; ++i) xv[i] = xp[i];
 #pragma unroll
-        for (int i = 0; i < kMaxK / 32; ++i)
-          if (i < p.k / 32 + 1) qv[i] = qp[i];
+        for (int i = 0; i < kMaxK / 64; ++i)
+          if (i < (p.k / 32 + 1) / 2) qv[i] = qp[i];
         float nx2 = 0.f, gg = 0.f, q = 0.f;
 #pragma unroll
         for (int i = 0; i < kMaxProjChunks; ++i) {
@@ -2066,9 +2091,9 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
           if (i < p.zp) nx2 += v;
         }
 #pragma unroll
-        for (int c = 0; c < kMaxK / 16; ++c) {
+        for (int c = 0; c < kMaxK / 32; ++c) {
           const float4 v = qv[c / 2];
-          if (c < p.k / 16) {
+          if (c < p.k / 32) {
             gg += c % 2 == 0 ? v.x : v.z;
             q += c % 2 == 0 ? v.y : v.w;
           }
@@ -2161,11 +2186,22 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
 BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
   BatchedSplit sp{0, 0, 0, 0, 0};
   if (dtype == GSI_F32 || ntok < 1 || ntok > 64) return sp;
-  if (L.d % 32 != 0 || L.d_out % 64 != 0 || L.k % 16 != 0 || L.k > kMaxK) return sp;
+  if (L.d % 32 != 0 || L.d_out % 64 != 0 || L.k % 32 != 0 || L.k > kMaxK) return sp;
   if (kMaxK / 16 + L.d_out / 64 > kBatchedCounters) return sp;
   if (L.mode != kSiteDense && (L.k == 0 || !L.VDt)) return sp;
-  sp.zp = 1;  // the projection covers all of K in one block
-  sp.kc = L.d;
+  // projection: tiles of 32 columns (of g and of h), about 256 blocks, at most kMaxProjChunks
+  // chunks of K, every chunk non-empty
+  if (L.mode != kSiteDense) {
+    int zp = std::max(1, std::min(kMaxProjChunks, 256 / (L.k / 32)));
+    for (;; --zp) {
+      const int kc = ((L.d + zp - 1) / zp + 7) / 8 * 8;
+      if ((long long)(zp - 1) * kc < L.d || zp == 1) {
+        sp.zp = zp;
+        sp.kc = kc;
+        break;
+      }
+    }
+  }
   // products: about 256 to 512 blocks of 64 output rows, at most kMaxProdChunks chunks of K;
   // every chunk of K (of W and of M) non-empty
   const int nrt = L.d_out / 64;
@@ -2195,19 +2231,21 @@ int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, c
     a.d = L.d;
     a.k = L.k;
     a.with_h = L.mode == kSiteGated;
+    a.kc = sp.kc;
     a.Vt = L.Vt;
     a.VDt = L.VDt;
+    a.Pp = w.Pp;
     a.nx2p = w.nx2p;
     a.Ghi = w.G;  // the float32 G region holds both 16-bit halves
     a.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
     a.gq = w.gq;
-    dim3 grid(L.k / 16, (ntok + 15) / 16);
-    // 8 waves with 16 sub-steps each in one batch (d <= 4096), or 16 waves in batches of 8
-    const bool wide = L.d >= 8192;
-    void* fn = dtype == GSI_BF16 ? (wide ? (void*)bproj_kernel<bf16_t, 16, 8> : (void*)bproj_kernel<bf16_t, 8, 16>)
-                                 : (wide ? (void*)bproj_kernel<f16_t, 16, 8> : (void*)bproj_kernel<f16_t, 8, 16>);
-    void* args[] = {&a};
-    if (hipLaunchKernel(fn, grid, dim3(wide ? 1024 : 512), args, 0, s) != hipSuccess) return GSI_ERR_HIP;
+    a.cnt = w.cnt;
+    dim3 grid(L.k / 32, 1, sp.zp);
+    if (dtype == GSI_BF16)
+      bproj_kernel<bf16_t><<<grid, 256, 0, s>>>(a);
+    else
+      bproj_kernel<f16_t><<<grid, 256, 0, s>>>(a);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
   }
   BProdArgs b;
   b.X = X;
@@ -2222,7 +2260,7 @@ int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, c
   b.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
   b.gq = w.gq;
   b.nx2p = w.nx2p;
-  b.zp = 1;
+  b.zp = sp.zp;
   b.M = L.M;
   b.W = L.W;
   b.kcm = sp.kcm;

@@ -176,7 +176,8 @@ struct BatchedWs {
   float* part2;  // [kMaxSplit, T, d_out] split-K partial sums of the slow product
   long long part_elems;
   // two-launch path (chunks of at most 64 tokens)
-  float* gq;     // [64][kMaxK / 16][2] per token and column tile: sum g^2, sum g h
+  float* Pp;     // [kMaxProjChunks][64][2 k] projection chunk sums
+  float* gq;     // [64][kMaxK / 16][2] per token and 32-column tile: sum g^2, sum g h
   float* nx2p;   // [64][kMaxProjChunks] per token, chunk sums of |x|^2
   int* cnt;      // [kBatchedCounters] arrival counters (projection tiles, then row tiles), zero between launches
 };
