@@ -2047,7 +2047,8 @@ struct BProdArgs {
   const void* M;
   const void* W;
   int kcm, kcw;
-  float* Py;  // [Zy][ntok][d_out]
+  int zs;     // K chunks of the slow product (the last zs blocks in z); the first are the fast product's
+  float* Py;  // [zf + zs][ntok][d_out]
   int* cnt;   // [d_out / 64], zero between launches
   void* Y;
   long long y_ld;
@@ -2060,14 +2061,19 @@ template <typename T>
 __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
   __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[4 * 8 * 64];
   __shared__ int s_fast[64], s_slow[64];
+  __shared__ unsigned char s_isfast[64];
   __shared__ int s_n[2], s_last;
-  const int z = blockIdx.z, nz = gridDim.z;
-  // the slow product's first sub-chunk of W is requested before the gate is known: it
-  // arrives while the gate and the fast product run (a site with no slow token wastes it)
+  // blocks z < zf (dispatched first) take the fast product, blocks zf .. zf + zs - 1 chunk
+  // z - zf of the slow product; the two kinds run side by side
+  const int nz = gridDim.z, zf = nz - p.zs;
+  const bool slow_blk = (int)blockIdx.z >= zf;
+  const int z = slow_blk ? blockIdx.z - zf : blockIdx.z;
+  // a slow block requests its first sub-chunk of W before the gate is known: it arrives while the
+  // gate is formed (a site with no slow token wastes it)
   const T* wt = reinterpret_cast<const T*>(p.W);
   const int kbw = z * p.kcw, kew = min(p.d, kbw + p.kcw);
   mu32x4 wb0[8], wb1[8];  // wb1 is loaded by the slow pass itself (registers)
-  skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0);
+  if (slow_blk) skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0);
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
     bool fast = false;
@@ -2111,19 +2117,20 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
     const u64 below = t ? (~0ull >> (64 - t)) : 0ull;
     if (valid && fast) s_fast[__popcll(mf & below)] = t;
     if (valid && !fast) s_slow[__popcll(ms & below)] = t;
+    s_isfast[t] = fast ? 1 : 0;
     if (t == 0) {
       s_n[0] = __popcll(mf);
       s_n[1] = __popcll(ms);
     }
-    if (blockIdx.x == 0 && z == 0 && valid) {
+    if (blockIdx.x == 0 && blockIdx.z == nz - 1 && valid) {
       p.gate[(long long)t * p.gate_ld] = fast ? 0 : 1;
       if (p.rho) p.rho[(long long)t * p.gate_ld] = r;
     }
   }
   __syncthreads();
   const int nf = s_n[0], ns = s_n[1];
-  float* pz = p.Py + (long long)z * p.ntok * p.d_out;
-  if (nf > 0) {  // fast tokens: y = M g     [GSI §2.2]
+  float* pz = p.Py + (long long)blockIdx.z * p.ntok * p.d_out;
+  if (!slow_blk && nf > 0) {  // fast tokens: y = M g     [GSI §2.2]
     const int kb = z * p.kcm, ke = min(p.k, kb + p.kcm);
     const T* gh = reinterpret_cast<const T*>(p.Ghi);
     const T* gl = reinterpret_cast<const T*>(p.Glo);
@@ -2135,9 +2142,8 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
       default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
     }
   }
-  if (ns > 0) {  // slow tokens: y = W x     [GSI §2.2]
+  if (slow_blk && ns > 0) {  // slow tokens: y = W x     [GSI §2.2]
     const T* xa = reinterpret_cast<const T*>(p.X);
-    __syncthreads();  // the fast pass's staged tokens are no longer read
     switch ((ns + 15) >> 4) {
       case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
       case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
@@ -2147,20 +2153,22 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
   }
   if (!arrive_last(&p.cnt[blockIdx.x], nz, &s_last)) return;
   // the last block of the row tile: thread i takes rows 64 b + 4 (i mod 16) .. + 3 of tokens
-  // i / 16 + 16 s, summing the chunks in chunk order
+  // i / 16 + 16 s, summing the chunks of the token's own product in chunk order; one device-scope
+  // acquire, then ordinary 16-byte loads, all in flight at once
   const int row = blockIdx.x * 64 + 4 * (threadIdx.x & 15);
-  // the four tokens' chunk values all in flight at once, then added in chunk order
-  // one device-scope acquire, then ordinary 16-byte loads (fewer loads than device-scope 4-byte
-  // ones, all in flight at once)
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float4 pv[4][kMaxProdChunks];
+  int z0[4], zn[4];
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
     const int t = (threadIdx.x >> 4) + 16 * sg;
+    const bool f = t < p.ntok && s_isfast[t];
+    z0[sg] = f ? 0 : zf;
+    zn[sg] = f ? zf : p.zs;
 #pragma unroll
     for (int zz = 0; zz < kMaxProdChunks; ++zz)
-      if (zz < nz && t < p.ntok)
-        pv[sg][zz] = *reinterpret_cast<const float4*>(p.Py + ((long long)zz * p.ntok + t) * p.d_out + row);
+      if (zz < zn[sg] && t < p.ntok)
+        pv[sg][zz] = *reinterpret_cast<const float4*>(p.Py + ((long long)(z0[sg] + zz) * p.ntok + t) * p.d_out + row);
   }
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
@@ -2169,7 +2177,7 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
     float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int zz = 0; zz < kMaxProdChunks; ++zz) {
-      if (zz < nz) {
+      if (zz < zn[sg]) {
         a[0] += pv[sg][zz].x;
         a[1] += pv[sg][zz].y;
         a[2] += pv[sg][zz].z;
@@ -2184,7 +2192,7 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
 }
 
 BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
-  BatchedSplit sp{0, 0, 0, 0, 0};
+  BatchedSplit sp{0, 0, 0, 0, 0, 0};
   if (dtype == GSI_F32 || ntok < 1 || ntok > 64) return sp;
   if (L.d % 32 != 0 || L.d_out % 64 != 0 || L.k % 32 != 0 || L.k > kMaxK) return sp;
   if (kMaxK / 16 + L.d_out / 64 > kBatchedCounters) return sp;
@@ -2202,21 +2210,21 @@ BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
       }
     }
   }
-  // products: about 256 to 512 blocks of 64 output rows, at most kMaxProdChunks chunks of K;
-  // every chunk of K (of W and of M) non-empty
+  // products: the fast one in one block per row tile over all of M's K (a dense site has none),
+  // the slow one beside it in chunks of W's K (at most kMaxProdChunks, non-empty), about 512
+  // blocks of 64 output rows in all (two per CU)
   const int nrt = L.d_out / 64;
-  int zy = std::max(1, std::min(kMaxProdChunks, 512 / nrt));
+  sp.zf = L.mode == kSiteDense ? 0 : 1;
+  int zy = std::max(1, std::min(kMaxProdChunks, (512 - nrt * sp.zf) / nrt));
   for (;; --zy) {
     const int kcw = ((L.d + zy - 1) / zy + 7) / 8 * 8;
-    const int kcm = L.mode == kSiteDense ? 8 : ((L.k + zy - 1) / zy + 7) / 8 * 8;
-    const bool ok = (long long)(zy - 1) * kcw < L.d && (L.mode == kSiteDense || (long long)(zy - 1) * kcm < L.k);
-    if (ok || zy == 1) {
+    if ((long long)(zy - 1) * kcw < L.d || zy == 1) {
       sp.zy = zy;
       sp.kcw = kcw;
-      sp.kcm = kcm;
       break;
     }
   }
+  sp.kcm = L.mode == kSiteDense ? 8 : L.k;
   return sp;
 }
 
@@ -2265,6 +2273,7 @@ int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, c
   b.W = L.W;
   b.kcm = sp.kcm;
   b.kcw = sp.kcw;
+  b.zs = sp.zy;
   b.Py = w.part;
   b.cnt = w.cnt + kMaxK / 16;
   b.Y = Y;
@@ -2272,7 +2281,7 @@ int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, c
   b.gate = gate;
   b.gate_ld = gate_ld;
   b.rho = rho;
-  dim3 grid(L.d_out / 64, 1, sp.zy);
+  dim3 grid(L.d_out / 64, 1, sp.zy + sp.zf);
   if (dtype == GSI_BF16)
     bprod_kernel<bf16_t><<<grid, 256, 0, s>>>(b);
   else

@@ -187,7 +187,8 @@ constexpr int kBatchedCounters = 4096;  // arrival counters of the two-launch pa
 // K chunks of the two-launch batched path of one site (zp == 0 and zy == 0: not applicable)
 struct BatchedSplit {
   int zp, kc;         // projection: chunks of x's K and their width
-  int zy, kcw, kcm;   // products: chunks of K and their widths over W and over M
+  int zy, kcw, kcm;   // products: chunks of W's K (slow product) and their width; M's chunk width
+  int zf;             // chunks of M's K (fast product, one or none)
 };
 constexpr int kMaxSplit = 8;  // K chunks of a split product
 // partial-sum elements the batched path may use (none when every call runs one token)
