@@ -88,9 +88,11 @@ int gsi_device_check(void);
 
 /*
  * Bytes of per-layer derived data ("aux") that gsi_layer_create fills: V^T [k, d] in the weight
- * dtype, then V^T V - I [k, k] in float32, each 256-byte aligned, then the work split of the
- * batch-1 kernel (32 KiB). k = 0 gives the size for gsi_layer_create_dense (the work split only).
- * 0 for invalid arguments.
+ * dtype, then V^T V - I [k, k] in float32, then the work split of the batch-1 kernel (256 rows of
+ * 80 bytes), then, for 16-bit weights, (V (V^T V - I))^T [k, d] in the weight dtype (the rows
+ * whose products with x give h = (V^T V - I) g, the gate's second term [GSI §2.2], for the
+ * batched path), each part 256-byte aligned. k = 0 gives the size for gsi_layer_create_dense (the
+ * work split only). 0 for invalid arguments.
  */
 size_t gsi_layer_aux_bytes(int dtype, int d_out, int d, int k);
 
@@ -105,7 +107,9 @@ size_t gsi_layer_create_workspace_bytes(int dtype, int d_out, int d, int k);
 /*
  * Create a GSI layer [GSI §2.1]: enqueue on `stream` the precomputation of the cached low-rank
  * weight image M = W V (written to the caller's buffer M, [d_out, k], weight dtype, float32
- * accumulation, rounded to nearest even) and of aux (V^T and V^T V - I). Returns after enqueueing;
+ * accumulation, rounded to nearest even) and of aux (V^T, V^T V - I and, for 16-bit weights,
+ * (V (V^T V - I))^T from V^T V - I split into two parts of the weight dtype). Returns after
+ * enqueueing;
  * *out receives a small host handle that borrows W, M and aux (V is not used after the
  * precomputation has run). On error *out is left NULL.
  * ws / ws_bytes: optional device scratch (NULL, or at least gsi_layer_create_workspace_bytes;
