@@ -91,25 +91,68 @@ BatchedWs batched_part(void* ws, int k, int T, int d_out) {
   return batched_ws_carve((char*)ws + align256(decode_ws_bytes()), k, T, d_out);
 }
 
-// Batched path for one site over T tokens whose rows sit at X (+ row stride x_ld) and Y.
-// d_out_ws: the d_out the workspace was sized for (the largest of a stack)
+// Units of the two-launch batched path in flight on one stream: each unit's projection runs in
+// the same launch as the products of the unit before it. A unit's inputs are given when it is
+// enqueued and its projection reads nothing the earlier unit writes, so the two are independent;
+// the projection's latency is then spent while the earlier products stream their weights. The
+// two alternate between the workspace's two sets of projection buffers.
+class BatchedPipe {
+ public:
+  BatchedPipe(int dtype, const BatchedWs& w, hipStream_t s) : dtype_(dtype), w_(&w), s_(s) {}
+  int push(BatchedUnit u) {
+    u.w = w_;
+    u.set = set_;
+    set_ ^= 1;
+    const int rc = launch_batched_step(dtype_, &u, pending_ ? &prev_ : nullptr, s_);
+    prev_ = u;
+    pending_ = rc == GSI_OK;
+    return rc;
+  }
+  // the products of the last unit
+  int flush() {
+    if (!pending_) return GSI_OK;
+    pending_ = false;
+    return launch_batched_step(dtype_, nullptr, &prev_, s_);
+  }
+
+ private:
+  int dtype_;
+  const BatchedWs* w_;
+  hipStream_t s_;
+  bool pending_ = false;
+  BatchedUnit prev_{};
+  int set_ = 0;
+};
+
+// Batched path for one site over T tokens whose rows sit at X (+ row stride x_ld) and Y; w is the
+// batched part of the workspace, carved for the largest k and d_out of the call.
 int run_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps, void* Y,
-                long long y_ld, uint8_t* gate, int gate_ld, float* rho, void* ws, int d_out_ws, hipStream_t s) {
-  BatchedWs w = batched_part(ws, L.k, T, d_out_ws);
+                long long y_ld, uint8_t* gate, int gate_ld, float* rho, const BatchedWs& w, BatchedPipe& pipe,
+                hipStream_t s) {
   if (batched_split(dtype, L, std::min(T, 64)).zy > 0) {
-    // two launches per chunk of at most 64 tokens
+    // two launches per chunk of at most 64 tokens, overlapped with the units around it
     for (int t0 = 0; t0 < T; t0 += 64) {
-      const int n = std::min(64, T - t0);
-      const BatchedSplit sp = batched_split(dtype, L, n);
-      const int rc = launch_batched_site(dtype, L, sp, (const char*)X + (size_t)t0 * x_ld * dtype_size(dtype), x_ld,
-                                         n, eps, (char*)Y + (size_t)t0 * y_ld * dtype_size(dtype), y_ld,
-                                         gate + (size_t)t0 * gate_ld, gate_ld, rho ? rho + (size_t)t0 * gate_ld : nullptr,
-                                         w, s);
+      BatchedUnit u{};
+      u.L = &L;
+      u.ntok = std::min(64, T - t0);
+      u.sp = batched_split(dtype, L, u.ntok);
+      u.X = (const char*)X + (size_t)t0 * x_ld * dtype_size(dtype);
+      u.x_ld = x_ld;
+      u.eps = eps;
+      u.Y = (char*)Y + (size_t)t0 * y_ld * dtype_size(dtype);
+      u.y_ld = y_ld;
+      u.gate = gate + (size_t)t0 * gate_ld;
+      u.gate_ld = gate_ld;
+      u.rho = rho ? rho + (size_t)t0 * gate_ld : nullptr;
+      const int rc = pipe.push(u);
       if (rc != GSI_OK) return rc;
     }
     return GSI_OK;
   }
-  int rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
+  // the kernels below use the workspace's other regions: the units in flight finish first
+  int rc = pipe.flush();
+  if (rc != GSI_OK) return rc;
+  rc = launch_gate_batched(dtype, L, X, x_ld, T, eps, w, gate, gate_ld, rho, s);
   if (rc != GSI_OK) return rc;
   if (L.mode == kSiteDense)  // every token: y = W x
     return launch_gemm_nt_split(dtype, dtype, dtype, X, x_ld, w.slow_idx, L.W, L.d, Y, y_ld, w.slow_idx, T, L.d_out,
@@ -315,7 +358,10 @@ int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, ui
     a.xr = L->xr;
     return launch_decode(L->dtype, a, s);
   }
-  return run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, ws, L->d_out, s);
+  const BatchedWs w = batched_part(ws, L->k, T, L->d_out);
+  BatchedPipe pipe(L->dtype, w, s);
+  rc = run_batched(L->dtype, L->desc, x, L->d, T, eps, y, L->d_out, gate, 1, rho, w, pipe, s);
+  return rc != GSI_OK ? rc : pipe.flush();
 }
 
 int gsi_stack_create_modes(gsi_stack** out, gsi_layer* const* sites, const int* modes, int n_sites) {
@@ -449,6 +495,10 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
     return launch_decode(S->dtype, a, s);
   }
   const size_t es = dtype_size(S->dtype);
+  // one carving of the workspace for every site (k_max, d_out_max): units of different sites are
+  // in flight together
+  const BatchedWs w = batched_part(ws, S->k_max, T_step, S->d_out_max);
+  BatchedPipe pipe(S->dtype, w, s);
   for (int st = 0; st < n_steps; ++st) {
     const long long row0 = (long long)st * T_step;
     for (int i = 0; i < S->n_sites; ++i) {
@@ -457,11 +507,11 @@ int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float
       char* ys = (char*)Y + (size_t)(row0 * S->y_ld + L.y_off) * es;
       uint8_t* gs = gates + row0 * S->n_sites + i;
       float* rs = rho ? rho + row0 * S->n_sites + i : nullptr;
-      rc = run_batched(S->dtype, L, xs, S->x_ld, T_step, eps, ys, S->y_ld, gs, S->n_sites, rs, ws, S->d_out_max, s);
+      rc = run_batched(S->dtype, L, xs, S->x_ld, T_step, eps, ys, S->y_ld, gs, S->n_sites, rs, w, pipe, s);
       if (rc != GSI_OK) return rc;
     }
   }
-  return GSI_OK;
+  return pipe.flush();
 }
 
 int gsi_workspace_status(void* ws, size_t ws_nbytes, int* host_status, void* stream) {

@@ -274,15 +274,16 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(const void* __restric
 // before this one's products.
 // B steps of one 256-column sub-chunk for this lane (row nn of B, the lane's 8-element K groups);
 // steps outside [kb, ke) read column kb and are zeroed
-// With B2, column tile b of C takes its first 32 columns from rows 32 b .. of B and the next 32
-// from the same rows of B2 (waves 0-1 and 2-3).
+// bx: the block's column tile (columns 64 bx .. 64 bx + 63 of C). With B2, column tile bx takes
+// its first 32 columns from rows 32 bx .. of B and the next 32 from the same rows of B2 (waves 0-1
+// and 2-3).
 template <typename TB>
 __device__ __forceinline__ void skinny_load_b(const TB* __restrict__ B, long long ldb, int n, int kb, int ke, int k0,
-                                              mu32x4 (&bv)[8], const TB* __restrict__ B2 = nullptr) {
+                                              mu32x4 (&bv)[8], int bx, const TB* __restrict__ B2 = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nn = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const int nn = bx * 64 + wave * 16 + (lane & 15);
   const bool bok = nn < n;
-  const int brow_i = B2 ? blockIdx.x * 32 + (wave & 1) * 16 + (lane & 15) : nn;
+  const int brow_i = B2 ? bx * 32 + (wave & 1) * 16 + (lane & 15) : nn;
   if (B2 && wave >= 2) B = B2;
   const long long brow = bok ? (long long)brow_i * ldb : 0;
 #pragma unroll
@@ -301,8 +302,9 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
                                                     float* __restrict__ part, mu32x4* __restrict__ lds_hi,
                                                     mu32x4* __restrict__ lds_lo, const int* __restrict__ o_idx,
                                                     bool coherent, const TA* __restrict__ A_lo, mu32x4 (&pb0)[8],
-                                                    mu32x4 (&pb1)[8], const TB* __restrict__ B2 = nullptr,
+                                                    mu32x4 (&pb1)[8], int bx, const TB* __restrict__ B2 = nullptr,
                                                     float* __restrict__ x2out = nullptr) {
+  // bx: the block's column tile
   // B2: second row source (skinny_load_b); x2out (16-bit A): each A row's sum of squares over
   // [kb, ke) to x2out[row * kMaxProjChunks]
   // kPreB (16-bit A only): the caller has already loaded the first kPreB sub-chunks' B steps into
@@ -314,14 +316,13 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
   constexpr int kSteps = 8;  // 32-column steps per sub-chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int nn = blockIdx.x * 64 + wave * 16 + r16;
+  const int nn = bx * 64 + wave * 16 + r16;
   const bool bok = nn < n;
-  const long long brow = bok ? (long long)nn * ldb : 0;
   mf32x4 acc[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t] = mf32x4{0.f, 0.f, 0.f, 0.f};
   static_assert(kSteps == 8, "skinny_load_b loads eight steps");
-  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) { skinny_load_b(B, ldb, n, kb, ke, k0, bv, B2); };
+  auto load_b = [&](int k0, mu32x4 (&bv)[kSteps]) { skinny_load_b(B, ldb, n, kb, ke, k0, bv, bx, B2); };
   // A fragments of a sub-chunk: thread tid takes fragments f = tid + 256 i (i < 2 NRT); they are
   // loaded into registers one sub-chunk ahead and written to LDS (split, for a float32 A) at the
   // start of the sub-chunk that uses them
@@ -546,10 +547,10 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_staged_kernel(const void* 
   const TB* b = reinterpret_cast<const TB*>(B);
   mu32x4 b0[8], b1[8];  // loaded inside (no early B loads here)
   switch ((mv + 15) >> 4) {  // uniform
-    case 1: skinny_staged_tiles<TA, TB, 1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
-    case 2: skinny_staged_tiles<TA, TB, 2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
-    case 3: skinny_staged_tiles<TA, TB, 3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
-    default: skinny_staged_tiles<TA, TB, 4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1); break;
+    case 1: skinny_staged_tiles<TA, TB, 1>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1, blockIdx.x); break;
+    case 2: skinny_staged_tiles<TA, TB, 2>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1, blockIdx.x); break;
+    case 3: skinny_staged_tiles<TA, TB, 3>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1, blockIdx.x); break;
+    default: skinny_staged_tiles<TA, TB, 4>(a, lda, a_idx, b, ldb, mv, n, kb, ke, pz, lds_hi, lds_lo, nullptr, false, nullptr, b0, b1, blockIdx.x); break;
   }
 }
 
@@ -1821,7 +1822,7 @@ static size_t proj_bytes(int k, int T) {
 }
 size_t batched_ws_bytes(int k, int T, int d_out) {
   return kBatchedCounters * 4 + 2 * align256((size_t)T * k * 4) + align256((size_t)T * 4) * 3 + align256(2 * 4) +
-         2 * align256(split_part_elems(T, d_out) * 4) + proj_bytes(k, T);
+         2 * align256(split_part_elems(T, d_out) * 4) + 2 * proj_bytes(k, T);
 }
 BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   char* p = (char*)base;
@@ -1842,9 +1843,11 @@ BatchedWs batched_ws_carve(void* base, int k, int T, int d_out) {
   w.part2 = w.part_elems ? (float*)p : nullptr;
   p += align256(w.part_elems * 4);
   const size_t t = (size_t)std::min(T, 64);
-  w.Pp = (float*)p; p += align256((size_t)kMaxProjChunks * t * 2 * k * 4);
-  w.gq = (float*)p; p += align256((size_t)(kMaxK / 16) * t * 2 * 4);
-  w.nx2p = (float*)p;
+  for (int set = 0; set < 2; ++set) {
+    w.Pp[set] = (float*)p; p += align256((size_t)kMaxProjChunks * t * 2 * k * 4);
+    w.gq[set] = (float*)p; p += align256((size_t)(kMaxK / 16) * t * 2 * 4);
+    w.nx2p[set] = (float*)p; p += align256((size_t)kMaxProjChunks * t * 4);
+  }
   return w;
 }
 
@@ -1936,11 +1939,9 @@ struct BProjArgs {
   int* cnt;     // [k / 32], zero between launches
 };
 
+// one block of the projection: column tile b, K chunk z of nz (lds_a: 32 KB)
 template <typename T>
-__global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
-  __shared__ mu32x4 lds_a[4 * 8 * 64];
-  __shared__ int s_last;
-  const int b = blockIdx.x, z = blockIdx.z, nz = gridDim.z;
+__device__ __forceinline__ void bproj_block(const BProjArgs& p, int b, int z, int nz, mu32x4* lds_a, int& s_last) {
   const int k2 = 2 * p.k;
   const int kb = z * p.kc, ke = min(p.d, kb + p.kc);
   float* pz = p.Pp + (long long)z * p.ntok * k2;
@@ -1950,10 +1951,10 @@ __global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
   float* x2 = b == 0 ? p.nx2p + z : nullptr;
   mu32x4 b0[8], b1[8];
   switch ((p.ntok + 15) >> 4) {  // uniform
-    case 1: skinny_staged_tiles<T, T, 1>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
-    case 2: skinny_staged_tiles<T, T, 2>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
-    case 3: skinny_staged_tiles<T, T, 3>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
-    default: skinny_staged_tiles<T, T, 4>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, vd, x2); break;
+    case 1: skinny_staged_tiles<T, T, 1>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, b, vd, x2); break;
+    case 2: skinny_staged_tiles<T, T, 2>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, b, vd, x2); break;
+    case 3: skinny_staged_tiles<T, T, 3>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, b, vd, x2); break;
+    default: skinny_staged_tiles<T, T, 4>(x, p.x_ld, nullptr, vt, p.d, p.ntok, k2, kb, ke, pz, lds_a, lds_a, nullptr, true, nullptr, b0, b1, b, vd, x2); break;
   }
   if (!arrive_last(&p.cnt[b], nz, &s_last)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -2023,6 +2024,13 @@ __global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
   if (threadIdx.x == 0) __hip_atomic_store(&p.cnt[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
+  __shared__ mu32x4 lds_a[4 * 8 * 64];
+  __shared__ int s_last;
+  bproj_block<T>(p, blockIdx.x, blockIdx.z, gridDim.z, lds_a, s_last);
+}
+
 // ---------------------------------------------------------------------------------------------
 // bprod_kernel: gate and both products of one site for the chunk's tokens. Every block first
 // forms the gate of every token from the projection's pieces, in one fixed order (nr2 =
@@ -2057,23 +2065,34 @@ struct BProdArgs {
   float* rho;
 };
 
+// LDS of a products block
+struct BProdLds {
+  mu32x4 hi[4 * 8 * 64], lo[4 * 8 * 64];  // staged A fragments (high and low parts), 64 KB
+  int fast[64], slow[64];                 // token lists
+  unsigned char isfast[64];
+  int n[2], last;
+};
+
+// one block of the products: row tile bx, block bz of nz (the first zf take the fast product)
 template <typename T>
-__global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
-  __shared__ mu32x4 lds_hi[4 * 8 * 64], lds_lo[4 * 8 * 64];
-  __shared__ int s_fast[64], s_slow[64];
-  __shared__ unsigned char s_isfast[64];
-  __shared__ int s_n[2], s_last;
+__device__ __forceinline__ void bprod_block(const BProdArgs& p, int bx, int bz, int nz, BProdLds& L) {
+  mu32x4* lds_hi = L.hi;
+  mu32x4* lds_lo = L.lo;
+  int* s_fast = L.fast;
+  int* s_slow = L.slow;
+  unsigned char* s_isfast = L.isfast;
+  int* s_n = L.n;
   // blocks z < zf (dispatched first) take the fast product, blocks zf .. zf + zs - 1 chunk
   // z - zf of the slow product; the two kinds run side by side
-  const int nz = gridDim.z, zf = nz - p.zs;
-  const bool slow_blk = (int)blockIdx.z >= zf;
-  const int z = slow_blk ? blockIdx.z - zf : blockIdx.z;
+  const int zf = nz - p.zs;
+  const bool slow_blk = bz >= zf;
+  const int z = slow_blk ? bz - zf : bz;
   // a slow block requests its first sub-chunk of W before the gate is known: it arrives while the
   // gate is formed (a site with no slow token wastes it)
   const T* wt = reinterpret_cast<const T*>(p.W);
   const int kbw = z * p.kcw, kew = min(p.d, kbw + p.kcw);
   mu32x4 wb0[8], wb1[8];  // wb1 is loaded by the slow pass itself (registers)
-  if (slow_blk) skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0);
+  if (slow_blk) skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0, bx);
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
     bool fast = false;
@@ -2122,40 +2141,40 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
       s_n[0] = __popcll(mf);
       s_n[1] = __popcll(ms);
     }
-    if (blockIdx.x == 0 && blockIdx.z == nz - 1 && valid) {
+    if (bx == 0 && bz == nz - 1 && valid) {
       p.gate[(long long)t * p.gate_ld] = fast ? 0 : 1;
       if (p.rho) p.rho[(long long)t * p.gate_ld] = r;
     }
   }
   __syncthreads();
   const int nf = s_n[0], ns = s_n[1];
-  float* pz = p.Py + (long long)blockIdx.z * p.ntok * p.d_out;
+  float* pz = p.Py + (long long)bz * p.ntok * p.d_out;
   if (!slow_blk && nf > 0) {  // fast tokens: y = M g     [GSI §2.2]
     const int kb = z * p.kcm, ke = min(p.k, kb + p.kcm);
     const T* gh = reinterpret_cast<const T*>(p.Ghi);
     const T* gl = reinterpret_cast<const T*>(p.Glo);
     const T* m = reinterpret_cast<const T*>(p.M);
     switch ((nf + 15) >> 4) {
-      case 1: skinny_staged_tiles<T, T, 1, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
-      case 2: skinny_staged_tiles<T, T, 2, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
-      case 3: skinny_staged_tiles<T, T, 3, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
-      default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1); break;
+      case 1: skinny_staged_tiles<T, T, 1, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
+      case 2: skinny_staged_tiles<T, T, 2, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
+      case 3: skinny_staged_tiles<T, T, 3, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
+      default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
     }
   }
   if (slow_blk && ns > 0) {  // slow tokens: y = W x     [GSI §2.2]
     const T* xa = reinterpret_cast<const T*>(p.X);
     switch ((ns + 15) >> 4) {
-      case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
-      case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
-      case 3: skinny_staged_tiles<T, T, 3, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
-      default: skinny_staged_tiles<T, T, 4, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1); break;
+      case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
+      case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
+      case 3: skinny_staged_tiles<T, T, 3, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
+      default: skinny_staged_tiles<T, T, 4, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
     }
   }
-  if (!arrive_last(&p.cnt[blockIdx.x], nz, &s_last)) return;
+  if (!arrive_last(&p.cnt[bx], nz, &L.last)) return;
   // the last block of the row tile: thread i takes rows 64 b + 4 (i mod 16) .. + 3 of tokens
   // i / 16 + 16 s, summing the chunks of the token's own product in chunk order; one device-scope
   // acquire, then ordinary 16-byte loads, all in flight at once
-  const int row = blockIdx.x * 64 + 4 * (threadIdx.x & 15);
+  const int row = bx * 64 + 4 * (threadIdx.x & 15);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float4 pv[4][kMaxProdChunks];
   int z0[4], zn[4];
@@ -2188,7 +2207,36 @@ __global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) yr[e] = from_f32<T>(a[e]);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&p.cnt[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(&p.cnt[bx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bprod_kernel(BProdArgs p) {
+  __shared__ BProdLds lds;
+  bprod_block<T>(p, blockIdx.x, blockIdx.z, gridDim.z, lds);
+}
+
+// One launch of the pipelined stack: the projection of one unit (np_x column tiles x np_z K
+// chunks) beside the products of the unit before it (nq_x row tiles x nq_z blocks, the first zf
+// of a row tile the fast product's). Dispatch order: the slow product's blocks (the longest:
+// they stream W), then the projection's, then the fast product's. The two units share no
+// buffer: the projection writes one set of g, gate pieces and chunk sums while the products read
+// the other set, written by the previous launch.
+template <typename T>
+__global__ __launch_bounds__(256) void bstep_kernel(BProjArgs pa, int np_x, int np_z, BProdArgs pb, int nq_x,
+                                                    int nq_z) {
+  __shared__ BProdLds lds;
+  const int np = np_x * np_z, zf = nq_z - pb.zs, nslow = nq_x * pb.zs;
+  int i = blockIdx.x;
+  if (i < nslow) {
+    bprod_block<T>(pb, i % nq_x, zf + i / nq_x, nq_z, lds);
+    return;
+  }
+  i -= nslow;
+  if (i < np)
+    bproj_block<T>(pa, i % np_x, i / np_x, np_z, lds.hi, lds.last);
+  else
+    bprod_block<T>(pb, (i - np) % nq_x, (i - np) / nq_x, nq_z, lds);
 }
 
 BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
@@ -2228,64 +2276,90 @@ BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
   return sp;
 }
 
-int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, const void* X, long long x_ld,
-                        int ntok, float eps, void* Y, long long y_ld, uint8_t* gate, int gate_ld, float* rho,
-                        const BatchedWs& w, hipStream_t s) {
-  if (L.mode != kSiteDense) {
-    BProjArgs a;
-    a.X = X;
-    a.x_ld = x_ld;
-    a.ntok = ntok;
-    a.d = L.d;
-    a.k = L.k;
-    a.with_h = L.mode == kSiteGated;
-    a.kc = sp.kc;
-    a.Vt = L.Vt;
-    a.VDt = L.VDt;
-    a.Pp = w.Pp;
-    a.nx2p = w.nx2p;
-    a.Ghi = w.G;  // the float32 G region holds both 16-bit halves
-    a.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
-    a.gq = w.gq;
-    a.cnt = w.cnt;
-    dim3 grid(L.k / 32, 1, sp.zp);
-    if (dtype == GSI_BF16)
-      bproj_kernel<bf16_t><<<grid, 256, 0, s>>>(a);
-    else
-      bproj_kernel<f16_t><<<grid, 256, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
-  }
+// the projection's and the products' arguments of one unit; g of the unit's buffer set sits in
+// the G (set 0) or H (set 1) region as its two 16-bit halves
+static void unit_g(const BatchedUnit& u, void** hi, void** lo) {
+  char* g = (char*)(u.set ? u.w->H : u.w->G);
+  *hi = g;
+  *lo = g + (size_t)u.ntok * u.L->k * 2;
+}
+
+static BProjArgs proj_args(const BatchedUnit& u) {
+  BProjArgs a;
+  a.X = u.X;
+  a.x_ld = u.x_ld;
+  a.ntok = u.ntok;
+  a.d = u.L->d;
+  a.k = u.L->k;
+  a.with_h = u.L->mode == kSiteGated;
+  a.kc = u.sp.kc;
+  a.Vt = u.L->Vt;
+  a.VDt = u.L->VDt;
+  a.Pp = u.w->Pp[u.set];
+  a.nx2p = u.w->nx2p[u.set];
+  unit_g(u, &a.Ghi, &a.Glo);
+  a.gq = u.w->gq[u.set];
+  a.cnt = u.w->cnt;
+  return a;
+}
+
+static BProdArgs prod_args(const BatchedUnit& u) {
   BProdArgs b;
-  b.X = X;
-  b.x_ld = x_ld;
-  b.ntok = ntok;
-  b.d = L.d;
-  b.d_out = L.d_out;
-  b.k = L.k;
-  b.mode = L.mode;
-  b.eps = eps;
-  b.Ghi = w.G;
-  b.Glo = (char*)w.G + (size_t)ntok * L.k * 2;
-  b.gq = w.gq;
-  b.nx2p = w.nx2p;
-  b.zp = sp.zp;
-  b.M = L.M;
-  b.W = L.W;
-  b.kcm = sp.kcm;
-  b.kcw = sp.kcw;
-  b.zs = sp.zy;
-  b.Py = w.part;
-  b.cnt = w.cnt + kMaxK / 16;
-  b.Y = Y;
-  b.y_ld = y_ld;
-  b.gate = gate;
-  b.gate_ld = gate_ld;
-  b.rho = rho;
-  dim3 grid(L.d_out / 64, 1, sp.zy + sp.zf);
-  if (dtype == GSI_BF16)
-    bprod_kernel<bf16_t><<<grid, 256, 0, s>>>(b);
-  else
-    bprod_kernel<f16_t><<<grid, 256, 0, s>>>(b);
+  b.X = u.X;
+  b.x_ld = u.x_ld;
+  b.ntok = u.ntok;
+  b.d = u.L->d;
+  b.d_out = u.L->d_out;
+  b.k = u.L->k;
+  b.mode = u.L->mode;
+  b.eps = u.eps;
+  void *hi, *lo;
+  unit_g(u, &hi, &lo);
+  b.Ghi = hi;
+  b.Glo = lo;
+  b.gq = u.w->gq[u.set];
+  b.nx2p = u.w->nx2p[u.set];
+  b.zp = u.sp.zp;
+  b.M = u.L->M;
+  b.W = u.L->W;
+  b.kcm = u.sp.kcm;
+  b.kcw = u.sp.kcw;
+  b.zs = u.sp.zy;
+  b.Py = u.w->part;
+  b.cnt = u.w->cnt + kMaxK / 16;
+  b.Y = u.Y;
+  b.y_ld = u.y_ld;
+  b.gate = u.gate;
+  b.gate_ld = u.gate_ld;
+  b.rho = u.rho;
+  return b;
+}
+
+int launch_batched_step(int dtype, const BatchedUnit* proj, const BatchedUnit* prod, hipStream_t s) {
+  if (proj && proj->L->mode == kSiteDense) proj = nullptr;  // a dense site has no projection
+  if (proj && prod && proj->set == prod->set) return GSI_ERR_SHAPE;
+  const bool bf = dtype == GSI_BF16;
+  if (proj && !prod) {
+    const dim3 grid(proj->L->k / 32, 1, proj->sp.zp);
+    if (bf)
+      bproj_kernel<bf16_t><<<grid, 256, 0, s>>>(proj_args(*proj));
+    else
+      bproj_kernel<f16_t><<<grid, 256, 0, s>>>(proj_args(*proj));
+  } else if (prod && !proj) {
+    const dim3 grid(prod->L->d_out / 64, 1, prod->sp.zy + prod->sp.zf);
+    if (bf)
+      bprod_kernel<bf16_t><<<grid, 256, 0, s>>>(prod_args(*prod));
+    else
+      bprod_kernel<f16_t><<<grid, 256, 0, s>>>(prod_args(*prod));
+  } else if (proj && prod) {
+    const int np_x = proj->L->k / 32, np_z = proj->sp.zp;
+    const int nq_x = prod->L->d_out / 64, nq_z = prod->sp.zy + prod->sp.zf;
+    const unsigned nb = (unsigned)(np_x * np_z + nq_x * nq_z);
+    if (bf)
+      bstep_kernel<bf16_t><<<nb, 256, 0, s>>>(proj_args(*proj), np_x, np_z, prod_args(*prod), nq_x, nq_z);
+    else
+      bstep_kernel<f16_t><<<nb, 256, 0, s>>>(proj_args(*proj), np_x, np_z, prod_args(*prod), nq_x, nq_z);
+  }
   return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 

@@ -175,11 +175,12 @@ struct BatchedWs {
   float* part;   // [kMaxSplit, T, d_out] split-K partial sums of the fast product (and the projection)
   float* part2;  // [kMaxSplit, T, d_out] split-K partial sums of the slow product
   long long part_elems;
-  // two-launch path (chunks of at most 64 tokens)
-  float* Pp;     // [kMaxProjChunks][64][2 k] projection chunk sums
-  float* gq;     // [64][kMaxK / 16][2] per token and 32-column tile: sum g^2, sum g h
-  float* nx2p;   // [64][kMaxProjChunks] per token, chunk sums of |x|^2
-  int* cnt;      // [kBatchedCounters] arrival counters (projection tiles, then row tiles), zero between launches
+  // two-launch path (chunks of at most 64 tokens), two sets of the projection's outputs: one
+  // launch writes one set while the products of the same launch read the other
+  float* Pp[2];    // [kMaxProjChunks][64][2 k] projection chunk sums
+  float* gq[2];    // [64][kMaxK / 16][2] per token and 32-column tile: sum g^2, sum g h
+  float* nx2p[2];  // [64][kMaxProjChunks] per token, chunk sums of |x|^2
+  int* cnt;        // [kBatchedCounters] arrival counters (projection tiles, then row tiles), zero between launches
 };
 constexpr int kMaxProjChunks = 16;
 constexpr int kMaxProdChunks = 4;  // K chunks of the two-launch path's products
@@ -209,9 +210,25 @@ int launch_reduce2(int c_type, const float* pa, int sa, const int* ca, const int
 int launch_gate_batched(int dtype, const LayerDesc& L, const void* X, long long x_ld, int T, float eps,
                         const BatchedWs& w, uint8_t* gate, int gate_ld, float* rho, hipStream_t s);
 BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok);
-// projection (with the gate pieces) and products of one site over ntok <= 64 tokens
-int launch_batched_site(int dtype, const LayerDesc& L, const BatchedSplit& sp, const void* X, long long x_ld,
-                        int ntok, float eps, void* Y, long long y_ld, uint8_t* gate, int gate_ld, float* rho,
-                        const BatchedWs& w, hipStream_t s);
+// One site over ntok <= 64 tokens on the two-launch path: its projection (g split in two 16-bit
+// halves, the gate pieces) writes buffer set `set`, which its products read.
+struct BatchedUnit {
+  const LayerDesc* L;
+  BatchedSplit sp;
+  const void* X;
+  long long x_ld;
+  int ntok;
+  float eps;
+  void* Y;
+  long long y_ld;
+  uint8_t* gate;
+  int gate_ld;
+  float* rho;
+  const BatchedWs* w;
+  int set;  // 0 or 1
+};
+// One launch: the projection of `proj` and the products of `prod` (either may be null; a dense
+// site's projection is skipped); the two must use different buffer sets.
+int launch_batched_step(int dtype, const BatchedUnit* proj, const BatchedUnit* prod, hipStream_t s);
 
 }  // namespace gsi
