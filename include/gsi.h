@@ -137,10 +137,13 @@ size_t gsi_workspace_bytes(int dtype, int d_out, int d, int k, int T_max);
 /*
  * Run one GSI layer over T tokens [GSI §2.1-§2.2]: y[t] = M g_t if rho_t < eps else W x_t,
  * gate[t] = 0 (fast) or 1 (slow), rho[t] if rho != NULL. T = 0 returns GSI_OK with nothing
- * enqueued. T < 16 runs the per-token persistent path; T >= 16 the batched path (projection,
- * device-side gate with fast/slow token compaction, then the two products), with no host
- * synchronisation in either. The workspace must be zero-filled before its first use and is
- * kept consistent by the library afterwards.
+ * enqueued. T < 16 runs the per-token persistent path; T >= 16 the batched path in chunks of at
+ * most 64 tokens (16-bit weights: a projection, then one launch that forms every gate and lists
+ * the fast and slow tokens on the device and runs the two products, the next chunk's projection
+ * beside them; float32 weights: projection, gate, compaction and products in their own
+ * launches), with no host synchronisation in either. x must not overlap y, gate or rho. The
+ * workspace must be zero-filled before its first use and is kept consistent by the library
+ * afterwards.
  */
 int gsi_forward(const gsi_layer* L, const void* x, int T, float eps, void* y, uint8_t* gate, float* rho,
                 void* ws, size_t ws_bytes, void* stream);
@@ -169,12 +172,15 @@ size_t gsi_stack_workspace_bytes(const gsi_stack* S, int T_step);
  *   Y     [n_steps * T_step, sum_s d_out_s]  same stacking for the outputs
  *   gates [n_steps * T_step, n_sites] uint8  (1 = slow)
  *   rho   [n_steps * T_step, n_sites] float32, optional (NULL)
- * Sites run in order within a step and steps run in order; each site starts after the previous
- * site's output and gate are complete. Site inputs are read from X (they are not chained from
- * the previous site's output). T_step < 16 runs one persistent kernel for the whole call, one
- * token at a time (inside a step: each site for each of the step's tokens in turn) on the vector
- * ALU; n_steps * T_step * n_sites must then be below 2^28 (GSI_ERR_SHAPE). T_step >= 16 runs the
- * batched path per (step, site), whose products use the matrix cores.
+ * Sites run in order within a step and steps run in order. Site inputs are read from X (they are
+ * not chained from the previous site's output), so a site's input may be read before the
+ * previous site's output is complete; X must not overlap Y, gates or rho. T_step < 16 runs one
+ * persistent kernel for the whole call, one token at a time (inside a step: each site for each of
+ * the step's tokens in turn) on the vector ALU; n_steps * T_step * n_sites must then be below
+ * 2^28 (GSI_ERR_SHAPE). T_step >= 16 runs the batched path per (step, site) in chunks of at most
+ * 64 tokens, whose products use the matrix cores; a chunk's projection (g, ||x||^2 and the gate
+ * pieces, from X and the site's basis only) runs in the same launch as the previous chunk's
+ * products, and its gate and products start after those products are complete.
  */
 int gsi_stack_decode(gsi_stack* S, const void* X, int n_steps, int T_step, float eps, void* Y, uint8_t* gates,
                      float* rho, void* ws, size_t ws_bytes, void* stream);
