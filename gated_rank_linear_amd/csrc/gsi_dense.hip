@@ -303,8 +303,10 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
                                                     mu32x4* __restrict__ lds_lo, const int* __restrict__ o_idx,
                                                     bool coherent, const TA* __restrict__ A_lo, mu32x4 (&pb0)[8],
                                                     mu32x4 (&pb1)[8], int bx, const TB* __restrict__ B2 = nullptr,
-                                                    float* __restrict__ x2out = nullptr) {
-  // bx: the block's column tile
+                                                    float* __restrict__ x2out = nullptr, TB* __restrict__ yout = nullptr,
+                                                    long long y_ld = 0) {
+  // bx: the block's column tile; yout: the sums are complete (one K chunk) and go straight to
+  // yout[row][nn] rounded to TB instead of to part
   // B2: second row source (skinny_load_b); x2out (16-bit A): each A row's sum of squares over
   // [kb, ke) to x2out[row * kMaxProjChunks]
   // kPreB (16-bit A only): the caller has already loaded the first kPreB sub-chunks' B steps into
@@ -514,7 +516,9 @@ __device__ __forceinline__ void skinny_staged_tiles(const TA* __restrict__ A, lo
     for (int r = 0; r < 4; ++r) {
       if (orow[t][r] >= 0 && bok) {
         float* q = part + (long long)orow[t][r] * n + nn;
-        if (coherent)  // read by another block of the same launch
+        if (yout)  // uniform
+          yout[(long long)orow[t][r] * y_ld + nn] = from_f32<TB>(acc[t][r]);
+        else if (coherent)  // read by another block of the same launch
           __hip_atomic_store(q, acc[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
           *q = acc[t][r];
@@ -2035,11 +2039,14 @@ __global__ __launch_bounds__(256) void bproj_kernel(BProjArgs p) {
 // bprod_kernel: gate and both products of one site for the chunk's tokens. Every block first
 // forms the gate of every token from the projection's pieces, in one fixed order (nr2 =
 // (|x|^2 - |g|^2) + g^T h, fast iff nr2 < fl(eps^2) |x|^2 [GSI §2.2]), so all blocks agree, and
-// lists the fast and slow tokens in token order in LDS; block (0, 0) stores the gate bits and
-// rho. Block (b, z) then owns output rows 64 b .. 64 b + 63 and K chunk z: y = M g over the fast
-// tokens (g as its two 16-bit parts, two matrix-core passes; K columns of M in [z kcm, ..)) and y = W x over the slow tokens (K columns of W in
-// [z kcw, ..)), both on the staged skinny tiles, raw float32 sums to Py[z][t][row]. The last
-// block of a row tile adds the chunks in chunk order and stores y rows in the weight dtype.
+// lists the fast and slow tokens in token order in LDS; block (0, nz - 1) stores the gate bits
+// and rho. Block (b, z) then owns output rows 64 b .. 64 b + 63: the first zf blocks of a row tile
+// (zf = 1, none on a dense site) compute y = M g over the fast tokens and all of M's K (g as its
+// two 16-bit parts, two matrix-core passes), the other zs blocks y = W x over the slow tokens and
+// chunk z - zf of W's K, both on the staged skinny tiles. A product that one block computes whole
+// (M g; W x when W's K is one chunk) is rounded and stored as y rows by that block; a slow product
+// split over K leaves raw float32 sums in Py[chunk][t][row], which the last slow block of the row
+// tile adds in chunk order.
 // A static-projection site lists every token as fast, a dense site every token as slow.
 // ---------------------------------------------------------------------------------------------
 struct BProdArgs {
@@ -2088,11 +2095,11 @@ __device__ __forceinline__ void bprod_block(const BProdArgs& p, int bx, int bz, 
   const bool slow_blk = bz >= zf;
   const int z = slow_blk ? bz - zf : bz;
   // a slow block requests its first sub-chunk of W before the gate is known: it arrives while the
-  // gate is formed (a site with no slow token wastes it)
+  // gate is formed (a gated site with no slow token wastes it)
   const T* wt = reinterpret_cast<const T*>(p.W);
   const int kbw = z * p.kcw, kew = min(p.d, kbw + p.kcw);
   mu32x4 wb0[8], wb1[8];  // wb1 is loaded by the slow pass itself (registers)
-  if (slow_blk) skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0, bx);
+  if (slow_blk && p.mode != kSiteStatic) skinny_load_b(wt, p.d, p.d_out, kbw, kew, kbw, wb0, bx);
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
     bool fast = false;
@@ -2148,55 +2155,62 @@ __device__ __forceinline__ void bprod_block(const BProdArgs& p, int bx, int bz, 
   }
   __syncthreads();
   const int nf = s_n[0], ns = s_n[1];
-  float* pz = p.Py + (long long)bz * p.ntok * p.d_out;
+  // a token whose product one block computes whole (every fast token; the slow tokens when W's K
+  // is one chunk) gets its y row straight from that block; only a slow product split over K
+  // leaves partial sums for the last block of the row tile. ns is the same in every block.
+  if (slow_blk && ns == 0) {
+    dwait_vmcnt<0>();  // the early W loads have landed
+    return;
+  }
+  const bool direct = !slow_blk || p.zs == 1;
+  T* yd = direct ? reinterpret_cast<T*>(p.Y) : nullptr;
+  float* pz = p.Py + (long long)z * p.ntok * p.d_out;
   if (!slow_blk && nf > 0) {  // fast tokens: y = M g     [GSI §2.2]
     const int kb = z * p.kcm, ke = min(p.k, kb + p.kcm);
     const T* gh = reinterpret_cast<const T*>(p.Ghi);
     const T* gl = reinterpret_cast<const T*>(p.Glo);
     const T* m = reinterpret_cast<const T*>(p.M);
     switch ((nf + 15) >> 4) {
-      case 1: skinny_staged_tiles<T, T, 1, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
-      case 2: skinny_staged_tiles<T, T, 2, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
-      case 3: skinny_staged_tiles<T, T, 3, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
-      default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx); break;
+      case 1: skinny_staged_tiles<T, T, 1, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      case 2: skinny_staged_tiles<T, T, 2, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      case 3: skinny_staged_tiles<T, T, 3, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      default: skinny_staged_tiles<T, T, 4, true>(gh, p.k, s_fast, m, p.k, nf, p.d_out, kb, ke, pz, lds_hi, lds_lo, s_fast, true, gl, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
     }
   }
   if (slow_blk && ns > 0) {  // slow tokens: y = W x     [GSI §2.2]
     const T* xa = reinterpret_cast<const T*>(p.X);
     switch ((ns + 15) >> 4) {
-      case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
-      case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
-      case 3: skinny_staged_tiles<T, T, 3, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
-      default: skinny_staged_tiles<T, T, 4, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx); break;
+      case 1: skinny_staged_tiles<T, T, 1, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      case 2: skinny_staged_tiles<T, T, 2, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      case 3: skinny_staged_tiles<T, T, 3, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
+      default: skinny_staged_tiles<T, T, 4, false, 1>(xa, p.x_ld, s_slow, wt, p.d, ns, p.d_out, kbw, kew, pz, lds_hi, lds_lo, s_slow, true, nullptr, wb0, wb1, bx, nullptr, nullptr, yd, p.y_ld); break;
     }
   }
-  if (!arrive_last(&p.cnt[bx], nz, &L.last)) return;
-  // the last block of the row tile: thread i takes rows 64 b + 4 (i mod 16) .. + 3 of tokens
-  // i / 16 + 16 s, summing the chunks of the token's own product in chunk order; one device-scope
-  // acquire, then ordinary 16-byte loads, all in flight at once
+  if (direct || !arrive_last(&p.cnt[bx], p.zs, &L.last)) return;
+  // the last slow block of the row tile: thread i takes rows 64 b + 4 (i mod 16) .. + 3 of the
+  // slow tokens i / 16 + 16 s, summing the chunks in chunk order; one device-scope acquire, then
+  // ordinary 16-byte loads, all in flight at once
   const int row = bx * 64 + 4 * (threadIdx.x & 15);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float4 pv[4][kMaxProdChunks];
-  int z0[4], zn[4];
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
-    const int t = (threadIdx.x >> 4) + 16 * sg;
-    const bool f = t < p.ntok && s_isfast[t];
-    z0[sg] = f ? 0 : zf;
-    zn[sg] = f ? zf : p.zs;
+    const int i = (threadIdx.x >> 4) + 16 * sg;
+    if (i >= ns) continue;
+    const int t = s_slow[i];
 #pragma unroll
     for (int zz = 0; zz < kMaxProdChunks; ++zz)
-      if (zz < zn[sg] && t < p.ntok)
-        pv[sg][zz] = *reinterpret_cast<const float4*>(p.Py + ((long long)(z0[sg] + zz) * p.ntok + t) * p.d_out + row);
+      if (zz < p.zs) pv[sg][zz] = *reinterpret_cast<const float4*>(p.Py + ((long long)zz * p.ntok + t) * p.d_out + row);
   }
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
-    const int t = (threadIdx.x >> 4) + 16 * sg;
-    if (t >= p.ntok) continue;
+    const int i = (threadIdx.x >> 4) + 16 * sg;
+    if (i >= ns) continue;
+    const int t = s_slow[i];
     float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int zz = 0; zz < kMaxProdChunks; ++zz) {
-      if (zz < zn[sg]) {
+      if (zz < p.zs) {
         a[0] += pv[sg][zz].x;
         a[1] += pv[sg][zz].y;
         a[2] += pv[sg][zz].z;
