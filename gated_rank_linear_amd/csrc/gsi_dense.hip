@@ -2253,6 +2253,9 @@ __global__ __launch_bounds__(256) void bstep_kernel(BProjArgs pa, int np_x, int 
     bprod_block<T>(pb, (i - np) % nq_x, (i - np) / nq_x, nq_z, lds);
 }
 
+// the products' partial sums (slow chunks) and the fast chunk fit the split-K buffer
+static_assert(kMaxProdChunks + 1 <= kMaxSplit, "products chunks exceed the partial-sum buffer");
+
 BatchedSplit batched_split(int dtype, const LayerDesc& L, int ntok) {
   BatchedSplit sp{0, 0, 0, 0, 0, 0};
   if (dtype == GSI_F32 || ntok < 1 || ntok > 64) return sp;
