@@ -48,6 +48,9 @@ SIGNATURES = [
     ("gsi_stack_decode_noalloc", _int, [_vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp]),
     ("gsi_calibrate_workspace_bytes", _sz, [_int, _int, _int]),
     ("gsi_calibrate", _int, [_int, _int, _int, _vp, _vp, _int, _vp, _vp, _sz, _vp]),
+    ("gsi_block_step_workspace_bytes", _sz, [_vp, _vp, _int]),
+    ("gsi_block_step", _int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _sz, _vp]),
 ]
 
 
@@ -235,6 +238,22 @@ def gsi_calibrate(A: torch.Tensor, Q0t: torch.Tensor, n_iter: int, Qt: torch.Ten
     rc = lib.gsi_calibrate(n, d, k, _ptr(A), _ptr(Q0t), int(n_iter), _ptr(Qt), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gsi_calibrate")
+
+
+def gsi_block_step_workspace_bytes(A: Stack, B: Stack, n_heads: int) -> int:
+    return lib.gsi_block_step_workspace_bytes(A.handle, B.handle, int(n_heads))
+
+
+def gsi_block_step(A: Stack, B: Stack, gamma: torch.Tensor, beta: torch.Tensor, x: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, pos: int, n_heads: int, eps: float,
+                   xa: torch.Tensor, ya: torch.Tensor, xb: torch.Tensor, yb: torch.Tensor, gates: torch.Tensor,
+                   rho: torch.Tensor | None, ws: torch.Tensor, stream=None) -> None:
+    """One decode-step block: LayerNorm, stack A [QKV, fc_in], attention over the caches (row pos
+    written), GELU, stack B [out, fc_out], x += y_out + y_mlp (x updated in place)."""
+    rc = lib.gsi_block_step(A.handle, B.handle, _ptr(gamma), _ptr(beta), _ptr(x), _ptr(k_cache), _ptr(v_cache),
+                            int(pos), int(n_heads), float(eps), _ptr(xa), _ptr(ya), _ptr(xb), _ptr(yb), _ptr(gates),
+                            _ptr(rho), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "gsi_block_step")
 
 
 # ------------------------------------------------------------------------------------------------

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libgsi.so")
 BENCH_LIB = os.path.join(OUT_DIR, "libgsi_bench.so")
-SOURCES = ["gsi_api.cpp", "gsi_dense.hip", "gsi_decode.hip", "gsi_calibrate.hip", "gsi_noalloc.hip"]
+SOURCES = ["gsi_api.cpp", "gsi_dense.hip", "gsi_decode.hip", "gsi_calibrate.hip", "gsi_noalloc.hip", "gsi_step.hip"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -9,6 +9,7 @@
 #include <new>
 
 #include "gsi_internal.h"
+#include "gsi_step.h"
 
 using namespace gsi;
 
@@ -526,6 +527,56 @@ int gsi_workspace_status(void* ws, size_t ws_nbytes, int* host_status, void* str
   *host_status = v;
   int zero = 0;
   return hip_rc(hipMemcpy(&ws_header(ws)->status, &zero, sizeof(int), hipMemcpyHostToDevice));
+}
+
+// ---- one decode-step block: GSI sites around an unchanged plain attention ----
+
+static bool block_shapes(const gsi_stack* A, const gsi_stack* B, int n_heads, int* d_out, int* dff_out) {
+  if (A->n_sites != 2 || B->n_sites != 2) return false;
+  const LayerDesc &q = A->h_table[0], &f = A->h_table[1], &o = B->h_table[0], &m = B->h_table[1];
+  const int d = q.d, dff = f.d_out;
+  if (d < 64 || d > 16384 || n_heads < 1 || d % n_heads != 0) return false;
+  const int dh = d / n_heads;
+  if (dh != 64 && dh != 128 && dh != 256) return false;
+  if (q.d_out != 3 * d || f.d != d || o.d != d || o.d_out != d || m.d != dff || m.d_out != d || dff < 1) return false;
+  *d_out = d;
+  *dff_out = dff;
+  return true;
+}
+
+size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, int n_heads) {
+  int d = 0, dff = 0;
+  if (!A || !B || !block_shapes(A, B, n_heads, &d, &dff)) return 0;
+  const size_t st = std::max(ws_bytes_for(A->k_max, A->d_out_max, 1), ws_bytes_for(B->k_max, B->d_out_max, 1));
+  return align256(st) + align256(attn_ws_bytes(d, n_heads));
+}
+
+int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
+                   void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
+                   uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !B || !gamma || !beta || !x || !k_cache || !v_cache || !xa || !ya || !xb || !yb || !gates || !ws)
+    return GSI_ERR_NULL;
+  if (A->dtype != B->dtype || (A->dtype != GSI_BF16 && A->dtype != GSI_F16)) return GSI_ERR_DTYPE;
+  int d = 0, dff = 0;
+  if (!block_shapes(A, B, n_heads, &d, &dff) || pos < 0 || pos >= (1 << 24)) return GSI_ERR_SHAPE;
+  int rc = check_eps(eps);
+  if (rc != GSI_OK) return rc;
+  for (const void* p : {gamma, beta, (const void*)x, (const void*)k_cache, (const void*)v_cache, (const void*)xa,
+                        (const void*)ya, (const void*)xb, (const void*)yb, (const void*)ws})
+    if (!aligned16(p)) return GSI_ERR_ALIGN;
+  if (ws_bytes < gsi_block_step_workspace_bytes(A, B, n_heads)) return GSI_ERR_WORKSPACE;
+  const size_t st = align256(std::max(ws_bytes_for(A->k_max, A->d_out_max, 1), ws_bytes_for(B->k_max, B->d_out_max, 1)));
+  float* part = (float*)((char*)ws + st);
+  hipStream_t s = (hipStream_t)stream;
+  rc = launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
+  if (rc != GSI_OK) return rc;
+  rc = gsi_stack_decode(A, xa, 1, 1, eps, ya, gates, rho, ws, st, stream);
+  if (rc != GSI_OK) return rc;
+  rc = launch_attention_gelu(A->dtype, ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+  if (rc != GSI_OK) return rc;
+  rc = gsi_stack_decode(B, xb, 1, 1, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, st, stream);
+  if (rc != GSI_OK) return rc;
+  return launch_residual(A->dtype, x, yb, d, s);
 }
 
 }  // extern "C"

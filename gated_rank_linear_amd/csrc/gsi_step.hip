@@ -1,0 +1,274 @@
+// The kernels of one batch-1 decode step of a GPT-J-shaped parallel block that are not GSI sites:
+// LayerNorm, plain softmax attention over the key/value cache, GELU and the residual add. The
+// pages run every linear map as a GSI site and leave attention unchanged [GSI §3 item 4, §5];
+// the block's form (one LayerNorm feeding attention and MLP, tanh GELU, no positional rotation)
+// is the plainest GPT-J-shaped reading. All arithmetic is float32 on 16-bit stored values; every
+// result is rounded once to the stored type.
+#include <algorithm>
+#include <cmath>
+
+#include "gsi_step.h"
+
+namespace gsi {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ T bits_as(unsigned short v) {
+  T t;
+  t.b = v;
+  return t;
+}
+
+// EPL consecutive 16-bit elements starting at p (aligned to 2 EPL bytes), as float32
+template <typename T, int EPL>
+__device__ __forceinline__ void load_row(const T* p, float (&out)[EPL]) {
+  const unsigned short* q = reinterpret_cast<const unsigned short*>(p);
+  if constexpr (EPL == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(q);
+    out[0] = to_f32(bits_as<T>(v.x & 0xffffu));
+    out[1] = to_f32(bits_as<T>(v.x >> 16));
+    out[2] = to_f32(bits_as<T>(v.y & 0xffffu));
+    out[3] = to_f32(bits_as<T>(v.y >> 16));
+  } else if constexpr (EPL == 2) {
+    const unsigned v = *reinterpret_cast<const unsigned*>(q);
+    out[0] = to_f32(bits_as<T>(v & 0xffffu));
+    out[1] = to_f32(bits_as<T>(v >> 16));
+  } else {
+    out[0] = to_f32(bits_as<T>(q[0]));
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// sum over the block's waves in wave order (deterministic); every thread gets the result
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // red is free
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[w];
+  return s;
+}
+
+// LayerNorm of one row (d <= 16384), written twice: the stack's two sites read the same input
+template <typename T>
+__global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
+                                                      const T* __restrict__ beta, int d, T* __restrict__ xa) {
+  constexpr int kMaxPer = 16;
+  __shared__ float red[16];
+  float v[kMaxPer];
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = i < d ? to_f32(x[i]) : 0.f;
+    s += v[u];
+  }
+  const float mean = block_sum<16>(s, red) / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    const float dv = i < d ? v[u] - mean : 0.f;
+    q = __builtin_fmaf(dv, dv, q);
+  }
+  const float var = block_sum<16>(q, red) / (float)d;
+  const float rs = 1.0f / sqrtf(var + kLnEps);
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    if (i < d) {
+      const T a = from_f32<T>((v[u] - mean) * rs * to_f32(gamma[i]) + to_f32(beta[i]));
+      xa[i] = a;
+      xa[d + i] = a;
+    }
+  }
+}
+
+// Block (h, c): head h over the positions of chunk c, [c lc, min(L, (c + 1) lc)), L = pos + 1.
+// Wave w takes positions c lc + w, + 4, ...; lane l holds elements EPL l .. EPL l + EPL - 1 of the
+// head. Per position: the score <q, k> / sqrt(dh) (a wave sum), then the running maximum m, the
+// running sum l of exp(s - m) and the running exp(s - m)-weighted sum of the value rows. The four
+// waves are merged through LDS; the chunk's (m, l, sums) go to part. Position pos reads the new
+// token's k and v from ya, and the chunk holding it writes them into row pos of the caches.
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const T* __restrict__ ya, T* __restrict__ kc,
+                                                           T* __restrict__ vc, int pos, int d, int lc, int nsplit,
+                                                           float* __restrict__ part) {
+  constexpr int dh = 64 * EPL;
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_acc[4][dh];
+  const int h = blockIdx.x, c = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = h * dh + lane * EPL;
+  const int j0 = c * lc, j1 = min(pos + 1, j0 + lc);
+  float q[EPL];
+  load_row<T, EPL>(ya + col, q);
+  const float scale = 1.0f / sqrtf((float)dh);
+  if (wave == 0 && pos >= j0 && pos < j1) {
+    // the new token joins the caches (this launch reads row pos from ya only)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      kc[(long long)pos * d + col + e] = ya[d + col + e];
+      vc[(long long)pos * d + col + e] = ya[2 * d + col + e];
+    }
+  }
+  float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int j = j0 + wave; j < j1; j += 4) {
+    const T* kr = j == pos ? ya + d : kc + (long long)j * d;
+    const T* vr = j == pos ? ya + 2 * d : vc + (long long)j * d;
+    float kv[EPL], vv[EPL];
+    load_row<T, EPL>(kr + col, kv);
+    load_row<T, EPL>(vr + col, vv);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(q[e], kv[e], dot);
+    const float sc = wave_sum(dot) * scale;
+    const float mn = fmaxf(m, sc);
+    const float cf = expf(m - mn), p = expf(sc - mn);
+    l = l * cf + p;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * cf + p * vv[e];
+    m = mn;
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[e];
+  __syncthreads();
+  float* out = part + ((long long)h * nsplit + c) * (dh + 2);
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  if (threadIdx.x < dh) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) a += s_acc[w][threadIdx.x] * expf(s_m[w] - M);
+    out[2 + threadIdx.x] = a;
+  }
+  if (threadIdx.x == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += s_l[w] * expf(s_m[w] - M);
+    out[0] = M;
+    out[1] = L;
+  }
+}
+
+// Blocks 0 .. H - 1: head h's output from its chunks (o = sum_c e^(m_c - M) sums_c / sum_c
+// e^(m_c - M) l_c, chunks in order) to xb[0:d]; blocks H ..: u = gelu(f) for 256 elements each
+// to xb[d:d+dff], f = ya[3d:3d+dff].
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void attn_combine_gelu_kernel(const float* __restrict__ part, int nsplit, int d,
+                                                                int n_heads, const T* __restrict__ f, int dff,
+                                                                T* __restrict__ xb) {
+  constexpr int dh = 64 * EPL;
+  if ((int)blockIdx.x < n_heads) {
+    const int h = blockIdx.x;
+    if (threadIdx.x >= dh) return;
+    const float* ph = part + (long long)h * nsplit * (dh + 2);
+    float M = -INFINITY;
+    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, ph[(long long)c * (dh + 2)]);
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < nsplit; ++c) {
+      const float* pc = ph + (long long)c * (dh + 2);
+      const float w = expf(pc[0] - M);
+      den = __builtin_fmaf(pc[1], w, den);
+      num = __builtin_fmaf(pc[2 + threadIdx.x], w, num);
+    }
+    xb[h * dh + threadIdx.x] = from_f32<T>(num / den);
+    return;
+  }
+  const int i = ((int)blockIdx.x - n_heads) * 256 + threadIdx.x;
+  if (i >= dff) return;
+  const float z = to_f32(f[i]);
+  const float u = 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
+  xb[d + i] = from_f32<T>(u);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void residual_kernel(T* __restrict__ x, const T* __restrict__ yb, int d) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < d) x[i] = from_f32<T>((to_f32(x[i]) + to_f32(yb[i])) + to_f32(yb[d + i]));
+}
+
+}  // namespace
+
+int attn_splits(int L, int n_heads) {
+  const int want = std::max(1, std::min(kMaxAttnSplit, (512 + n_heads - 1) / n_heads));
+  const int lc = std::max(16, (L + want - 1) / want);
+  return (L + lc - 1) / lc;
+}
+
+size_t attn_ws_bytes(int d, int n_heads) { return (size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4; }
+
+int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta, int d, void* xa, hipStream_t s) {
+  if (d < 1 || d > 16384) return GSI_ERR_SHAPE;
+  if (dtype == GSI_BF16)
+    ln_dup_kernel<bf16_t><<<1, 1024, 0, s>>>((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)beta, d,
+                                             (bf16_t*)xa);
+  else if (dtype == GSI_F16)
+    ln_dup_kernel<f16_t><<<1, 1024, 0, s>>>((const f16_t*)x, (const f16_t*)gamma, (const f16_t*)beta, d,
+                                            (f16_t*)xa);
+  else
+    return GSI_ERR_DTYPE;
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+template <typename T, int EPL>
+static void attention_launch(const void* ya, void* kc, void* vc, int pos, int d, int n_heads, int dff, void* xb,
+                             float* part, hipStream_t s) {
+  const int L = pos + 1;
+  const int nsplit = attn_splits(L, n_heads);
+  const int lc = (L + nsplit - 1) / nsplit;
+  attn_partial_kernel<T, EPL><<<dim3(n_heads, nsplit), 256, 0, s>>>((const T*)ya, (T*)kc, (T*)vc, pos, d, lc, nsplit,
+                                                                     part);
+  const int nb = n_heads + (dff + 255) / 256;
+  attn_combine_gelu_kernel<T, EPL><<<nb, 256, 0, s>>>(part, nsplit, d, n_heads, (const T*)ya + 3 * (long long)d, dff,
+                                                      (T*)xb);
+}
+
+int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cache, int pos, int d, int n_heads,
+                          int dff, void* xb, float* part, hipStream_t s) {
+  if (n_heads < 1 || d % n_heads != 0 || pos < 0) return GSI_ERR_SHAPE;
+  const int dh = d / n_heads;
+  const bool bf = dtype == GSI_BF16;
+  if (dtype != GSI_BF16 && dtype != GSI_F16) return GSI_ERR_DTYPE;
+  if (dh == 64) {
+    if (bf) attention_launch<bf16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    else attention_launch<f16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+  } else if (dh == 128) {
+    if (bf) attention_launch<bf16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    else attention_launch<f16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+  } else if (dh == 256) {
+    if (bf) attention_launch<bf16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    else attention_launch<f16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+  } else {
+    return GSI_ERR_SHAPE;
+  }
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+int launch_residual(int dtype, void* x, const void* yb, int d, hipStream_t s) {
+  const unsigned nb = (unsigned)((d + 255) / 256);
+  if (dtype == GSI_BF16)
+    residual_kernel<bf16_t><<<nb, 256, 0, s>>>((bf16_t*)x, (const bf16_t*)yb, d);
+  else if (dtype == GSI_F16)
+    residual_kernel<f16_t><<<nb, 256, 0, s>>>((f16_t*)x, (const f16_t*)yb, d);
+  else
+    return GSI_ERR_DTYPE;
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+}  // namespace gsi

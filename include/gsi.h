@@ -232,6 +232,37 @@ size_t gsi_calibrate_workspace_bytes(int n, int d, int k);
 int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_iter, float* Qt, void* ws,
                   size_t ws_bytes, void* stream);
 
+/*
+ * One block of a batch-1 decode step with the GSI sites embedded in an unchanged plain attention
+ * [GSI §3 item 4, §5 last bullet]: the pages run every linear map as a GSI site and leave
+ * attention as it is; the block around the sites is the GPT-J-shaped parallel form (one
+ * LayerNorm feeding both branches). For a token x (one row of d, updated in place):
+ *   a = LayerNorm(x; gamma, beta), eps_ln 1e-5, statistics in float32
+ *   [q | k | v] = site QKV(a), f = site fc_in(a)               stack A: [QKV, fc_in], input [a | a]
+ *   K[pos] = k, V[pos] = v; per head h (dh = d / n_heads): o_h = softmax(q_h K_h^T / sqrt(dh)) V_h
+ *   over cache rows 0 .. pos (plain softmax, no positional rotation, float32)
+ *   u = gelu(f), tanh form
+ *   y_out = site out(o), y_mlp = site fc_out(u)                stack B: [out, fc_out], input [o | u]
+ *   x += y_out + y_mlp
+ * A and B are stacks of exactly two sites of one 16-bit dtype with those shapes (A: d -> 3 d and
+ * d -> dff; B: d -> d and dff -> d; any site mode), n_heads divides d with d / n_heads in
+ * {64, 128, 256}, d <= 16384; otherwise GSI_ERR_SHAPE / GSI_ERR_DTYPE. Each site runs with gate
+ * threshold eps through the batch-1 kernel (gsi_stack_decode with one token).
+ * Buffers (device, 16-byte aligned, the caller's): gamma, beta [d]; x [d]; k_cache, v_cache
+ * [>= pos + 1, d] row-major (rows 0 .. pos - 1 are read, row pos is written); the step's
+ * intermediates, readable after the call: xa [2 d] = [a | a], ya [3 d + dff] = [q | k | v | f],
+ * xb [d + dff] = [o | u], yb [2 d] = [y_out | y_mlp]; gates [4] uint8 = QKV, fc_in, out, fc_out
+ * (1 = slow); rho [4] float32 in the same order, optional (NULL). None of them may overlap.
+ * Workspace: gsi_block_step_workspace_bytes, zero-filled before its first use (it holds the
+ * batch-1 kernel's exchange state, kept consistent by the library afterwards, and the attention's
+ * partial sums); calls on one workspace must not overlap. Arguments are checked before anything
+ * is enqueued; the call enqueues five launches on `stream` and returns.
+ */
+size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, int n_heads);
+int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
+                   void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
+                   uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

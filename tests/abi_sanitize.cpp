@@ -78,6 +78,10 @@ int main() {
   int st = 0;
   EXPECT(gsi_workspace_status(nullptr, 0, &st, nullptr), GSI_ERR_NULL);
   EXPECT(gsi_workspace_status(p, sizeof(buf), nullptr, nullptr), GSI_ERR_NULL);
+  // decode-step block: NULL stacks or buffers are refused before anything else
+  EXPECT(gsi_block_step_workspace_bytes(nullptr, nullptr, 16), 0);
+  EXPECT(gsi_block_step(nullptr, nullptr, p, p, p, p, p, 0, 16, 0.1f, p, p, p, p, buf, nullptr, p, sizeof(buf),
+                        nullptr), GSI_ERR_NULL);
   // calibration
   EXPECT(gsi_calibrate(0, 64, 16, (const float*)p, (const float*)p, 1, (float*)p, p, sizeof(buf), nullptr), GSI_ERR_SHAPE);
   EXPECT(gsi_calibrate(32, 64, 16, nullptr, (const float*)p, 1, (float*)p, p, sizeof(buf), nullptr), GSI_ERR_NULL);

@@ -1,0 +1,203 @@
+"""GPU parity of the decode-step block (gsi_block_step): GSI sites embedded in an unchanged plain
+attention [GSI §3 item 4, §5], GPT-J-shaped parallel blocks on the synthetic step model.
+
+Each call is checked op by op against the fp64 oracle applied to the GPU's own stored inputs of
+that op (teacher forcing): LayerNorm, the four sites (gates bit for bit where the oracle's ratio
+is more than 1e-3 from eps, y within 2e-2), the cache row written, attention, GELU and the
+residual add (within 8e-3, one rounding to the 16-bit type). A chain run from the embeddings is
+then compared with the oracle's own chain."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gsi_oracle as orc
+from oracle import gsi_step as ostep
+from synth.step import step_config, step_model
+from tests.gpu_util import TOL, compare_site, rel_l2, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+OP_TOL = 8e-3
+SITES_A = ("qkv", "fc_in")
+SITES_B = ("out", "fc_out")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gated_rank_linear_amd as g
+    assert g.gsi_device_check() == 0
+    return g
+
+
+class Model:
+    """The synthetic step model on the GPU: per block two stacks, LayerNorm parameters, caches."""
+
+    def __init__(self, g, cfg):
+        self.cfg = cfg
+        self.host = step_model(cfg)
+        self.blocks = []
+        self.keep = []
+        for hb in self.host["blocks"]:
+            dev = {n: (hb[n][0].cuda(), hb[n][1].cuda()) for n in SITES_A + SITES_B}
+            layers = {n: g.create_layer(*dev[n]) for n in dev}
+            A = g.gsi_stack_create([layers[n] for n in SITES_A])
+            B = g.gsi_stack_create([layers[n] for n in SITES_B])
+            blk = {"A": A, "B": B, "gamma": hb["gamma"].cuda(), "beta": hb["beta"].cuda(),
+                   "K": hb["K"].cuda(), "V": hb["V"].cuda(), "layers": layers, "dev": dev}
+            self.blocks.append(blk)
+        torch.cuda.synchronize()
+        d, dff = cfg.d, cfg.d_ff
+        dt = self.host["x0"].dtype
+        self.xa = torch.zeros(2 * d, dtype=dt, device="cuda")
+        self.ya = torch.zeros(3 * d + dff, dtype=dt, device="cuda")
+        self.xb = torch.zeros(d + dff, dtype=dt, device="cuda")
+        self.yb = torch.zeros(2 * d, dtype=dt, device="cuda")
+        self.gates = torch.zeros(4, dtype=torch.uint8, device="cuda")
+        self.rho = torch.zeros(4, dtype=torch.float32, device="cuda")
+        b0 = self.blocks[0]
+        self.ws = g.new_workspace(g.gsi_block_step_workspace_bytes(b0["A"], b0["B"], cfg.n_heads))
+
+    def step(self, g, b, x, pos):
+        blk = self.blocks[b]
+        g.gsi_block_step(blk["A"], blk["B"], blk["gamma"], blk["beta"], x, blk["K"], blk["V"], pos,
+                         self.cfg.n_heads, self.cfg.eps, self.xa, self.ya, self.xb, self.yb, self.gates, self.rho,
+                         self.ws)
+
+    def destroy(self):
+        for blk in self.blocks:
+            blk["A"].destroy()
+            blk["B"].destroy()
+
+
+def _site_check(W, V, x_in, y_got, gate_got, eps, dt, where, tally):
+    """One site call: gate bit for bit and y within tolerance where the oracle's ratio is clear of
+    the line; within 1e-3 of it either gate is valid and y is compared with that gate's path."""
+    ref = orc.forward(W, V, x_in[None], eps)
+    clear = bool(abs(ref["rho"][0] - eps) > 1e-3)
+    tally.append(clear)
+    if not clear:
+        ref = orc.forward(W, V, x_in[None], 0.0 if gate_got else 1.5)  # that path for this token
+    compare_site(y_got[None], np.array([gate_got]), ref, TOL["bf16"], where=where)
+    return int(ref["gate"][0])
+
+
+def _teacher_forced(g, model, n_tokens):
+    cfg = model.cfg
+    d, dff, H = cfg.d, cfg.d_ff, cfg.n_heads
+    tally, n_slow = [], 0
+    for t in range(n_tokens):
+        x = model.host["x0"][t].cuda().clone()
+        pos = cfg.L0 + t
+        for b in range(cfg.n_blocks):
+            hb = model.host["blocks"][b]
+            blk = model.blocks[b]
+            x_before = to_np(x)
+            model.step(g, b, x, pos)
+            torch.cuda.synchronize()
+            assert g.gsi_workspace_status(model.ws) == 0
+            xa, ya, xb, yb = (to_np(v) for v in (model.xa, model.ya, model.xb, model.yb))
+            gates = model.gates.cpu().numpy()
+            where = f"token {t} block {b}"
+            # LayerNorm of the stored x, written twice
+            assert np.array_equal(xa[:d], xa[d:]), where
+            e = rel_l2(xa[:d], ostep.layer_norm(x_before, hb["gamma"], hb["beta"]))
+            assert e <= OP_TOL, f"{where}: LayerNorm rel L2 {e:.2e}"
+            # stack A on the GPU's a
+            n_slow += _site_check(*hb["qkv"], xa[:d], ya[:3 * d], gates[0], cfg.eps, model.xa.dtype, f"{where} qkv", tally)
+            n_slow += _site_check(*hb["fc_in"], xa[:d], ya[3 * d:], gates[1], cfg.eps, model.xa.dtype, f"{where} fc_in", tally)
+            # the new k and v joined the caches bit for bit
+            Kc, Vc = to_np(blk["K"][:pos + 1]), to_np(blk["V"][:pos + 1])
+            assert np.array_equal(Kc[pos], ya[d:2 * d]) and np.array_equal(Vc[pos], ya[2 * d:3 * d]), where
+            e = rel_l2(xb[:d], ostep.attention_decode(ya[:d], Kc, Vc, H))
+            assert e <= OP_TOL, f"{where}: attention rel L2 {e:.2e}"
+            e = rel_l2(xb[d:], ostep.gelu_tanh(ya[3 * d:]))
+            assert e <= OP_TOL, f"{where}: GELU rel L2 {e:.2e}"
+            # stack B on the GPU's o and u
+            n_slow += _site_check(*hb["out"], xb[:d], yb[:d], gates[2], cfg.eps, model.xa.dtype, f"{where} out", tally)
+            n_slow += _site_check(*hb["fc_out"], xb[d:], yb[d:], gates[3], cfg.eps, model.xa.dtype, f"{where} fc_out", tally)
+            e = rel_l2(to_np(x), x_before + yb[:d] + yb[d:])
+            assert e <= OP_TOL, f"{where}: residual rel L2 {e:.2e}"
+    assert np.mean(tally) >= 0.9, f"only {sum(tally)} of {len(tally)} site calls clear of the gate line"
+    return len(tally), n_slow
+
+
+def test_step_blocks_teacher_forced(g):
+    """GPT-2-shaped widths (d 768, 12 heads of 64, fp16), two blocks, six tokens after a 24-position
+    prefix (two attention chunks per head)."""
+    cfg = step_config(71)
+    say(f"case: {cfg.name}, teacher-forced per op")
+    model = Model(g, cfg)
+    n, n_slow = _teacher_forced(g, model, cfg.n_tokens)
+    say(f"  {n} site calls, {n_slow} slow")
+    assert 0 < n_slow < n
+    model.destroy()
+
+
+def test_step_full_width_teacher_forced(g):
+    """GPT-J-shaped widths (d 4096, 16 heads of 256, d_ff 16384, bf16), one block, eight tokens (two
+    planned slow) after a 64-position prefix."""
+    cfg = step_config(73)
+    say(f"case: {cfg.name}, teacher-forced per op")
+    model = Model(g, cfg)
+    n, n_slow = _teacher_forced(g, model, cfg.n_tokens)
+    say(f"  {n} site calls, {n_slow} slow")
+    assert 0 < n_slow < n
+    model.destroy()
+
+
+def test_step_long_cache(g):
+    """A 2000-position prefix (43 attention chunks per head at 12 heads), two tokens."""
+    cfg = dataclasses.replace(step_config(71), L0=2000, n_tokens=2, n_blocks=1)
+    say(f"case: {cfg.name} with a 2000-position prefix")
+    model = Model(g, cfg)
+    _teacher_forced(g, model, cfg.n_tokens)
+    model.destroy()
+
+
+def test_step_chain_matches_oracle_chain(g):
+    """Two blocks, six tokens from the embeddings, each block's output feeding the next: the GPU's
+    final rows and gates against the oracle's own float64 chain (gates compared where the oracle's
+    ratio is more than 1e-2 from eps; the rows within 3e-2, the chain's roundings compound)."""
+    cfg = step_config(71)
+    say(f"case: {cfg.name}, chained")
+    model = Model(g, cfg)
+    d = cfg.d
+    Kh = [orc.as_f64(hb["K"]) for hb in model.host["blocks"]]
+    Vh = [orc.as_f64(hb["V"]) for hb in model.host["blocks"]]
+    worst = 0.0
+    for t in range(cfg.n_tokens):
+        x = model.host["x0"][t].cuda().clone()
+        xo = orc.as_f64(model.host["x0"][t])
+        pos = cfg.L0 + t
+        for b in range(cfg.n_blocks):
+            model.step(g, b, x, pos)
+            torch.cuda.synchronize()
+            r = ostep.decode_block(xo, model.host["blocks"][b], Kh[b], Vh[b], pos, cfg.eps, cfg.n_heads)
+            gates = model.gates.cpu().numpy()[[0, 2, 1, 3]]  # GPU order QKV, fc_in, out, fc_out
+            clear = np.abs(r["rho"] - cfg.eps) > 1e-2
+            assert np.array_equal(gates[clear], r["gates"][clear]), f"token {t} block {b}: gates {gates} vs {r['gates']}"
+            xo = r["x_next"]
+        e = rel_l2(to_np(x), xo)
+        worst = max(worst, e)
+        assert e <= 3e-2, f"token {t}: final row rel L2 {e:.2e}"
+    say(f"  worst final-row rel L2 {worst:.2e}")
+    model.destroy()
+
+
+def test_block_step_rejects_bad_shapes(g):
+    """Stacks in the wrong order, a head count that does not divide d, a head width outside
+    {64, 128, 256}: GSI_ERR_SHAPE before anything is enqueued."""
+    cfg = step_config(71)
+    model = Model(g, cfg)
+    blk = model.blocks[0]
+    x = model.host["x0"][0].cuda().clone()
+    for A, B, H in ((blk["B"], blk["A"], 12), (blk["A"], blk["B"], 7), (blk["A"], blk["B"], 24)):
+        with pytest.raises(g.GsiError, match="GSI_ERR_SHAPE"):
+            g.gsi_block_step(A, B, blk["gamma"], blk["beta"], x, blk["K"], blk["V"], cfg.L0, H, cfg.eps, model.xa,
+                             model.ya, model.xb, model.yb, model.gates, model.rho, model.ws)
+    with pytest.raises(g.GsiError, match="GSI_ERR_EPS"):
+        g.gsi_block_step(blk["A"], blk["B"], blk["gamma"], blk["beta"], x, blk["K"], blk["V"], cfg.L0, 12, -1.0,
+                         model.xa, model.ya, model.xb, model.yb, model.gates, model.rho, model.ws)
+    model.destroy()
