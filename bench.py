@@ -57,6 +57,9 @@ def parse():
                     help="depth-cascade calibration of the bases on the GPT-J-shaped chain (prints its own line)")
     ap.add_argument("--cal-cold", type=int, default=8, help="subspace-iteration steps of a cold start")
     ap.add_argument("--cal-warm", type=int, default=2, help="steps of a cascade (warm) start")
+    ap.add_argument("--step", action="store_true",
+                    help="batch-1 decode step of the GPT-J-shaped model: the GSI sites around an unchanged "
+                         "plain attention, against the same step with every site dense (prints its own line)")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline workload (not the shared-input and T = 64 workloads)")
     return ap.parse_args()
@@ -86,6 +89,9 @@ def main():
         return
     if args.calibration:
         calibration(args, g, torch, np)
+        return
+    if args.step:
+        decode_step(args, g, torch, np)
         return
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
@@ -592,6 +598,141 @@ def calibration(args, g, torch, np):
            "accuracy": acc,
            "max_sine_vs_planted": {"cascade": round(float(max(sines_casc)), 5), "cold": round(float(max(sines_cold)), 5)},
            "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+def decode_step(args, g, torch, np):
+    """Batch-1 decode step of a GPT-J-shaped model (28 parallel blocks, d 4096, 16 heads of 256,
+    d_ff 16384, k 256, eps 0.10, bf16) on the synthetic step model: per block gsi_block_step
+    (LayerNorm, the [QKV, fc_in] stack, plain attention over a key/value cache that starts with a
+    1024-position prefix, GELU, the [out, fc_out] stack, residual add), token after token, each
+    block's output feeding the next. The same step with both stacks in the dense site mode (y = W x
+    for every site, the same kernels otherwise) is the reference. Tokens/s over --steps tokens
+    (default 48) after --warmup (default 8), one gsi_decode_step call per token, HIP events on the
+    stream the library enqueues on.
+    Algorithmic bytes per token: per site V_k + M (+ W when slow), W for the dense step, plus the
+    attention's key and value rows (2 (pos + 1) d 2 bytes per block)."""
+    import dataclasses
+
+    from oracle import gsi_oracle as orc
+    from oracle import gsi_step as ostep
+    from synth.step import step_config, step_model
+
+    n_warm = min(args.warmup, 8) if args.warmup != 64 else 8
+    n_time = min(args.steps, 48) if args.steps != 512 else 48
+    cfg = dataclasses.replace(step_config(72), n_tokens=n_warm + n_time)
+    t0 = time.time()
+    model = step_model(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[step] generated {cfg.n_blocks} blocks on the GPU in {time.time() - t0:.1f}s")
+    names_a, names_b = ("qkv", "fc_in"), ("out", "fc_out")
+    blocks = []
+    for hb in model["blocks"]:
+        layers = {n: g.create_layer(hb[n][0], hb[n][1]) for n in names_a + names_b}
+        blocks.append({"layers": layers, "hb": hb,
+                       "A": g.gsi_stack_create([layers[n] for n in names_a]),
+                       "B": g.gsi_stack_create([layers[n] for n in names_b]),
+                       "Ad": g.gsi_stack_create_modes([layers[n] for n in names_a], [g.GSI_SITE_DENSE] * 2),
+                       "Bd": g.gsi_stack_create_modes([layers[n] for n in names_b], [g.GSI_SITE_DENSE] * 2)})
+    torch.cuda.synchronize()
+    log(f"[step] layers and stacks in {time.time() - t0:.1f}s")
+    d, dff, H = cfg.d, cfg.d_ff, cfg.n_heads
+    dt = torch.bfloat16
+    xa = torch.zeros(2 * d, dtype=dt, device="cuda")
+    ya = torch.zeros(3 * d + dff, dtype=dt, device="cuda")
+    xb = torch.zeros(d + dff, dtype=dt, device="cuda")
+    yb = torch.zeros(2 * d, dtype=dt, device="cuda")
+    n_tok = cfg.n_tokens
+    gates = torch.zeros((n_tok, cfg.n_blocks, 4), dtype=torch.uint8, device="cuda")
+    ws = g.new_workspace(g.gsi_block_step_workspace_bytes(blocks[0]["A"], blocks[0]["B"], H))
+    K0 = [hb["K"].clone() for hb in model["blocks"]]  # the prefix, restored before each pass
+    V0 = [hb["V"].clone() for hb in model["blocks"]]
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gam = [hb["gamma"] for hb in model["blocks"]]
+    bet = [hb["beta"] for hb in model["blocks"]]
+    Ks = [hb["K"] for hb in model["blocks"]]
+    Vs = [hb["V"] for hb in model["blocks"]]
+    gates = gates.view(n_tok, cfg.n_blocks * 4)
+
+    def run(dense):
+        for b, hb in enumerate(model["blocks"]):
+            hb["K"].copy_(K0[b])
+            hb["V"].copy_(V0[b])
+        xs = model["x0"].clone()
+        sa, sb = ("Ad", "Bd") if dense else ("A", "B")
+        A = [blk[sa] for blk in blocks]
+        B = [blk[sb] for blk in blocks]
+        for t in range(n_tok):
+            if t == n_warm:
+                ev0.record(stream)
+            # one call per token: the library enqueues the 28 blocks' 140 launches
+            g.gsi_decode_step(A, B, gam, bet, Ks, Vs, cfg.L0 + t, H, cfg.eps, xs[t], xa, ya, xb, yb, gates[t], None, ws)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / n_time, xs
+
+    t_gsi, xs = run(False)
+    gt = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)  # [QKV, fc_in, out, fc_out]
+    t_dense, _ = run(True)
+    assert g.gsi_workspace_status(ws) == 0
+    # algorithmic bytes of the timed tokens
+    shapes = {"qkv": (3 * d, d), "fc_in": (dff, d), "out": (d, d), "fc_out": (d, dff)}
+    order = ("qkv", "fc_in", "out", "fc_out")
+    k = cfg.k
+    gsi_b, dense_b = 0.0, 0.0
+    for t in range(n_time):
+        pos = cfg.L0 + n_warm + t
+        att = 2.0 * (pos + 1) * d * 2 * cfg.n_blocks
+        for i, n in enumerate(order):
+            do, di = shapes[n]
+            slow = gt[t, :, i].sum()
+            gsi_b += cfg.n_blocks * (di * k + do * k) * 2.0 + slow * do * di * 2.0
+            dense_b += cfg.n_blocks * do * di * 2.0
+        gsi_b += att
+        dense_b += att
+    gsi_b /= n_time
+    dense_b /= n_time
+    fast = 1.0 - gt.mean()
+    # CPU baseline: the oracle's step on block 0 for as many tokens as about --cpu-seconds allow
+    cpu = None
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        hb = model["blocks"][0]
+        blk64 = {"gamma": orc.as_f64(hb["gamma"].cpu()), "beta": orc.as_f64(hb["beta"].cpu())}
+        for n in order:
+            W64, V64 = orc.as_f64(hb[n][0].cpu()), orc.as_f64(hb[n][1].cpu())
+            blk64[n] = (W64, V64, orc.precompute_image(W64, V64))
+        K64, V64c = orc.as_f64(K0[0].cpu()), orc.as_f64(V0[0].cpu())
+        x64 = orc.as_f64(model["x0"].cpu())
+        t1 = time.perf_counter()
+        n_cpu = 0
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            t = n_cpu % n_tok  # the step's tokens in turn, each at its own position
+            ostep.decode_block(x64[t], blk64, K64, V64c, cfg.L0 + t, cfg.eps, H)
+            n_cpu += 1
+        el = time.perf_counter() - t1
+        threads = max([q.get("num_threads", 1) for q in threadpoolctl.threadpool_info()] or [1])
+        cpu = {"value": round(n_cpu / (el * cfg.n_blocks), 4), "unit": "tokens/s", "cores": int(threads),
+               "kind": "oracle", "sample": f"fp64 oracle step, block 0 x {n_cpu} tokens in {el:.1f}s, scaled "
+                                           f"x{cfg.n_blocks} blocks; M precomputed; BLAS threads {threads}"}
+    out = {"metric": "batch-1 decode step tokens/s, GSI sites around an unchanged plain attention, GPT-J-shaped",
+           "value": round(1.0 / t_gsi, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n_time, "warmup": n_warm,
+           "ms_per_step": round(t_gsi * 1e3, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{cfg.name}: {cfg.n_blocks} parallel blocks, d {d}, {H} heads, d_ff {dff}, "
+                                  f"k {k}, eps {cfg.eps}, cache prefix {cfg.L0}, batch 1"},
+           "roofline": {"bound": "hbm", "achieved": round(gsi_b / t_gsi / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(gsi_b / t_gsi / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "all launches of a step", "bytes_per_step": round(gsi_b)},
+           "fast_fraction": round(float(fast), 5),
+           "dense_step": {"value": round(1.0 / t_dense, 2), "ms_per_step": round(t_dense * 1e3, 4),
+                          "achieved_gbps": round(dense_b / t_dense / 1e9, 1), "bytes_per_step": round(dense_b)},
+           "speedup_vs_dense": round(t_dense / t_gsi, 3),
+           "cpu_baseline": cpu}
+    for blk in blocks:
+        for key in ("A", "B", "Ad", "Bd"):
+            blk[key].destroy()
+    torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

@@ -51,6 +51,9 @@ SIGNATURES = [
     ("gsi_block_step_workspace_bytes", _sz, [_vp, _vp, _int]),
     ("gsi_block_step", _int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _float, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _sz, _vp]),
+    ("gsi_decode_step", _int, [_int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                               ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _int, _int, _float, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 ]
 
 
@@ -254,6 +257,24 @@ def gsi_block_step(A: Stack, B: Stack, gamma: torch.Tensor, beta: torch.Tensor, 
                             int(pos), int(n_heads), float(eps), _ptr(xa), _ptr(ya), _ptr(xb), _ptr(yb), _ptr(gates),
                             _ptr(rho), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gsi_block_step")
+
+
+def gsi_decode_step(A: list, B: list, gamma: list, beta: list, k_cache: list, v_cache: list, pos: int,
+                    n_heads: int, eps: float, x: torch.Tensor, xa: torch.Tensor, ya: torch.Tensor, xb: torch.Tensor,
+                    yb: torch.Tensor, gates: torch.Tensor, rho: torch.Tensor | None, ws: torch.Tensor,
+                    stream=None) -> None:
+    """A whole decode step: gsi_block_step for every block in order on the token row x (per-block
+    lists of stacks, LayerNorm parameters and caches; gates [n_blocks * 4])."""
+    n = len(A)
+    if not (len(B) == len(gamma) == len(beta) == len(k_cache) == len(v_cache) == n):
+        raise ValueError("per-block lists differ in length")
+    arr = lambda vals: (_vp * n)(*vals)
+    rc = lib.gsi_decode_step(n, arr([s.handle for s in A]), arr([s.handle for s in B]), arr([_ptr(t) for t in gamma]),
+                             arr([_ptr(t) for t in beta]), arr([_ptr(t) for t in k_cache]),
+                             arr([_ptr(t) for t in v_cache]), int(pos), int(n_heads), float(eps), _ptr(x), _ptr(xa),
+                             _ptr(ya), _ptr(xb), _ptr(yb), _ptr(gates), _ptr(rho), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "gsi_decode_step")
 
 
 # ------------------------------------------------------------------------------------------------

@@ -544,6 +544,30 @@ static bool block_shapes(const gsi_stack* A, const gsi_stack* B, int n_heads, in
   return true;
 }
 
+// one token through a stack on the batch-1 kernel, launched as an ordinary launch (arguments
+// already checked by the caller)
+static int stack_one_token(gsi_stack* S, const void* X, float eps, void* Y, uint8_t* gates, float* rho, void* ws,
+                           hipStream_t s) {
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.plan = S->d_plan;
+  a.n_sites = S->n_sites;
+  a.n_steps = 1;
+  a.t_step = 1;
+  a.X = X;
+  a.x_ld = S->x_ld;
+  a.Y = Y;
+  a.y_ld = S->y_ld;
+  a.gates = gates;
+  a.rho = rho;
+  a.gate_ld = S->n_sites;
+  a.eps = eps;
+  a.ws = ws;
+  a.P = S->P;
+  a.xr = S->xr;
+  return launch_decode_resident(S->dtype, a, s);
+}
+
 size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, int n_heads) {
   int d = 0, dff = 0;
   if (!A || !B || !block_shapes(A, B, n_heads, &d, &dff)) return 0;
@@ -551,32 +575,77 @@ size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, in
   return align256(st) + align256(attn_ws_bytes(d, n_heads));
 }
 
-int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
-                   void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
-                   uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream) {
+// checks of one block's arguments (nothing enqueued); d and dff of the block on success
+static int block_check(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
+                       void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
+                       uint8_t* gates, void* ws, size_t ws_bytes, int* d, int* dff) {
   if (!A || !B || !gamma || !beta || !x || !k_cache || !v_cache || !xa || !ya || !xb || !yb || !gates || !ws)
     return GSI_ERR_NULL;
   if (A->dtype != B->dtype || (A->dtype != GSI_BF16 && A->dtype != GSI_F16)) return GSI_ERR_DTYPE;
-  int d = 0, dff = 0;
-  if (!block_shapes(A, B, n_heads, &d, &dff) || pos < 0 || pos >= (1 << 24)) return GSI_ERR_SHAPE;
+  if (!block_shapes(A, B, n_heads, d, dff) || pos < 0 || pos >= (1 << 24)) return GSI_ERR_SHAPE;
   int rc = check_eps(eps);
   if (rc != GSI_OK) return rc;
   for (const void* p : {gamma, beta, (const void*)x, (const void*)k_cache, (const void*)v_cache, (const void*)xa,
                         (const void*)ya, (const void*)xb, (const void*)yb, (const void*)ws})
     if (!aligned16(p)) return GSI_ERR_ALIGN;
   if (ws_bytes < gsi_block_step_workspace_bytes(A, B, n_heads)) return GSI_ERR_WORKSPACE;
+  return GSI_OK;
+}
+
+// enqueue one checked block
+static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
+                         void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
+                         uint8_t* gates, float* rho, void* ws, int d, int dff, hipStream_t s) {
   const size_t st = align256(std::max(ws_bytes_for(A->k_max, A->d_out_max, 1), ws_bytes_for(B->k_max, B->d_out_max, 1)));
   float* part = (float*)((char*)ws + st);
-  hipStream_t s = (hipStream_t)stream;
-  rc = launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
+  int rc = launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
   if (rc != GSI_OK) return rc;
-  rc = gsi_stack_decode(A, xa, 1, 1, eps, ya, gates, rho, ws, st, stream);
+  rc = stack_one_token(A, xa, eps, ya, gates, rho, ws, s);
   if (rc != GSI_OK) return rc;
   rc = launch_attention_gelu(A->dtype, ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
   if (rc != GSI_OK) return rc;
-  rc = gsi_stack_decode(B, xb, 1, 1, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, st, stream);
+  rc = stack_one_token(B, xb, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, s);
   if (rc != GSI_OK) return rc;
   return launch_residual(A->dtype, x, yb, d, s);
+}
+
+int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
+                   void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
+                   uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream) {
+  int d = 0, dff = 0;
+  const int rc = block_check(A, B, gamma, beta, x, k_cache, v_cache, pos, n_heads, eps, xa, ya, xb, yb, gates, ws,
+                             ws_bytes, &d, &dff);
+  if (rc != GSI_OK) return rc;
+  return block_enqueue(A, B, gamma, beta, x, k_cache, v_cache, pos, n_heads, eps, xa, ya, xb, yb, gates, rho, ws, d,
+                       dff, (hipStream_t)stream);
+}
+
+int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                    const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int n_heads,
+                    float eps, void* x, void* xa, void* ya, void* xb, void* yb, uint8_t* gates, float* rho, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (n_blocks < 1) return GSI_ERR_SHAPE;
+  if (!A || !B || !gamma || !beta || !k_cache || !v_cache) return GSI_ERR_NULL;
+  int d0 = 0, dff0 = 0;
+  for (int b = 0; b < n_blocks; ++b) {  // every block checked before anything is enqueued
+    int d = 0, dff = 0;
+    const int rc = block_check(A[b], B[b], gamma[b], beta[b], x, k_cache[b], v_cache[b], pos, n_heads, eps, xa, ya,
+                               xb, yb, gates, ws, ws_bytes, &d, &dff);
+    if (rc != GSI_OK) return rc;
+    if (b == 0) {
+      d0 = d;
+      dff0 = dff;
+    } else if (d != d0 || dff != dff0 || A[b]->dtype != A[0]->dtype) {
+      return GSI_ERR_SHAPE;
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int b = 0; b < n_blocks; ++b) {
+    const int rc = block_enqueue(A[b], B[b], gamma[b], beta[b], x, k_cache[b], v_cache[b], pos, n_heads, eps, xa, ya,
+                                 xb, yb, gates + 4 * b, rho ? rho + 4 * b : nullptr, ws, d0, dff0, s);
+    if (rc != GSI_OK) return rc;
+  }
+  return GSI_OK;
 }
 
 }  // extern "C"

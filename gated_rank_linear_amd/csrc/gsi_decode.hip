@@ -747,7 +747,7 @@ int launch_plan(const LayerDesc& d, int P, int es, PlanRow* out, hipStream_t s) 
   return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
-int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
+static int launch_decode_as(int dtype, const DecodeArgs& a, hipStream_t s, bool cooperative) {
   const void* fn = decode_fn(dtype, a.xr);
   if (!fn) return GSI_ERR_DTYPE;
   DecodeParams p;
@@ -765,8 +765,20 @@ int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
   p.eps = a.eps;
   decode_boxes(a.ws, &p.hdr, &p.box_g, &p.box_p, &p.box_f);
   void* args[] = {&p};
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.P), dim3(kDecodeThreads), args, 0, s);
+  hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(a.P), dim3(kDecodeThreads), args, 0, s)
+                             : hipLaunchKernel(fn, dim3(a.P), dim3(kDecodeThreads), args, 0, s);
   return e == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) { return launch_decode_as(dtype, a, s, true); }
+
+// The same grid as an ordinary launch. The grid is one a device holds at once (decode_grid), the
+// launch starts after the stream's earlier work has finished, and every wait inside the kernel is
+// bounded, so a block that becomes resident late only delays the others. The cooperative launch
+// switches queues before and after the kernel (about 10 us each way); a call that decodes a single
+// token would spend more time there than in the kernel.
+int launch_decode_resident(int dtype, const DecodeArgs& a, hipStream_t s) {
+  return launch_decode_as(dtype, a, s, false);
 }
 
 }  // namespace gsi

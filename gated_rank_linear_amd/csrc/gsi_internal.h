@@ -136,6 +136,8 @@ int decode_grid(int dtype, int xr);
 // plan rows of one site for a grid of P blocks, computed on the device into out[0..P)
 int launch_plan(const LayerDesc& d, int P, int es, PlanRow* out, hipStream_t s);
 int launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
+// the same kernel and grid as an ordinary (not cooperative) launch, for one-token calls
+int launch_decode_resident(int dtype, const DecodeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Dense helpers (create time and the batched path)

@@ -246,8 +246,9 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
  *   x += y_out + y_mlp
  * A and B are stacks of exactly two sites of one 16-bit dtype with those shapes (A: d -> 3 d and
  * d -> dff; B: d -> d and dff -> d; any site mode), n_heads divides d with d / n_heads in
- * {64, 128, 256}, d <= 16384; otherwise GSI_ERR_SHAPE / GSI_ERR_DTYPE. Each site runs with gate
- * threshold eps through the batch-1 kernel (gsi_stack_decode with one token).
+ * {64, 128, 256}, d <= 16384; otherwise GSI_ERR_SHAPE / GSI_ERR_DTYPE. Each stack runs with gate
+ * threshold eps through the batch-1 kernel for one token, as an ordinary launch of its co-resident
+ * grid (a cooperative launch would add a queue switch before and after each of the two).
  * Buffers (device, 16-byte aligned, the caller's): gamma, beta [d]; x [d]; k_cache, v_cache
  * [>= pos + 1, d] row-major (rows 0 .. pos - 1 are read, row pos is written); the step's
  * intermediates, readable after the call: xa [2 d] = [a | a], ya [3 d + dff] = [q | k | v | f],
@@ -262,6 +263,21 @@ size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, in
 int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
                    void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
                    uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A whole batch-1 decode step: gsi_block_step for blocks 0 .. n_blocks - 1 in order on the one
+ * token row x (each block's output is the next block's input), at cache position pos. A, B, gamma,
+ * beta, k_cache and v_cache are HOST arrays of n_blocks per-block arguments as in gsi_block_step;
+ * every block must have the same d, d_ff and dtype. xa, ya, xb, yb are shared by the blocks (they
+ * hold the last block's intermediates afterwards); gates [n_blocks * 4] and rho [n_blocks * 4]
+ * (optional) take each block's four entries in turn. One workspace of
+ * gsi_block_step_workspace_bytes of block 0's stacks. Every block's arguments are checked before
+ * anything is enqueued; the call enqueues 5 n_blocks launches on `stream` and returns.
+ */
+int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                    const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int n_heads,
+                    float eps, void* x, void* xa, void* ya, void* xb, void* yb, uint8_t* gates, float* rho, void* ws,
+                    size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

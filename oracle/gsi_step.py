@@ -67,25 +67,31 @@ def attention_decode(q, K, V, n_heads: int) -> np.ndarray:
     return o
 
 
+def _site(pair, x, eps):
+    """gsi_oracle.forward on one site given as (W, V) or (W, V, M) with M = W V precomputed."""
+    return orc.forward(pair[0], pair[1], x[None], eps, M=pair[2] if len(pair) > 2 else None)
+
+
 def decode_block(x, blk: dict, K_cache, V_cache, pos: int, eps: float, n_heads: int) -> dict:
     """One block for one token. blk holds the block's weights and bases: gamma, beta, and per site
-    ("qkv", "out", "fc_in", "fc_out") W and V (the out site's input is the attention output, the
-    fc_out site's the GELU of the fc_in output). K_cache / V_cache (>= pos + 1 rows x d) hold the
-    earlier positions; rows pos are overwritten with this token's k and v (in float64). Returns
-    every intermediate: a, qkv (with gate and rho), f, o, u, y_out, y_mlp and x_next."""
+    ("qkv", "out", "fc_in", "fc_out") (W, V) or (W, V, M) with M = W V already formed [GSI §2.1]
+    (the out site's input is the attention output, the fc_out site's the GELU of the fc_in output).
+    K_cache / V_cache (>= pos + 1 rows x d) hold the earlier positions; rows pos are overwritten
+    with this token's k and v (in float64). Returns every intermediate: a, qkv, f, o, u, y_out,
+    y_mlp, x_next, and the four sites' gates and ratios in the order QKV, out, fc_in, fc_out."""
     x = orc.as_f64(x).reshape(-1)
     d = x.shape[0]
     a = layer_norm(x, blk["gamma"], blk["beta"])
-    r_qkv = orc.forward(blk["qkv"][0], blk["qkv"][1], a[None], eps)
-    r_fc = orc.forward(blk["fc_in"][0], blk["fc_in"][1], a[None], eps)
+    r_qkv = _site(blk["qkv"], a, eps)
+    r_fc = _site(blk["fc_in"], a, eps)
     qkv = r_qkv["y"][0]
     q, k, v = qkv[:d], qkv[d:2 * d], qkv[2 * d:3 * d]
     K_cache[pos] = k
     V_cache[pos] = v
     o = attention_decode(q, K_cache[:pos + 1], V_cache[:pos + 1], n_heads)
     u = gelu_tanh(r_fc["y"][0])
-    r_out = orc.forward(blk["out"][0], blk["out"][1], o[None], eps)
-    r_mlp = orc.forward(blk["fc_out"][0], blk["fc_out"][1], u[None], eps)
+    r_out = _site(blk["out"], o, eps)
+    r_mlp = _site(blk["fc_out"], u, eps)
     x_next = x + r_out["y"][0] + r_mlp["y"][0]
     return {"a": a, "qkv": qkv, "f": r_fc["y"][0], "o": o, "u": u, "y_out": r_out["y"][0],
             "y_mlp": r_mlp["y"][0], "x_next": x_next,

@@ -82,6 +82,15 @@ int main() {
   EXPECT(gsi_block_step_workspace_bytes(nullptr, nullptr, 16), 0);
   EXPECT(gsi_block_step(nullptr, nullptr, p, p, p, p, p, 0, 16, 0.1f, p, p, p, p, buf, nullptr, p, sizeof(buf),
                         nullptr), GSI_ERR_NULL);
+  gsi_stack* stacks[1] = {nullptr};
+  const void* cptr[1] = {p};
+  void* vptr[1] = {p};
+  EXPECT(gsi_decode_step(0, stacks, stacks, cptr, cptr, vptr, vptr, 0, 16, 0.1f, p, p, p, p, p, buf, nullptr, p,
+                         sizeof(buf), nullptr), GSI_ERR_SHAPE);
+  EXPECT(gsi_decode_step(1, nullptr, stacks, cptr, cptr, vptr, vptr, 0, 16, 0.1f, p, p, p, p, p, buf, nullptr, p,
+                         sizeof(buf), nullptr), GSI_ERR_NULL);
+  EXPECT(gsi_decode_step(1, stacks, stacks, cptr, cptr, vptr, vptr, 0, 16, 0.1f, p, p, p, p, p, buf, nullptr, p,
+                         sizeof(buf), nullptr), GSI_ERR_NULL);
   // calibration
   EXPECT(gsi_calibrate(0, 64, 16, (const float*)p, (const float*)p, 1, (float*)p, p, sizeof(buf), nullptr), GSI_ERR_SHAPE);
   EXPECT(gsi_calibrate(32, 64, 16, nullptr, (const float*)p, 1, (float*)p, p, sizeof(buf), nullptr), GSI_ERR_NULL);

@@ -201,3 +201,35 @@ def test_block_step_rejects_bad_shapes(g):
         g.gsi_block_step(blk["A"], blk["B"], blk["gamma"], blk["beta"], x, blk["K"], blk["V"], cfg.L0, 12, -1.0,
                          model.xa, model.ya, model.xb, model.yb, model.gates, model.rho, model.ws)
     model.destroy()
+
+
+def test_decode_step_equals_block_calls(g):
+    """gsi_decode_step over both blocks gives, bit for bit, the rows, gates and cache rows of the same
+    blocks called one by one through gsi_block_step (six tokens)."""
+    cfg = step_config(71)
+    say(f"case: {cfg.name}, whole-step call against block calls")
+    m1, m2 = Model(g, cfg), Model(g, cfg)
+    nb = cfg.n_blocks
+    gates_all = torch.zeros((cfg.n_tokens, nb * 4), dtype=torch.uint8, device="cuda")
+    rho_all = torch.zeros((cfg.n_tokens, nb * 4), dtype=torch.float32, device="cuda")
+    for t in range(cfg.n_tokens):
+        pos = cfg.L0 + t
+        x1 = m1.host["x0"][t].cuda().clone()
+        x2 = x1.clone()
+        g1 = []
+        for b in range(nb):
+            m1.step(g, b, x1, pos)
+            g1.append(m1.gates.clone())
+        bl = m2.blocks
+        g.gsi_decode_step([k["A"] for k in bl], [k["B"] for k in bl], [k["gamma"] for k in bl],
+                          [k["beta"] for k in bl], [k["K"] for k in bl], [k["V"] for k in bl], pos, cfg.n_heads,
+                          cfg.eps, x2, m2.xa, m2.ya, m2.xb, m2.yb, gates_all[t], rho_all[t], m2.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(x1, x2), f"token {t}: rows differ"
+        assert torch.equal(torch.cat(g1), gates_all[t]), f"token {t}: gates differ"
+        for b in range(nb):
+            assert torch.equal(m1.blocks[b]["K"][pos], m2.blocks[b]["K"][pos])
+            assert torch.equal(m1.blocks[b]["V"][pos], m2.blocks[b]["V"][pos])
+    assert g.gsi_workspace_status(m2.ws) == 0
+    m1.destroy()
+    m2.destroy()

@@ -6,6 +6,7 @@ must sit on the planned side of eps and at least 1e-3 away from it, so gate bits
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import synth
@@ -129,3 +130,30 @@ def test_config6_shared_input_margins():
     for site in range(3):
         si, out = _margin_check(cfg, 0, site)
         assert int(out["gate"].sum()) == 1
+
+
+def test_step_model_gates_and_margins():
+    """The decode-step model (two GPT-2-width blocks): through the oracle's own chain every site's
+    ratio stays more than 1e-2 from eps, the QKV and fc_in ratios follow the planned ones, and both
+    gates occur; the model's tensors are row-major in the storage dtype."""
+    from oracle import gsi_oracle as orc
+    from oracle import gsi_step as ostep
+    from synth.step import step_config, step_model
+
+    cfg = step_config(71)
+    m = step_model(cfg)
+    for hb in m["blocks"]:
+        for n in ("qkv", "out", "fc_in", "fc_out"):
+            W, V = hb[n]
+            assert W.is_contiguous() and V.is_contiguous() and W.dtype == V.dtype == torch.float16
+    gates, rhos = [], []
+    for t in range(cfg.n_tokens):
+        x = orc.as_f64(m["x0"][t])
+        for b, hb in enumerate(m["blocks"]):
+            r = ostep.decode_block(x, hb, orc.as_f64(hb["K"]), orc.as_f64(hb["V"]), cfg.L0 + t, cfg.eps, cfg.n_heads)
+            assert np.all(np.abs(r["rho"] - cfg.eps) > 1e-2), (t, b, r["rho"])
+            assert abs(r["rho"][0] - float(m["planned_rho"][t])) < 5e-3 and abs(r["rho"][2] - r["rho"][0]) < 5e-3
+            gates.append(r["gates"])
+            x = r["x_next"]
+    gates = np.array(gates)
+    assert 0 < gates.sum() < gates.size
