@@ -592,13 +592,16 @@ static int block_check(gsi_stack* A, gsi_stack* B, const void* gamma, const void
   return GSI_OK;
 }
 
-// enqueue one checked block
+// enqueue one checked block. ln_done: xa already holds this block's LayerNorm (the previous
+// block's residual launch formed it); next_gamma / next_beta (optional): the residual launch also
+// forms the next block's LayerNorm into xa.
 static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
                          void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
-                         uint8_t* gates, float* rho, void* ws, int d, int dff, hipStream_t s) {
+                         uint8_t* gates, float* rho, void* ws, int d, int dff, hipStream_t s, bool ln_done = false,
+                         const void* next_gamma = nullptr, const void* next_beta = nullptr) {
   const size_t st = align256(std::max(ws_bytes_for(A->k_max, A->d_out_max, 1), ws_bytes_for(B->k_max, B->d_out_max, 1)));
   float* part = (float*)((char*)ws + st);
-  int rc = launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
+  int rc = ln_done ? GSI_OK : launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
   if (rc != GSI_OK) return rc;
   rc = stack_one_token(A, xa, eps, ya, gates, rho, ws, s);
   if (rc != GSI_OK) return rc;
@@ -606,7 +609,8 @@ static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const vo
   if (rc != GSI_OK) return rc;
   rc = stack_one_token(B, xb, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, s);
   if (rc != GSI_OK) return rc;
-  return launch_residual(A->dtype, x, yb, d, s);
+  return next_gamma ? launch_residual_ln(A->dtype, x, yb, next_gamma, next_beta, d, xa, s)
+                    : launch_residual(A->dtype, x, yb, d, s);
 }
 
 int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
@@ -641,8 +645,11 @@ int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, cons
   }
   hipStream_t s = (hipStream_t)stream;
   for (int b = 0; b < n_blocks; ++b) {
+    // each block's residual add also forms the next block's LayerNorm (one launch fewer per block)
+    const bool more = b + 1 < n_blocks;
     const int rc = block_enqueue(A[b], B[b], gamma[b], beta[b], x, k_cache[b], v_cache[b], pos, n_heads, eps, xa, ya,
-                                 xb, yb, gates + 4 * b, rho ? rho + 4 * b : nullptr, ws, d0, dff0, s);
+                                 xb, yb, gates + 4 * b, rho ? rho + 4 * b : nullptr, ws, d0, dff0, s, b > 0,
+                                 more ? gamma[b + 1] : nullptr, more ? beta[b + 1] : nullptr);
     if (rc != GSI_OK) return rc;
   }
   return GSI_OK;

@@ -11,7 +11,8 @@ constexpr float kLnEps = 1e-5f;
 
 // position chunks of the attention over L positions with n_heads heads
 int attn_splits(int L, int n_heads);
-// float32 partial sums the attention needs: per (head, chunk) its max, sum and dh values
+// scratch of the attention: per (head, chunk) its max, sum and dh float32 values, then one
+// arrival counter per head (zero before the first launch; each launch leaves them zero)
 size_t attn_ws_bytes(int d, int n_heads);
 
 // xa[0:d] = xa[d:2d] = LayerNorm(x) (unit row, float32 statistics, rounded to the dtype)
@@ -23,5 +24,9 @@ int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cach
                           int dff, void* xb, float* part, hipStream_t s);
 // x += yb[0:d] + yb[d:2d]
 int launch_residual(int dtype, void* x, const void* yb, int d, hipStream_t s);
+// x += yb[0:d] + yb[d:2d], then xa = [a | a] with a = LayerNorm(x) for the next block (the values
+// of launch_residual followed by launch_ln_dup)
+int launch_residual_ln(int dtype, void* x, const void* yb, const void* gamma, const void* beta, int d, void* xa,
+                       hipStream_t s);
 
 }  // namespace gsi

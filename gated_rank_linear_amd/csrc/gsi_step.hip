@@ -59,24 +59,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// LayerNorm of one row (d <= 16384), written twice: the stack's two sites read the same input
+constexpr int kLnPer = 16;  // row elements per thread of a 1024-thread LayerNorm block (d <= 16384)
+
+// LayerNorm of the row held in v (thread t has elements t + 1024 u), written twice to xa: the
+// stack's two sites read the same input
 template <typename T>
-__global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
-                                                      const T* __restrict__ beta, int d, T* __restrict__ xa) {
-  constexpr int kMaxPer = 16;
-  __shared__ float red[16];
-  float v[kMaxPer];
+__device__ __forceinline__ void ln_dup_row(const float (&v)[kLnPer], const T* __restrict__ gamma,
+                                           const T* __restrict__ beta, int d, T* __restrict__ xa, float* red) {
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int i = threadIdx.x + 1024 * u;
-    v[u] = i < d ? to_f32(x[i]) : 0.f;
-    s += v[u];
-  }
+  for (int u = 0; u < kLnPer; ++u) s += v[u];
   const float mean = block_sum<16>(s, red) / (float)d;
   float q = 0.f;
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
+  for (int u = 0; u < kLnPer; ++u) {
     const int i = threadIdx.x + 1024 * u;
     const float dv = i < d ? v[u] - mean : 0.f;
     q = __builtin_fmaf(dv, dv, q);
@@ -84,7 +80,7 @@ __global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, c
   const float var = block_sum<16>(q, red) / (float)d;
   const float rs = 1.0f / sqrtf(var + kLnEps);
 #pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
+  for (int u = 0; u < kLnPer; ++u) {
     const int i = threadIdx.x + 1024 * u;
     if (i < d) {
       const T a = from_f32<T>((v[u] - mean) * rs * to_f32(gamma[i]) + to_f32(beta[i]));
@@ -94,20 +90,76 @@ __global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, c
   }
 }
 
-// Block (h, c): head h over the positions of chunk c, [c lc, min(L, (c + 1) lc)), L = pos + 1.
-// Wave w takes positions c lc + w, + 4, ...; lane l holds elements EPL l .. EPL l + EPL - 1 of the
-// head. Per position: the score <q, k> / sqrt(dh) (a wave sum), then the running maximum m, the
-// running sum l of exp(s - m) and the running exp(s - m)-weighted sum of the value rows. The four
-// waves are merged through LDS; the chunk's (m, l, sums) go to part. Position pos reads the new
-// token's k and v from ya, and the chunk holding it writes them into row pos of the caches.
+template <typename T>
+__global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
+                                                      const T* __restrict__ beta, int d, T* __restrict__ xa) {
+  __shared__ float red[16];
+  float v[kLnPer];
+#pragma unroll
+  for (int u = 0; u < kLnPer; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = i < d ? to_f32(x[i]) : 0.f;
+  }
+  ln_dup_row<T>(v, gamma, beta, d, xa, red);
+}
+
+// x += yb[0:d] + yb[d:2d] (rounded and stored), then the next block's LayerNorm of the stored row
+// to xa: the same values as the residual kernel followed by ln_dup_kernel, in one launch
+template <typename T>
+__global__ __launch_bounds__(1024) void residual_ln_kernel(T* __restrict__ x, const T* __restrict__ yb,
+                                                           const T* __restrict__ gamma, const T* __restrict__ beta,
+                                                           int d, T* __restrict__ xa) {
+  __shared__ float red[16];
+  float v[kLnPer];
+#pragma unroll
+  for (int u = 0; u < kLnPer; ++u) {
+    const int i = threadIdx.x + 1024 * u;
+    v[u] = 0.f;
+    if (i < d) {
+      const T xn = from_f32<T>((to_f32(x[i]) + to_f32(yb[i])) + to_f32(yb[d + i]));
+      x[i] = xn;
+      v[u] = to_f32(xn);
+    }
+  }
+  ln_dup_row<T>(v, gamma, beta, d, xa, red);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {  // this wave's vector memory operations, down to N
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One launch: blocks 0 .. H nsplit - 1 are (head h, chunk c) = (i / nsplit, i mod nsplit) of the
+// attention, the rest compute u = gelu(f) for 256 elements each (f = ya[3d:3d+dff], u to
+// xb[d:d+dff]).
+// Attention block (h, c): head h over the positions of chunk c, [c lc, min(L, (c + 1) lc)),
+// L = pos + 1. Wave w takes positions c lc + w, + 4, ...; lane l holds elements EPL l .. + EPL - 1 of
+// the head. Per group of positions: the scores <q, k> / sqrt(dh) (wave sums), then the running
+// maximum m, the running sum l of exp(s - m) and the running exp(s - m)-weighted sum of the value
+// rows. The
+// four waves are merged through LDS and the chunk's (m, l, sums) stored with device-scope stores;
+// the head's last chunk to arrive (counter cnt[h], zero between launches) adds the chunks in chunk
+// order, o_h = sum_c e^(m_c - M) sums_c / sum_c e^(m_c - M) l_c, to xb[h dh ..]. Position pos reads
+// the new token's k and v from ya, and the chunk holding it writes them into row pos of the caches.
 template <typename T, int EPL>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const T* __restrict__ ya, T* __restrict__ kc,
-                                                           T* __restrict__ vc, int pos, int d, int lc, int nsplit,
-                                                           float* __restrict__ part) {
+__global__ __launch_bounds__(256) void attn_gelu_kernel(const T* __restrict__ ya, T* __restrict__ kc,
+                                                        T* __restrict__ vc, int pos, int d, int n_heads, int lc,
+                                                        int nsplit, float* __restrict__ part, int* __restrict__ cnt,
+                                                        int dff, T* __restrict__ xb) {
   constexpr int dh = 64 * EPL;
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_acc[4][dh];
-  const int h = blockIdx.x, c = blockIdx.y;
+  __shared__ int s_last;
+  const int na = n_heads * nsplit;
+  if ((int)blockIdx.x >= na) {
+    const int i = ((int)blockIdx.x - na) * 256 + threadIdx.x;
+    if (i >= dff) return;
+    const float z = to_f32(ya[3 * (long long)d + i]);
+    const float u = 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
+    xb[d + i] = from_f32<T>(u);
+    return;
+  }
+  const int h = blockIdx.x / nsplit, c = blockIdx.x % nsplit;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = h * dh + lane * EPL;
   const int j0 = c * lc, j1 = min(pos + 1, j0 + lc);
@@ -125,21 +177,45 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const T* __restrict__
   float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int j = j0 + wave; j < j1; j += 4) {
-    const T* kr = j == pos ? ya + d : kc + (long long)j * d;
-    const T* vr = j == pos ? ya + 2 * d : vc + (long long)j * d;
-    float kv[EPL], vv[EPL];
-    load_row<T, EPL>(kr + col, kv);
-    load_row<T, EPL>(vr + col, vv);
-    float dot = 0.f;
+  // PP positions of the wave at a time (positions jb, jb + 4, ...): every key and value row
+  // loaded first, then PP independent scores, then one rescale of the running sums
+  constexpr int PP = 8;
+  for (int jb = j0 + wave; jb < j1; jb += 4 * PP) {
+    float kv[PP][EPL], vv[PP][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(q[e], kv[e], dot);
-    const float sc = wave_sum(dot) * scale;
-    const float mn = fmaxf(m, sc);
-    const float cf = expf(m - mn), p = expf(sc - mn);
-    l = l * cf + p;
+    for (int p = 0; p < PP; ++p) {
+      const int j = jb + 4 * p;
+      const int jr = j < j1 ? j : jb;  // rows past the chunk read a valid row and are not used
+      const T* kr = jr == pos ? ya + d : kc + (long long)jr * d;
+      const T* vr = jr == pos ? ya + 2 * d : vc + (long long)jr * d;
+      load_row<T, EPL>(kr + col, kv[p]);
+      load_row<T, EPL>(vr + col, vv[p]);
+    }
+    float sc[PP];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * cf + p * vv[e];
+    for (int p = 0; p < PP; ++p) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(q[e], kv[p][e], dot);
+      sc[p] = wave_sum(dot) * scale;
+    }
+    float mn = m;
+#pragma unroll
+    for (int p = 0; p < PP; ++p)
+      if (jb + 4 * p < j1) mn = fmaxf(mn, sc[p]);
+    const float cf = expf(m - mn);
+    l *= cf;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= cf;
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      if (jb + 4 * p < j1) {
+        const float w = expf(sc[p] - mn);
+        l += w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, vv[p][e], acc[e]);
+      }
+    }
     m = mn;
   }
   if (lane == 0) {
@@ -149,52 +225,51 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const T* __restrict__
 #pragma unroll
   for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = acc[e];
   __syncthreads();
-  float* out = part + ((long long)h * nsplit + c) * (dh + 2);
+  float* ph = part + (long long)h * nsplit * (dh + 2);
+  float* out = ph + (long long)c * (dh + 2);
   const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
   if (threadIdx.x < dh) {
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) a += s_acc[w][threadIdx.x] * expf(s_m[w] - M);
-    out[2 + threadIdx.x] = a;
+    __hip_atomic_store(out + 2 + threadIdx.x, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (threadIdx.x == 0) {
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) L += s_l[w] * expf(s_m[w] - M);
-    out[0] = M;
-    out[1] = L;
+    __hip_atomic_store(out, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(out + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
-
-// Blocks 0 .. H - 1: head h's output from its chunks (o = sum_c e^(m_c - M) sums_c / sum_c
-// e^(m_c - M) l_c, chunks in order) to xb[0:d]; blocks H ..: u = gelu(f) for 256 elements each
-// to xb[d:d+dff], f = ya[3d:3d+dff].
-template <typename T, int EPL>
-__global__ __launch_bounds__(256) void attn_combine_gelu_kernel(const float* __restrict__ part, int nsplit, int d,
-                                                                int n_heads, const T* __restrict__ f, int dff,
-                                                                T* __restrict__ xb) {
-  constexpr int dh = 64 * EPL;
-  if ((int)blockIdx.x < n_heads) {
-    const int h = blockIdx.x;
-    if (threadIdx.x >= dh) return;
-    const float* ph = part + (long long)h * nsplit * (dh + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, ph[(long long)c * (dh + 2)]);
+  // hand-off: every wave's stores complete, then one count per block; the last chunk combines
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&cnt[h], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // one device-scope acquire, then ordinary loads: the chunks' maxima and sums through LDS, the
+  // value sums straight from memory, all independent
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __shared__ float s_cm[kMaxAttnSplit], s_cl[kMaxAttnSplit];
+  if ((int)threadIdx.x < nsplit) {
+    s_cm[threadIdx.x] = ph[(long long)threadIdx.x * (dh + 2)];
+    s_cl[threadIdx.x] = ph[(long long)threadIdx.x * (dh + 2) + 1];
+  }
+  __syncthreads();
+  float Mx = -INFINITY;
+  for (int cc = 0; cc < nsplit; ++cc) Mx = fmaxf(Mx, s_cm[cc]);
+  if (threadIdx.x < dh) {
     float num = 0.f, den = 0.f;
-    for (int c = 0; c < nsplit; ++c) {
-      const float* pc = ph + (long long)c * (dh + 2);
-      const float w = expf(pc[0] - M);
-      den = __builtin_fmaf(pc[1], w, den);
-      num = __builtin_fmaf(pc[2 + threadIdx.x], w, num);
+#pragma unroll 8
+    for (int cc = 0; cc < nsplit; ++cc) {
+      const float w = expf(s_cm[cc] - Mx);
+      den = __builtin_fmaf(s_cl[cc], w, den);
+      num = __builtin_fmaf(ph[(long long)cc * (dh + 2) + 2 + threadIdx.x], w, num);
     }
     xb[h * dh + threadIdx.x] = from_f32<T>(num / den);
-    return;
   }
-  const int i = ((int)blockIdx.x - n_heads) * 256 + threadIdx.x;
-  if (i >= dff) return;
-  const float z = to_f32(f[i]);
-  const float u = 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
-  xb[d + i] = from_f32<T>(u);
+  if (threadIdx.x == 0) __hip_atomic_store(&cnt[h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T>
@@ -211,7 +286,10 @@ int attn_splits(int L, int n_heads) {
   return (L + lc - 1) / lc;
 }
 
-size_t attn_ws_bytes(int d, int n_heads) { return (size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4; }
+// partial sums, then one arrival counter per head (zero between launches)
+size_t attn_ws_bytes(int d, int n_heads) {
+  return align256((size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4) + align256((size_t)n_heads * 4);
+}
 
 int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta, int d, void* xa, hipStream_t s) {
   if (d < 1 || d > 16384) return GSI_ERR_SHAPE;
@@ -232,11 +310,10 @@ static void attention_launch(const void* ya, void* kc, void* vc, int pos, int d,
   const int L = pos + 1;
   const int nsplit = attn_splits(L, n_heads);
   const int lc = (L + nsplit - 1) / nsplit;
-  attn_partial_kernel<T, EPL><<<dim3(n_heads, nsplit), 256, 0, s>>>((const T*)ya, (T*)kc, (T*)vc, pos, d, lc, nsplit,
-                                                                     part);
-  const int nb = n_heads + (dff + 255) / 256;
-  attn_combine_gelu_kernel<T, EPL><<<nb, 256, 0, s>>>(part, nsplit, d, n_heads, (const T*)ya + 3 * (long long)d, dff,
-                                                      (T*)xb);
+  int* cnt = (int*)((char*)part + align256((size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4));
+  const unsigned nb = (unsigned)(n_heads * nsplit + (dff + 255) / 256);
+  attn_gelu_kernel<T, EPL><<<nb, 256, 0, s>>>((const T*)ya, (T*)kc, (T*)vc, pos, d, n_heads, lc, nsplit, part, cnt,
+                                               dff, (T*)xb);
 }
 
 int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cache, int pos, int d, int n_heads,
@@ -257,6 +334,20 @@ int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cach
   } else {
     return GSI_ERR_SHAPE;
   }
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+}
+
+int launch_residual_ln(int dtype, void* x, const void* yb, const void* gamma, const void* beta, int d, void* xa,
+                      hipStream_t s) {
+  if (d < 1 || d > 16384) return GSI_ERR_SHAPE;
+  if (dtype == GSI_BF16)
+    residual_ln_kernel<bf16_t><<<1, 1024, 0, s>>>((bf16_t*)x, (const bf16_t*)yb, (const bf16_t*)gamma,
+                                                  (const bf16_t*)beta, d, (bf16_t*)xa);
+  else if (dtype == GSI_F16)
+    residual_ln_kernel<f16_t><<<1, 1024, 0, s>>>((f16_t*)x, (const f16_t*)yb, (const f16_t*)gamma,
+                                                 (const f16_t*)beta, d, (f16_t*)xa);
+  else
+    return GSI_ERR_DTYPE;
   return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 

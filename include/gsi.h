@@ -255,9 +255,10 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
  * xb [d + dff] = [o | u], yb [2 d] = [y_out | y_mlp]; gates [4] uint8 = QKV, fc_in, out, fc_out
  * (1 = slow); rho [4] float32 in the same order, optional (NULL). None of them may overlap.
  * Workspace: gsi_block_step_workspace_bytes, zero-filled before its first use (it holds the
- * batch-1 kernel's exchange state, kept consistent by the library afterwards, and the attention's
- * partial sums); calls on one workspace must not overlap. Arguments are checked before anything
- * is enqueued; the call enqueues five launches on `stream` and returns.
+ * batch-1 kernel's exchange state and the attention's partial sums and per-head arrival counters,
+ * kept consistent by the library afterwards); calls on one workspace must not overlap. Arguments are checked before anything
+ * is enqueued; the call enqueues five launches on `stream` (LayerNorm, stack A, attention with
+ * GELU, stack B, residual add) and returns.
  */
 size_t gsi_block_step_workspace_bytes(const gsi_stack* A, const gsi_stack* B, int n_heads);
 int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
@@ -272,7 +273,8 @@ int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* be
  * hold the last block's intermediates afterwards); gates [n_blocks * 4] and rho [n_blocks * 4]
  * (optional) take each block's four entries in turn. One workspace of
  * gsi_block_step_workspace_bytes of block 0's stacks. Every block's arguments are checked before
- * anything is enqueued; the call enqueues 5 n_blocks launches on `stream` and returns.
+ * anything is enqueued; the call enqueues 4 n_blocks + 1 launches on `stream` (a block's residual
+ * add and the next block's LayerNorm share one) and returns.
  */
 int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
                     const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int n_heads,
