@@ -608,8 +608,10 @@ def decode_step(args, g, torch, np):
     1024-position prefix, GELU, the [out, fc_out] stack, residual add), token after token, each
     block's output feeding the next. The same step with both stacks in the dense site mode (y = W x
     for every site, the same kernels otherwise) is the reference. Tokens/s over --steps tokens
-    (default 48) after --warmup (default 8), one gsi_decode_step call per token, HIP events on the
-    stream the library enqueues on.
+    (default 48) after --warmup (default 8), one gsi_decode_step call per token followed by a
+    synchronisation (decoding is autoregressive: a token's input exists only once the previous
+    token is done), HIP events on the stream the library enqueues on; "queued" gives the rate with
+    the synthetic tokens enqueued back to back.
     Algorithmic bytes per token: per site V_k + M (+ W when slow), W for the dense step, plus the
     attention's key and value rows (2 (pos + 1) d 2 bytes per block)."""
     import dataclasses
@@ -655,7 +657,7 @@ def decode_step(args, g, torch, np):
     Vs = [hb["V"] for hb in model["blocks"]]
     gates = gates.view(n_tok, cfg.n_blocks * 4)
 
-    def run(dense):
+    def run(dense, sync_each=True):
         for b, hb in enumerate(model["blocks"]):
             hb["K"].copy_(K0[b])
             hb["V"].copy_(V0[b])
@@ -663,18 +665,25 @@ def decode_step(args, g, torch, np):
         sa, sb = ("Ad", "Bd") if dense else ("A", "B")
         A = [blk[sa] for blk in blocks]
         B = [blk[sb] for blk in blocks]
+        h0 = 0.0
         for t in range(n_tok):
             if t == n_warm:
                 ev0.record(stream)
-            # one call per token: the library enqueues the 28 blocks' 140 launches
+                h0 = time.perf_counter()
+            # one call per token: the library enqueues the blocks' 4 n_blocks + 1 launches
             g.gsi_decode_step(A, B, gam, bet, Ks, Vs, cfg.L0 + t, H, cfg.eps, xs[t], xa, ya, xb, yb, gates[t], None, ws)
+            if sync_each:  # autoregressive: the next token's input exists only after this token
+                torch.cuda.synchronize()
+        host = (time.perf_counter() - h0) / n_time
         ev1.record(stream)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / 1e3 / n_time, xs
+        return ev0.elapsed_time(ev1) / 1e3 / n_time, xs, host
 
-    t_gsi, xs = run(False)
+    t_gsi, xs, host_gsi = run(False)
+    t_gsi_q, _, _ = run(False, sync_each=False)
     gt = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)  # [QKV, fc_in, out, fc_out]
-    t_dense, _ = run(True)
+    t_dense, _, host_dense = run(True)
+    t_dense_q, _, _ = run(True, sync_each=False)
     assert g.gsi_workspace_status(ws) == 0
     # algorithmic bytes of the timed tokens
     shapes = {"qkv": (3 * d, d), "fc_in": (dff, d), "out": (d, d), "fc_out": (d, dff)}
@@ -728,6 +737,9 @@ def decode_step(args, g, torch, np):
            "dense_step": {"value": round(1.0 / t_dense, 2), "ms_per_step": round(t_dense * 1e3, 4),
                           "achieved_gbps": round(dense_b / t_dense / 1e9, 1), "bytes_per_step": round(dense_b)},
            "speedup_vs_dense": round(t_dense / t_gsi, 3),
+           # the given tokens enqueued without waiting between them (not autoregressive)
+           "queued": {"value": round(1.0 / t_gsi_q, 2), "ms_per_step": round(t_gsi_q * 1e3, 4),
+                      "dense_value": round(1.0 / t_dense_q, 2)},
            "cpu_baseline": cpu}
     for blk in blocks:
         for key in ("A", "B", "Ad", "Bd"):
