@@ -250,7 +250,7 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
  * threshold eps through the batch-1 kernel for one token, as an ordinary launch of its co-resident
  * grid (a cooperative launch would add a queue switch before and after each of the two).
  * Buffers (device, 16-byte aligned, the caller's): gamma, beta [d]; x [d]; k_cache, v_cache
- * [>= pos + 1, d] row-major (rows 0 .. pos - 1 are read, row pos is written); the step's
+ * [>= pos + 1, d] row-major, 0 <= pos < 2^24 (rows 0 .. pos - 1 are read, row pos is written); the step's
  * intermediates, readable after the call: xa [2 d] = [a | a], ya [3 d + dff] = [q | k | v | f],
  * xb [d + dff] = [o | u], yb [2 d] = [y_out | y_mlp]; gates [4] uint8 = QKV, fc_in, out, fc_out
  * (1 = slow); rho [4] float32 in the same order, optional (NULL). None of them may overlap.
