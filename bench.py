@@ -337,6 +337,12 @@ def batched(args, cfg, g, torch, np):
         times.append(ev0.elapsed_time(ev1) / 1e3)
     if g.gsi_workspace_status(ws) != 0:
         raise SystemExit("batched path reported a wait timeout")
+    if args.copy_calibration:  # reference kernel for the HBM counters: a 1 GiB device copy
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b2 = torch.empty_like(a)
+        b2.copy_(a)
+        torch.cuda.synchronize()
+        del a, b2
     times.sort()
     t_gpu = times[len(times) // 2]
     gs = torch.cat(slow_steps).cpu().numpy().astype(bool)          # [steps, T, sites]
@@ -363,6 +369,8 @@ def batched(args, cfg, g, torch, np):
         "sites_with_slow_tokens": round(float(any_slow.mean()), 4),
         "cpu_baseline": None,
     }
+    tr, tr_src = measured_traffic_batched(cfg)
+    out["roofline"]["traffic"], out["roofline"]["traffic_source"] = tr, tr_src
     stack.destroy()
     torch.cuda.synchronize()
     return out
@@ -819,6 +827,29 @@ def decode_kernel_name(cfg) -> str:
     need = max((s.d * es // 16 + 255) // 256 for s in cfg.sites)
     t = {"f32": "float", "f16": "gsi::f16_t", "bf16": "gsi::bf16_t"}[cfg.dtype]
     return f"gsi::decode_kernel<{t}, {2 if need <= 2 else 8}>"
+
+
+def batched_sources_sha256() -> str:
+    """sha256 over the sources of the batched path's kernels and its driver."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("gsi_dense.hip", "gsi_api.cpp", "gsi_internal.h"):
+        h.update(open(os.path.join(ROOT, "gated_rank_linear_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic_batched(cfg):
+    """HBM bytes per step of the batched path (all its launches) from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a 1 GiB copy); (None,
+    reason) when the sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "batched_path_gptj_t64_bf16.traffic.json")
+    if cfg.cid != 5 or not os.path.exists(path):
+        return None, "no counter run for this workload"
+    rec = json.load(open(path))
+    if batched_sources_sha256() != rec.get("sources_sha256"):
+        return None, "batched path changed since the committed counter run"
+    return rec["traffic_bytes_per_step"], "rocprofv3 FETCH_SIZE + WRITE_SIZE per step of the committed profile run, copy-calibrated"
 
 
 def decode_sources_sha256() -> str:
