@@ -91,7 +91,7 @@ def main():
         calibration(args, g, torch, np)
         return
     if args.step:
-        decode_step(args, g, torch, np)
+        print(json.dumps(decode_step(args, g, torch, np)), flush=True)
         return
     cfg = synth.get(args.config)
     if cfg.t_step != 1:
@@ -104,9 +104,11 @@ def main():
 
 
 def extra_workloads(args, g, torch, np) -> dict:
-    """Two more workloads timed in the same run, each with its own bytes and roofline fraction:
-    the shared-input GPT-J-shaped stack (batch 1, q/k/v and fc_in as one site) and the T = 64
-    batched workload (k = 512, ~20% slow tokens per step)."""
+    """Three more workloads timed in the same run, each with its own bytes and roofline fraction:
+    the shared-input GPT-J-shaped stack (batch 1, q/k/v and fc_in as one site), the T = 64
+    batched workload (k = 512, ~20% slow tokens per step) and the decode step (the GSI sites of a
+    GPT-J-shaped model around an unchanged plain attention, against the same step with dense
+    sites)."""
     import argparse
     import gc
 
@@ -125,6 +127,14 @@ def extra_workloads(args, g, torch, np) -> dict:
     res["gptj_batched_t64"] = {k: o5[k] for k in ("value", "unit", "ms_per_step", "roofline", "slow_fraction",
                                                     "sites_with_slow_tokens")}
     res["gptj_batched_t64"]["workload"] = o5["config"]["workload"]
+    gc.collect()
+    torch.cuda.empty_cache()
+    a7 = argparse.Namespace(**vars(args))
+    a7.steps, a7.warmup, a7.no_cpu_baseline = 48, 8, True
+    o7 = decode_step(a7, g, torch, np)
+    res["gptj_decode_step"] = {k: o7[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction",
+                                                   "dense_step", "speedup_vs_dense")}
+    res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
     gc.collect()
     torch.cuda.empty_cache()
     return res
@@ -753,7 +763,7 @@ def decode_step(args, g, torch, np):
         for key in ("A", "B", "Ad", "Bd"):
             blk[key].destroy()
     torch.cuda.synchronize()
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def synth_weight(cfg, si):
