@@ -270,9 +270,10 @@ int gsi_layer_create(gsi_layer** out, int dtype, int d_out, int d, int k, const 
   }
   // V^T (k x d) and the decode plan, then M = W V = W (V^T)^T and V^T V - I   [GSI §2.1]; for the
   // batched gate also (V (V^T V - I))^T = (V^T V - I) V^T, row j of it = sum_l D[j][l] V[:, l]
+  const void* dd = nullptr;
   if ((rc = launch_transpose(dtype, V, Vt, d, k, L->desc, L->P, L->plan, s)) != GSI_OK ||
-      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK ||
-      (L->desc.VDt && (rc = launch_vdt(dtype, Dl, V, (void*)L->desc.VDt, d, k, ws, ws ? ws_nbytes : 0, s)) != GSI_OK)) {
+      (rc = launch_precompute(dtype, W, Vt, M, Dl, d_out, d, k, ws, ws ? ws_nbytes : 0, &dd, s)) != GSI_OK ||
+      (L->desc.VDt && (rc = launch_vdt(dtype, Dl, dd, V, (void*)L->desc.VDt, d, k, s)) != GSI_OK)) {
     delete L;
     return rc;
   }

@@ -5,6 +5,7 @@
 #include "gsi_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gsi {
 
@@ -580,12 +581,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // eight sums added in a fixed tree, rounded to TC. Blocks from nb_img on: rows of V^T V (n x n),
 // eight threads per four columns, thread u summing chunks u, u + 8, ... of the sd chunks at pd
 // (chunk stride cd), the eight threads' sums added in a fixed butterfly; stored to Dl as float32
-// with I subtracted. Results do not depend on timing.
+// with I subtracted and, when DD is given, also split into two parts of TC, hi = round(v) and
+// lo = round(v - hi), stored as row r of DD = [hi | lo] (n x 2n). Results do not depend on timing.
 template <typename TC>
 __global__ __launch_bounds__(256) void precompute_reduce_kernel(const float* __restrict__ pw, int sw, long long cw,
                                                                 const float* __restrict__ pd, int sd, long long cd,
                                                                 int m_img, int n, void* __restrict__ M,
-                                                                float* __restrict__ Dl, int nb_img) {
+                                                                float* __restrict__ Dl, TC* __restrict__ DD,
+                                                                int nb_img) {
   if ((int)blockIdx.x < nb_img) {
     const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
     if (q >= (long long)m_img * (n / 4)) return;
@@ -651,7 +654,15 @@ __global__ __launch_bounds__(256) void precompute_reduce_kernel(const float* __r
   }
   if (valid && u == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Dl[(long long)r * n + n4 + e] = acc[e] - (r == n4 + e ? 1.0f : 0.0f);
+    for (int e = 0; e < 4; ++e) {
+      const float v = acc[e] - (r == n4 + e ? 1.0f : 0.0f);
+      Dl[(long long)r * n + n4 + e] = v;
+      if (DD) {
+        const TC hi = from_f32<TC>(v);
+        DD[(long long)r * 2 * n + n4 + e] = hi;
+        DD[(long long)r * 2 * n + n + n4 + e] = from_f32<TC>(v - to_f32(hi));
+      }
+    }
   }
 }
 
@@ -935,33 +946,59 @@ __global__ __launch_bounds__(256) void gemm_nt_wide_kernel(const void* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
-// Split-K partial products of the create-time precompute ([W; V^T] (V^T)^T and V^T V): a
-// 128 x 256 output tile per block of 8 waves, two waves per SIMD; wave w owns rows
-// 64 (w / 4) .. + 63 and columns 64 (w mod 4) .. + 63 of the tile (64 accumulator registers per
-// lane). Copies, operand blocks, swizzle and stages as in gemm_nt_wide_kernel (48 blocks of 1 KB
-// per 64-column step, 6 copies per wave). Block z covers K columns [z k_chunk, (z + 1) k_chunk)
-// and stores its raw float32 sums to part[z][m][n]; rows from m_split on come from A2.
+// Products of the create-time precompute ([W; V^T] (V^T)^T and V^T V split over K, and
+// (V^T V - I) V^T): a 128 x 256 output tile per block of 8 waves, two waves per SIMD; wave w owns
+// rows 64 (w / 4) .. + 63 and columns 64 (w mod 4) .. + 63 of the tile (16 tiles of
+// v_mfma_f32_16x16x32, 64 accumulator registers per lane). Operands are copied straight into LDS
+// (global_load_lds_dwordx4) in blocks of 1 KB = 8 rows x 128 bytes of a 64-column K step, with
+// the block layout and xor swizzle of gemm_nt_wide_kernel, so operand reads are one conflict-free
+// 16-byte LDS read per lane. One copy ring per operand: waves 0-3 copy only A (16 blocks per K
+// step, 4 copies per wave) into RA stages, waves 4-7 only B (32 blocks, 8 copies per wave) into
+// RB stages; each group waits on its own copies (A issued RA - 1 steps ahead, B RB - 1), and the
+// barrier after the waits joins them. B's column index wraps at kwrap_b (its kwrap_b columns
+// serve an A with kdim = a multiple of them). Rows from m_split on come from A2. Block z covers K
+// columns [z k_chunk, (z + 1) k_chunk); with C given (one K chunk) results are rounded to T and
+// stored to C (row stride ldc), otherwise raw float32 sums go to part[z][m][n].
 // ---------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(512) void gemm_nt_wide8_kernel(const void* __restrict__ A, const void* __restrict__ A2,
-                                                            int m_split, long long lda,
-                                                            const void* __restrict__ B, long long ldb, int m, int n,
-                                                            int kdim, int k_chunk, float* __restrict__ part) {
-  constexpr int NA = 16, NB = NA + 32, CPW = NB / 8;
-  __shared__ mu32x4 st0[NB * 64], st1[NB * 64], st2[NB * 64];
+constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
+
+template <int I, int L, typename F>
+__device__ __forceinline__ void unroll_steps(F&& f) {
+  if constexpr (I < L) {
+    f(std::integral_constant<int, I>{});
+    unroll_steps<I + 1, L>(f);
+  }
+}
+
+template <typename T, int RA, int RB>
+__global__ __launch_bounds__(512) void gemm_nt_ring_kernel(const void* __restrict__ A, const void* __restrict__ A2,
+                                                           int m_split, long long lda, const void* __restrict__ B,
+                                                           long long ldb, int kwrap_b, int m, int n, int kdim,
+                                                           int k_chunk, float* __restrict__ part, void* __restrict__ C,
+                                                           long long ldc) {
+  static_assert(RA >= 2 && RA <= 6 && RB >= 2 && RB <= 3 && RA + RB <= 8, "ring depths");
+  constexpr int CA = 4, CB = 8;  // copies per wave and K step
+  // one LDS object per ring slot: the compiler then knows which copies a slot's reads wait for
+  // (with one array and a run-time slot it would wait for every copy in flight before any read)
+  __shared__ mu32x4 sa0[16 * 64], sa1[16 * 64], sa2[RA > 2 ? 16 * 64 : 1], sa3[RA > 3 ? 16 * 64 : 1],
+      sa4[RA > 4 ? 16 * 64 : 1], sa5[RA > 5 ? 16 * 64 : 1];
+  __shared__ mu32x4 sb0[32 * 64], sb1[32 * 64], sb2[RB > 2 ? 32 * 64 : 1];
   const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 256;
   if (m0 >= m) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave >> 2, wc = wave & 3;
-  const T* src[CPW];
+  const bool copies_a = wave < 4;
+  // copy t of this wave fills operand block q = (wave mod 4) + 4 t of its operand: row
+  // 8 q + ((l / 8) xor (q mod 2)), 16-byte chunk (l mod 8) xor (row mod 8) for lane l
+  const T* src[CB];
 #pragma unroll
-  for (int t = 0; t < CPW; ++t) {
-    const int qd = wave + 8 * t;
-    const int qo = qd < NA ? qd : qd - NA;
-    const int r = 8 * qo + ((lane >> 3) ^ (qo & 1));
+  for (int t = 0; t < CB; ++t) {
+    const int q = (wave & 3) + 4 * t;
+    const int r = 8 * q + ((lane >> 3) ^ (q & 1));
     const int ko = 8 * ((lane & 7) ^ (r & 7));
-    if (qd < NA) {
-      const int mm = m0 + r;
+    if (copies_a) {
+      const int mm = m0 + (t < CA ? r : 0);
       const long long row = mm < m ? mm : 0;
       const T* abase = row < m_split ? reinterpret_cast<const T*>(A) + row * lda
                                      : reinterpret_cast<const T*>(A2) + (row - m_split) * lda;
@@ -979,49 +1016,88 @@ __global__ __launch_bounds__(512) void gemm_nt_wide8_kernel(const void* __restri
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
-#define GSI_W8ISSUE(STAGE, K0)                                                                         \
-  do {                                                                                                 \
-    _Pragma("unroll") for (int t = 0; t < CPW; ++t) __builtin_amdgcn_global_load_lds(                  \
-        (const void*)(src[t] + (K0)), (dlds_void*)((dlu32x4*)(STAGE) + (wave + 8 * t) * 64), 16, 0, 0); \
-  } while (0)
-#define GSI_W8COMPUTE(STAGE)                                                                           \
-  do {                                                                                                 \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
-      mu32x4 af[4], bf[4];                                                                             \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
-        af[i] = ((const dlu32x4*)(STAGE))[2 * (4 * wr + i) * 64 + rd[u]];                             \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-        bf[j] = ((const dlu32x4*)(STAGE))[(NA + 2 * (4 * wc + j)) * 64 + rd[u]];                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]); \
-    }                                                                                                  \
-  } while (0)
-// every step issues exactly CPW copies per wave (past the last stage they re-read the last K step
-// into a stage nobody reads again), so waiting until at most CPW remain completes the current one
-#define GSI_W8STEP(CUR, FUT, ST)                                                                        \
-  do {                                                                                                 \
-    dwait_vmcnt<CPW>();                                                                                \
-    dlds_barrier();                                                                                    \
-    GSI_W8ISSUE(FUT, kb + min((ST) + 2, nk - 1) * 64);                                                 \
-    GSI_W8COMPUTE(CUR);                                                                                \
-  } while (0)
   const int kb = (int)blockIdx.z * k_chunk;
   const int nk = (min(kdim, kb + k_chunk) - kb) / 64;  // >= 1: the launch checks the split
-  GSI_W8ISSUE(st0, kb);
-  GSI_W8ISSUE(st1, kb + min(1, nk - 1) * 64);
-  int s0 = 0;
-  for (; s0 + 3 <= nk; s0 += 3) {
-    GSI_W8STEP(st0, st2, s0);
-    GSI_W8STEP(st1, st0, s0 + 1);
-    GSI_W8STEP(st2, st1, s0 + 2);
-  }
-  if (s0 < nk) GSI_W8STEP(st0, st2, s0);
-  if (s0 + 1 < nk) GSI_W8STEP(st1, st0, s0 + 1);
-  dwait_vmcnt<0>();  // no copy may land in LDS after the block ends
-#undef GSI_W8STEP
-#undef GSI_W8COMPUTE
-#undef GSI_W8ISSUE
-  float* pz = part + (long long)blockIdx.z * m * n;
+  const int wave4 = wave & 3;
+  auto slot_a = [&](auto ic) -> dlu32x4* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return (dlu32x4*)sa0;
+    else if constexpr (i == 1) return (dlu32x4*)sa1;
+    else if constexpr (i == 2) return (dlu32x4*)sa2;
+    else if constexpr (i == 3) return (dlu32x4*)sa3;
+    else if constexpr (i == 4) return (dlu32x4*)sa4;
+    else return (dlu32x4*)sa5;
+  };
+  auto slot_b = [&](auto ic) -> dlu32x4* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return (dlu32x4*)sb0;
+    else if constexpr (i == 1) return (dlu32x4*)sb1;
+    else return (dlu32x4*)sb2;
+  };
+  auto issue_a = [&](int step, dlu32x4* dst) {
+#pragma unroll
+    for (int t = 0; t < CA; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(src[t] + kb + step * 64), (dlds_void*)(dst + (wave4 + 4 * t) * 64),
+                                       16, 0, 0);
+  };
+  auto issue_b = [&](int step, dlu32x4* dst) {
+    const int kbb = (kb + step * 64) % kwrap_b;
+#pragma unroll
+    for (int t = 0; t < CB; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(src[t] + kbb), (dlds_void*)(dst + (wave4 + 4 * t) * 64), 16, 0, 0);
+  };
+  constexpr int DA = RA - 1, DB = RB - 1;  // steps issued ahead
+  constexpr int L = RA * RB / ring_gcd(RA, RB);  // the slots repeat after L steps
+  // the K loop, once per copy group: each copy of it holds only its group's copies (the waits
+  // the compiler adds for LDS reads then see only the copies this wave can have in flight) and
+  // both pass the same barriers
+  auto k_loop = [&](auto group) {
+    constexpr bool kA = decltype(group)::value;
+    constexpr int D = kA ? DA : DB;
+    // every step issues exactly its copies (past the last K step they re-read that step into a
+    // slot nobody reads again), so one fixed wait completes the current step: the copies of the
+    // D - 1 later steps may stay in flight
+    auto refill = [&](int step, auto slot) {
+      if constexpr (kA)
+        issue_a(min(step, nk - 1), slot_a(slot));
+      else
+        issue_b(min(step, nk - 1), slot_b(slot));
+    };
+    unroll_steps<0, D>([&](auto ic) { refill(decltype(ic)::value, ic); });
+    auto step = [&](auto ic, int s) {
+      constexpr int I = decltype(ic)::value;  // s mod L
+      dwait_vmcnt<(kA ? CA : CB) * (D - 1)>();
+      dlds_barrier();
+      // refill the slot every wave finished reading in step s - 1
+      refill(s + D, std::integral_constant<int, (I + D) % (kA ? RA : RB)>{});
+      const dlu32x4* pa = slot_a(std::integral_constant<int, I % RA>{});
+      const dlu32x4* pb = slot_b(std::integral_constant<int, I % RB>{});
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        mu32x4 af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = pa[2 * (4 * wr + i) * 64 + rd[u]];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = pb[2 * (4 * wc + j) * 64 + rd[u]];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op<T>::run(af[i], bf[j], acc[i][j]);
+      }
+    };
+    // whole groups of L steps, then the last nk mod L (kept apart so the loop body has no
+    // data-dependent step: the waits the compiler derives for it then match the fixed ones)
+    int s0 = 0;
+    for (; s0 + L <= nk; s0 += L) unroll_steps<0, L>([&](auto ic) { step(ic, s0 + decltype(ic)::value); });
+    unroll_steps<0, L - 1>([&](auto ic) {
+      if (s0 + decltype(ic)::value < nk) step(ic, s0 + decltype(ic)::value);
+    });
+  };
+  if (copies_a)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
+  dwait_vmcnt<0>();  // every copy was waited for above; kept so no copy can outlive the block
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1029,7 +1105,13 @@ __global__ __launch_bounds__(512) void gemm_nt_wide8_kernel(const void* __restri
       const int mm = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
       if (mm >= m) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pz[(long long)mm * n + n0 + wc * 64 + j * 16 + (lane & 15)] = acc[i][j][r];
+      for (int j = 0; j < 4; ++j) {
+        const int nn = n0 + wc * 64 + j * 16 + (lane & 15);
+        if (C)
+          reinterpret_cast<T*>(C)[(long long)mm * ldc + nn] = from_f32<T>(acc[i][j][r]);
+        else
+          part[((long long)blockIdx.z * m + mm) * n + nn] = acc[i][j][r];
+      }
     }
 }
 
@@ -1499,9 +1581,10 @@ struct PrecomputePlan {
 
 static int best_splits(long long tiles, int d) {
   // the most chunks (a power of two) that keep tiles x chunks within 256 blocks, with every chunk
-  // at least 64 columns and a whole number of 64-column steps
+  // at least 256 columns (four K steps: fewer partial sums to add, and copy rings that fill) and a
+  // whole number of 64-column steps
   int sp = 1;
-  while (tiles * sp * 2 <= 256 && d % (2 * sp) == 0 && d / (2 * sp) >= 64 && (d / (2 * sp)) % 64 == 0) sp *= 2;
+  while (tiles * sp * 2 <= 256 && d % (2 * sp) == 0 && d / (2 * sp) >= 256 && (d / (2 * sp)) % 64 == 0) sp *= 2;
   return sp;
 }
 
@@ -1529,62 +1612,62 @@ static PrecomputePlan precompute_plan(int dtype, int d_out, int d, int k) {
 
 int precompute_splits(int dtype, int d_out, int d, int k) { return precompute_plan(dtype, d_out, d, k).sm; }
 
-// the (V^T V - I) V^T product on matrix cores: D split into 16-bit high and low rows, one
-// product for both ([D_hi; D_lo] against V's rows, float32 sums), then their sum in that order
+// (V^T V - I) V^T on matrix cores: D = V^T V - I split into 16-bit high and low parts by the
+// precompute reduction, stored as DD = [D_hi | D_lo] (k x 2k), and one product of DD against V's
+// rows with V's k columns used twice (every product exact, float32 sums), rounded to the dtype
 static bool vdt_on_mfma(int dtype, int d, int k) { return dtype != GSI_F32 && d % 256 == 0 && k % 64 == 0 && k >= 64; }
-static size_t vdt_ws_bytes(int dtype, int d, int k) {
-  if (!vdt_on_mfma(dtype, d, k)) return 0;
-  return align256((size_t)2 * k * d * 4) + align256((size_t)2 * k * k * 2);
+static size_t dd_bytes(int dtype, int d, int k) {
+  return vdt_on_mfma(dtype, d, k) ? align256((size_t)2 * k * k * 2) : 0;
 }
 
+// create workspace: [DD][K-chunk partials of M (or [M; V^T V])][K-chunk partials of V^T V]
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k) {
   const PrecomputePlan pl = precompute_plan(dtype, d_out, d, k);
   if (pl.sm == 0) return 0;
   const size_t img = (size_t)pl.sm * (pl.fused ? d_out + k : d_out) * k * 4;
   const size_t gram = pl.fused ? 0 : (size_t)pl.sd * k * k * 4;
-  return std::max((img + 255) / 256 * 256 + (gram + 255) / 256 * 256, vdt_ws_bytes(dtype, d, k));
+  return dd_bytes(dtype, d, k) + align256(img) + align256(gram);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ D, long long n, T* __restrict__ hi,
-                                                         T* __restrict__ lo) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    const float v = D[i];
-    const T h = from_f32<T>(v);
-    hi[i] = h;
-    lo[i] = from_f32<T>(v - to_f32(h));
-  }
-}
+// depths of the two copy rings of gemm_nt_ring_kernel (A steps, B steps; 16 KB and 32 KB each)
+constexpr int kRingA = 4, kRingB = 3;
 
-static int launch_wide_partials(int dtype, const void* A, const void* A2, int m_split, const void* B, int m, int n,
-                                int kdim, int splits, float* part, hipStream_t s) {
-  void* fn = dtype == GSI_BF16 ? (void*)gemm_nt_wide8_kernel<bf16_t> : (void*)gemm_nt_wide8_kernel<f16_t>;
+static int launch_ring(int dtype, const void* A, const void* A2, int m_split, long long lda, const void* B,
+                       long long ldb, int kwrap_b, int m, int n, int kdim, int splits, float* part, void* C,
+                       long long ldc, hipStream_t s) {
+  void* fn = dtype == GSI_BF16 ? (void*)gemm_nt_ring_kernel<bf16_t, kRingA, kRingB>
+                               : (void*)gemm_nt_ring_kernel<f16_t, kRingA, kRingB>;
   int k_chunk = kdim / splits;
-  // every block needs at least one whole 64-column step of K, and n whole 256-column tiles
-  if (splits < 1 || kdim % splits != 0 || k_chunk % 64 != 0 || k_chunk < 64 || n % 256 != 0) return GSI_ERR_SHAPE;
-  long long lda = kdim, ldb = kdim;
+  // every block needs at least one whole 64-column step of K, n whole 256-column tiles, and B
+  // steps that do not straddle its wrap
+  if (splits < 1 || kdim % splits != 0 || k_chunk % 64 != 0 || k_chunk < 64 || n % 256 != 0 || kwrap_b % 64 != 0 ||
+      kdim % kwrap_b != 0 || (C && splits != 1) || (!C && !part))
+    return GSI_ERR_SHAPE;
   dim3 grid((m + 127) / 128, n / 256, splits);
-  void* args[] = {&A, &A2, &m_split, &lda, &B, &ldb, &m, &n, &kdim, &k_chunk, &part};
+  void* args[] = {&A, &A2, &m_split, &lda, &B, &ldb, &kwrap_b, &m, &n, &kdim, &k_chunk, &part, &C, &ldc};
   return hipLaunchKernel(fn, grid, dim3(512), args, 0, s) == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
-// With the workspace: the split products above, then one reduction that rounds M and subtracts
-// I from V^T V. Without: the single-pass kernels.
+// With the workspace: the split products above, then one reduction that rounds M, subtracts I
+// from V^T V and (16-bit layers) writes DD for launch_vdt (*dd then points to it). Without: the
+// single-pass kernels (*dd = null).
 int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
-                      void* ws, size_t ws_bytes, hipStream_t s) {
+                      void* ws, size_t ws_bytes, const void** dd, hipStream_t s) {
+  *dd = nullptr;
   const PrecomputePlan pl = precompute_plan(dtype, d_out, d, k);
   if (ws && pl.sm > 0 && precompute_ws_bytes(dtype, d_out, d, k) <= ws_bytes) {
-    float* pw = (float*)ws;
+    const size_t ddb = dd_bytes(dtype, d, k);
+    float* pw = (float*)((char*)ws + ddb);
     const int m_img = pl.fused ? d_out + k : d_out;
-    int rc = launch_wide_partials(dtype, W, Vt, d_out, Vt, m_img, k, d, pl.sm, pw, s);
+    int rc = launch_ring(dtype, W, Vt, d_out, d, Vt, d, d, m_img, k, d, pl.sm, pw, nullptr, 0, s);
     if (rc != GSI_OK) return rc;
     const long long cw = (long long)m_img * k;
     const float* pd = pw + (long long)d_out * k;  // fused: the V^T V rows follow the image rows
     long long cd = cw;
     int sd = pl.sm;
     if (!pl.fused) {
-      float* pg = (float*)((char*)ws + ((size_t)pl.sm * d_out * k * 4 + 255) / 256 * 256);
-      rc = launch_wide_partials(dtype, Vt, Vt, k, Vt, k, k, d, pl.sd, pg, s);
+      float* pg = (float*)((char*)pw + align256((size_t)pl.sm * d_out * k * 4));
+      rc = launch_ring(dtype, Vt, Vt, k, d, Vt, d, d, k, k, d, pl.sd, pg, nullptr, 0, s);
       if (rc != GSI_OK) return rc;
       pd = pg;
       cd = (long long)k * k;
@@ -1593,39 +1676,23 @@ int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* 
     const int nb_img = (int)(((long long)d_out * (k / 4) + 255) / 256);
     const int nb_gram = (int)(((long long)k * (k / 4) * 8 + 255) / 256);
     const unsigned nb = (unsigned)(nb_img + nb_gram);
+    void* ddp = ddb ? ws : nullptr;
     if (dtype == GSI_BF16)
-      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, nb_img);
+      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, (bf16_t*)ddp, nb_img);
     else
-      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, nb_img);
-    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
+      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(pw, pl.sm, cw, pd, sd, cd, d_out, k, M, Dl, (f16_t*)ddp, nb_img);
+    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
+    *dd = ddp;
+    return GSI_OK;
   }
   const int rc = launch_gemm_nt(dtype, dtype, dtype, W, d, nullptr, Vt, d, M, k, nullptr, d_out, k, d, nullptr, 0, s);
   if (rc != GSI_OK) return rc;
   return launch_gemm_nt(dtype, dtype, GSI_F32, Vt, d, nullptr, Vt, d, Dl, k, nullptr, k, k, d, nullptr, 1, s);
 }
 
-int launch_vdt(int dtype, const float* Dl, const void* V, void* VDt, int d, int k, void* ws, size_t ws_bytes,
-               hipStream_t s) {
-  if (ws && vdt_on_mfma(dtype, d, k) && vdt_ws_bytes(dtype, d, k) <= ws_bytes) {
-    float* part = (float*)ws;  // [2k][d]: rows D_hi V^T, then D_lo V^T
-    char* dh = (char*)ws + align256((size_t)2 * k * d * 4);
-    char* dl = dh + (size_t)k * k * 2;
-    const long long kk = (long long)k * k;
-    const unsigned sb = (unsigned)std::min<long long>(1024, (kk + 255) / 256);
-    if (dtype == GSI_BF16)
-      split_rows_kernel<bf16_t><<<sb, 256, 0, s>>>(Dl, kk, (bf16_t*)dh, (bf16_t*)dl);
-    else
-      split_rows_kernel<f16_t><<<sb, 256, 0, s>>>(Dl, kk, (f16_t*)dh, (f16_t*)dl);
-    if (hipGetLastError() != hipSuccess) return GSI_ERR_HIP;
-    int rc = launch_wide_partials(dtype, dh, dl, k, V, 2 * k, d, k, 1, part, s);
-    if (rc != GSI_OK) return rc;
-    const int nb = (int)(((long long)k * (d / 4) + 255) / 256);
-    if (dtype == GSI_BF16)
-      precompute_reduce_kernel<bf16_t><<<nb, 256, 0, s>>>(part, 2, (long long)k * d, nullptr, 0, 0, k, d, VDt, nullptr, nb);
-    else
-      precompute_reduce_kernel<f16_t><<<nb, 256, 0, s>>>(part, 2, (long long)k * d, nullptr, 0, 0, k, d, VDt, nullptr, nb);
-    return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
-  }
+int launch_vdt(int dtype, const float* Dl, const void* dd, const void* V, void* VDt, int d, int k, hipStream_t s) {
+  if (dd && vdt_on_mfma(dtype, d, k))  // row j: sum over K < 2k of DD[j][K] V[:, K mod k]
+    return launch_ring(dtype, dd, dd, k, 2LL * k, V, k, k, k, d, 2 * k, 1, nullptr, VDt, d, s);
   // row j of (V (V^T V - I))^T = sum_l D[j][l] V[:, l]: D against V's rows
   return launch_gemm_nt(GSI_F32, dtype, dtype, Dl, k, nullptr, V, k, VDt, d, nullptr, k, d, k, nullptr, 0, s);
 }
@@ -1704,32 +1771,53 @@ int launch_gemm_nt_split(int a_type, int b_type, int c_type, const void* A, long
 }
 
 // ---------------------------------------------------------------------------------------------
-// dst[k, d] = transpose(src[d, k]), 32x32 tiles through LDS
+// dst[k, d] = transpose(src[d, k]), 64 x 64 tiles through LDS. A whole tile is read and written
+// in 16-byte pieces (rows of both matrices are whole multiples of 16 bytes: d and k are multiples
+// of 8); tiles cut by the matrix edge (d or k not a multiple of 64) go element by element.
 // ---------------------------------------------------------------------------------------------
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst, int d, int k,
                                                         LayerDesc desc, int P, PlanRow* __restrict__ plan) {
-  __shared__ E t[32][33];
+  constexpr int T = 64, VE = 16 / (int)sizeof(E), CPR = T / VE;  // elements per piece, pieces per tile row
+  __shared__ E t[T][T + 2];
   // block (0, 0) also writes the decode kernel's plan rows of the layer (one per grid block)
   if (plan && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < P)
     plan[threadIdx.x] = make_plan_row(desc, threadIdx.x, P, (int)sizeof(E));
-  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;  // src rows r (d), cols c (k)
-  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
-  for (int i = ty; i < 32; i += 8) {
-    int r = r0 + i, c = c0 + tx;
-    if (r < d && c < k) t[i][tx] = src[(long long)r * k + c];
+  const int c0 = blockIdx.x * T, r0 = blockIdx.y * T;  // src rows r (d), cols c (k)
+  if (r0 + T <= d && c0 + T <= k) {
+    for (int q = threadIdx.x; q < T * CPR; q += 256) {
+      const int r = q / CPR, c = (q % CPR) * VE;
+      const mu32x4 v = *reinterpret_cast<const mu32x4*>(src + (long long)(r0 + r) * k + c0 + c);
+      const E* e = reinterpret_cast<const E*>(&v);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) t[r][c + i] = e[i];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < T * CPR; q += 256) {
+      const int c = q / CPR, r = (q % CPR) * VE;
+      mu32x4 v;
+      E* e = reinterpret_cast<E*>(&v);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) e[i] = t[r + i][c];
+      *reinterpret_cast<mu32x4*>(dst + (long long)(c0 + c) * d + r0 + r) = v;
+    }
+    return;
+  }
+  for (int q = threadIdx.x; q < T * T; q += 256) {
+    const int r = q / T, c = q % T;
+    if (r0 + r < d && c0 + c < k) t[r][c] = src[(long long)(r0 + r) * k + c0 + c];
   }
   __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    int c = c0 + i, r = r0 + tx;
-    if (r < d && c < k) dst[(long long)c * d + r] = t[tx][i];
+  for (int q = threadIdx.x; q < T * T; q += 256) {
+    const int c = q / T, r = q % T;
+    if (r0 + r < d && c0 + c < k) dst[(long long)(c0 + c) * d + r0 + r] = t[r][c];
   }
 }
 
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, const LayerDesc& desc, int P,
                      PlanRow* plan, hipStream_t s) {
   if (plan && (P < 1 || P > 256)) return GSI_ERR_DEVICE;
-  dim3 grid((k + 31) / 32, (d + 31) / 32);
+  dim3 grid((k + 63) / 64, (d + 63) / 64);
   if (dtype == GSI_F32)
     transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, d, k, desc, P, plan);
   else

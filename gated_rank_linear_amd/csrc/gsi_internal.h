@@ -151,13 +151,14 @@ int launch_gemm_nt(int a_type, int b_type, int c_type, const void* A, long long 
                    const int* m_count, int sub_identity, hipStream_t s);
 // Create-time products M = W V and V^T V - I (float32); with a workspace of at least
 // precompute_ws_bytes() they run split over K with fixed-order reductions (0: no workspace used)
+// and, for 16-bit weights, *dd receives the split D = V^T V - I that launch_vdt takes (inside ws;
+// null on the path without a workspace)
 size_t precompute_ws_bytes(int dtype, int d_out, int d, int k);
 int launch_precompute(int dtype, const void* W, const void* Vt, void* M, float* Dl, int d_out, int d, int k,
-                      void* ws, size_t ws_bytes, hipStream_t s);
-// VDt[k, d] = (V (V^T V - I))^T from Dl = V^T V - I and V (d x k), in the weight dtype; matrix
-// cores with a workspace of precompute_ws_bytes()
-int launch_vdt(int dtype, const float* Dl, const void* V, void* VDt, int d, int k, void* ws, size_t ws_bytes,
-               hipStream_t s);
+                      void* ws, size_t ws_bytes, const void** dd, hipStream_t s);
+// VDt[k, d] = (V (V^T V - I))^T from D = V^T V - I and V (d x k), in the weight dtype: one
+// matrix-core product from dd when given, else from Dl (float32) on the vector ALU
+int launch_vdt(int dtype, const float* Dl, const void* dd, const void* V, void* VDt, int d, int k, hipStream_t s);
 // dst[k, d] = transpose(src[d, k]); with `plan` (P <= 256 entries), also the decode plan rows of
 // the layer described by desc
 int launch_transpose(int dtype, const void* src, void* dst, int d, int k, const LayerDesc& desc, int P,

@@ -153,6 +153,19 @@ def test_precompute_tile_paths(g, dtype, shape, split):
     ref = orc.precompute_image(W, V)
     # one rounding to the 16-bit type on top of float32 accumulation
     assert rel_l2(M, ref) <= 4e-3, rel_l2(M, ref)
+    # (V (V^T V - I))^T, the batched path's second projection, from aux's documented layout
+    # against its definition on the stored V. V^T V - I is formed in float32, and its entries are
+    # small (~4e-4 for bf16-rounded bases, ~2e-5 for fp16 ones), so the float32 sum error of V^T V
+    # (~1e-7 sqrt(d)) weighs more for fp16: measured in a CPU emulation, 1.7e-3 - 3.3e-3 (bf16)
+    # and up to 6e-2 (fp16, d = 16384) relative; a wrong row, column or operand part is O(1).
+    es = 2
+    a256 = lambda n: (n + 255) // 256 * 256
+    off = a256(a256(k * d * es) + a256(k * k * 4) + 256 * 80)
+    aux = L._keep[2]
+    vdt = to_np(aux[off:off + k * d * es].view(dtype).view(k, d))
+    V_st = orc.as_f64(V)
+    ref_vdt = (V_st.T @ V_st - np.eye(k)) @ V_st.T
+    assert rel_l2(vdt, ref_vdt) <= (1e-2 if dtype == torch.bfloat16 else 0.15), rel_l2(vdt, ref_vdt)
     eps = 0.2
     X = torch.from_numpy(_planned_tokens(rng, V64, C64, eps, 3, 0.5)).to(dtype)
     x = X.cuda().contiguous()
