@@ -12,7 +12,10 @@ the decode kernel against the 8 TB/s HBM peak using the algorithmic bytes of the
 kernel's stream. The CPU baseline times the fp64 oracle on a bounded sample (see --cpu-seconds).
 The line also carries the create-time precompute (M = W V_k, V_k^T V_k - I and, for 16-bit layers,
 (V_k (V_k^T V_k - I))^T) at k = 256 and at k = 512 as matrix-core TFLOP/s, and the bandwidth of an
-in-repo streaming-read kernel.
+in-repo streaming-read kernel. Unless --no-extras is given, it also carries the same layers run
+in the other site modes (`site_modes`: every site a static projection, MLP-only gating, every
+site dense) and the extra workloads (`extra_workloads`: shared-input sites, T = 64 batched, the
+decode step).
 
 `--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
 batched path and prints its own line (tokens/s and algorithmic GB/s).
@@ -61,7 +64,8 @@ def parse():
                     help="batch-1 decode step of the GPT-J-shaped model: the GSI sites around an unchanged "
                          "plain attention, against the same step with every site dense (prints its own line)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="time only the headline workload (not the shared-input and T = 64 workloads)")
+                    help="time only the headline workload (not its site modes, nor the shared-input, T = 64 "
+                         "and decode-step workloads)")
     return ap.parse_args()
 
 
@@ -284,10 +288,78 @@ def batch1(args, cfg, g, torch, np, light: bool = False) -> dict:
                        "mfma_bf16_peak_tflops": BF16_MFMA_PEAK_TFLOPS},
         "precompute_k512": pre512,
     }
+    if cfg.cid == 3 and not light and not args.no_extras:
+        out["site_modes"] = site_modes(args, cfg, g, torch, np, layers, sites, X, n_tok, stream)
     # release the stack's device table while the runtime is up
     stack.destroy()
     torch.cuda.synchronize()
     return out
+
+
+def site_modes(args, cfg, g, torch, np, layers, sites, X, n_tok, stream) -> dict:
+    """The headline stack's layers run in the other site modes [GSI §2 intro, §2.2, §4]: every
+    site a static projection (y = M g, no residual norm, no gate), MLP-only gating (the attention
+    maps q/k/v and out dense, y = W x; the MLP maps gated) and every site dense (y = W x, the same
+    kernel). Each is timed like the headline (warm-up, then --steps tokens, HIP events on the
+    stream). Algorithmic bytes by mode per token and site: static V_k + M, dense W, gated V_k + M,
+    plus W when the token is slow."""
+    es = 2 if cfg.dtype != "f32" else 4
+    v_b = np.array([si.d * cfg.k * es for si in sites], dtype=np.float64)
+    m_b = np.array([si.d_out * cfg.k * es for si in sites], dtype=np.float64)
+    w_b = np.array([si.d_out * si.d * es for si in sites], dtype=np.float64)
+    attention = np.array([cfg.sites[si.site].name in ("qkv", "out") for si in sites])
+    plans = {
+        "static_projection": [g.GSI_SITE_STATIC] * len(layers),
+        "mlp_only_gating": [g.GSI_SITE_DENSE if a else g.GSI_SITE_GATED for a in attention],
+        "all_dense": [g.GSI_SITE_DENSE] * len(layers),
+    }
+    y_ld = sum(si.d_out for si in sites)
+    res = {}
+    for name, modes in plans.items():
+        st = g.gsi_stack_create_modes(layers, modes)
+        Y = torch.zeros((n_tok, y_ld), dtype=X.dtype, device="cuda")
+        gates = torch.zeros((n_tok, len(layers)), dtype=torch.uint8, device="cuda")
+        ws = g.new_workspace(g.gsi_stack_workspace_bytes(st, 1))
+
+        def run(tokens):
+            done = 0
+            while done < tokens:
+                n = min(n_tok, tokens - done)
+                g.gsi_stack_decode(st, X, n, 1, cfg.eps, Y, gates, None, ws, stream)
+                done += n
+
+        run(args.warmup)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(args.steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if g.gsi_workspace_status(ws) != 0:
+            raise SystemExit(f"decode kernel reported a wait timeout ({name})")
+        t = e0.elapsed_time(e1) / 1e3
+        mode = np.array(modes)
+        slow = gates.cpu().numpy()[np.arange(args.steps) % n_tok].astype(np.float64)
+        per_tok = np.where(mode == g.GSI_SITE_DENSE, w_b, v_b + m_b)
+        gated = mode == g.GSI_SITE_GATED
+        total = float(per_tok.sum() * args.steps + np.sum(slow[:, gated] * w_b[None, gated]))
+        achieved = total / t / 1e9
+        res[name] = {"value": round(args.steps / t, 2), "unit": "tokens/s",
+                     "ms_per_step": round(t * 1e3 / args.steps, 5),
+                     "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                                  "bytes_per_step": total / args.steps},
+                     "sites": {"gated": int(gated.sum()), "static": int((mode == g.GSI_SITE_STATIC).sum()),
+                               "dense": int((mode == g.GSI_SITE_DENSE).sum())}}
+        if gated.any():
+            res[name]["fast_fraction_gated_sites"] = round(1.0 - float(slow[:, gated].mean()), 5)
+        st.destroy()
+        del Y, gates, ws
+        torch.cuda.synchronize()
+    dense = res["all_dense"]["value"]
+    for name in ("static_projection", "mlp_only_gating"):
+        res[name]["speedup_vs_all_dense"] = round(res[name]["value"] / dense, 3)
+    return res
 
 
 def batched(args, cfg, g, torch, np):
