@@ -15,7 +15,7 @@ The line also carries the create-time precompute (M = W V_k, V_k^T V_k - I and, 
 in-repo streaming-read kernel. Unless --no-extras is given, it also carries the same layers run
 in the other site modes (`site_modes`: every site a static projection, MLP-only gating, every
 site dense) and the extra workloads (`extra_workloads`: shared-input sites, T = 64 batched, the
-decode step).
+decode step, the depth-cascade calibration).
 
 `--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
 batched path and prints its own line (tokens/s and algorithmic GB/s).
@@ -92,7 +92,7 @@ def main():
         sweep(args, g, torch, np)
         return
     if args.calibration:
-        calibration(args, g, torch, np)
+        print(json.dumps(calibration(args, g, torch, np)), flush=True)
         return
     if args.step:
         print(json.dumps(decode_step(args, g, torch, np)), flush=True)
@@ -108,11 +108,12 @@ def main():
 
 
 def extra_workloads(args, g, torch, np) -> dict:
-    """Three more workloads timed in the same run, each with its own bytes and roofline fraction:
-    the shared-input GPT-J-shaped stack (batch 1, q/k/v and fc_in as one site), the T = 64
-    batched workload (k = 512, ~20% slow tokens per step) and the decode step (the GSI sites of a
-    GPT-J-shaped model around an unchanged plain attention, against the same step with dense
-    sites)."""
+    """More workloads timed in the same run: the shared-input GPT-J-shaped stack (batch 1, q/k/v
+    and fc_in as one site), the T = 64 batched workload (k = 512, ~20% slow tokens per step) and
+    the decode step (the GSI sites of a GPT-J-shaped model around an unchanged plain attention,
+    against the same step with dense sites), each with its own bytes and roofline fraction; and
+    the depth-cascade calibration of the bases (GPU time against cold starts on the same kernels,
+    without its oracle leg)."""
     import argparse
     import gc
 
@@ -139,6 +140,16 @@ def extra_workloads(args, g, torch, np) -> dict:
     res["gptj_decode_step"] = {k: o7[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction",
                                                    "dense_step", "speedup_vs_dense")}
     res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
+    gc.collect()
+    torch.cuda.empty_cache()
+    a8 = argparse.Namespace(**vars(args))
+    a8.no_cpu_baseline = True
+    o8 = calibration(a8, g, torch, np)
+    res["gptj_calibration"] = {k: o8[k] for k in ("cascade_s", "cold_every_layer_s", "cascade_saving_vs_cold",
+                                                   "svd_every_layer_s", "time_ratio_cascade_to_svd", "step_ms",
+                                                   "max_sine_vs_planted")}
+    res["gptj_calibration"]["unit"] = "s"
+    res["gptj_calibration"]["workload"] = o8["config"]["workload"]
     gc.collect()
     torch.cuda.empty_cache()
     return res
@@ -688,7 +699,8 @@ def calibration(args, g, torch, np):
            "accuracy": acc,
            "max_sine_vs_planted": {"cascade": round(float(max(sines_casc)), 5), "cold": round(float(max(sines_cold)), 5)},
            "cpu_baseline": cpu}
-    print(json.dumps(out), flush=True)
+    del As, outs, ws
+    return out
 
 
 def decode_step(args, g, torch, np):
