@@ -15,7 +15,7 @@ The line also carries the create-time precompute (M = W V_k, V_k^T V_k - I and, 
 in-repo streaming-read kernel. Unless --no-extras is given, it also carries the same layers run
 in the other site modes (`site_modes`: every site a static projection, MLP-only gating, every
 site dense) and the extra workloads (`extra_workloads`: shared-input sites, T = 64 batched, the
-decode step, the depth-cascade calibration).
+decode step, the operating-point sweep at k = 256, the depth-cascade calibration).
 
 `--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
 batched path and prints its own line (tokens/s and algorithmic GB/s).
@@ -89,7 +89,7 @@ def main():
     if g.gsi_device_check() != 0:
         raise SystemExit("not a gfx950 device")
     if args.sweep:
-        sweep(args, g, torch, np)
+        print(json.dumps(sweep(args, g, torch, np)), flush=True)
         return
     if args.calibration:
         print(json.dumps(calibration(args, g, torch, np)), flush=True)
@@ -111,9 +111,10 @@ def extra_workloads(args, g, torch, np) -> dict:
     """More workloads timed in the same run: the shared-input GPT-J-shaped stack (batch 1, q/k/v
     and fc_in as one site), the T = 64 batched workload (k = 512, ~20% slow tokens per step) and
     the decode step (the GSI sites of a GPT-J-shaped model around an unchanged plain attention,
-    against the same step with dense sites), each with its own bytes and roofline fraction; and
-    the depth-cascade calibration of the bases (GPU time against cold starts on the same kernels,
-    without its oracle leg)."""
+    against the same step with dense sites), each with its own bytes and roofline fraction; the
+    operating-point sweep at k = 256 (tokens/s against the fast fraction, next to the vendor dense
+    chain); and the depth-cascade calibration of the bases (GPU time against cold starts on the
+    same kernels, without its oracle leg)."""
     import argparse
     import gc
 
@@ -140,6 +141,13 @@ def extra_workloads(args, g, torch, np) -> dict:
     res["gptj_decode_step"] = {k: o7[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction",
                                                    "dense_step", "speedup_vs_dense")}
     res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
+    gc.collect()
+    torch.cuda.empty_cache()
+    a9 = argparse.Namespace(**vars(args))
+    a9.sweep_ranks = "256"
+    o9 = sweep(a9, g, torch, np)
+    res["gptj_sweep_k256"] = {"unit": "tokens/s", "dense": o9["dense"], "rows": o9["rows"],
+                              "workload": o9["config"]["workload"] + ", k=256, planned slow counts per 512 tokens"}
     gc.collect()
     torch.cuda.empty_cache()
     a8 = argparse.Namespace(**vars(args))
@@ -588,7 +596,8 @@ def sweep(args, g, torch, np):
                      "gbps": round(float(w_bytes.sum()) / t_dense / 1e9, 1),
                      "what": "torch linear (vendor BLAS) y = W x, 112 sites in order, batch 1"},
            "rows": rows}
-    print(json.dumps(out), flush=True)
+    del Ws, xs
+    return out
 
 
 def calibration(args, g, torch, np):
