@@ -15,7 +15,8 @@ The line also carries the create-time precompute (M = W V_k, V_k^T V_k - I and, 
 in-repo streaming-read kernel. Unless --no-extras is given, it also carries the same layers run
 in the other site modes (`site_modes`: every site a static projection, MLP-only gating, every
 site dense) and the extra workloads (`extra_workloads`: shared-input sites, T = 64 batched, the
-decode step, the operating-point sweep at k = 256, the depth-cascade calibration).
+decode step, the GPT-2- and OPT-shaped stacks, the operating-point sweep at k = 256, the
+depth-cascade calibration).
 
 `--config 5` instead times the T = 64 workload (k = 512, ~20% slow tokens per step) through the
 batched path and prints its own line (tokens/s and algorithmic GB/s).
@@ -109,7 +110,8 @@ def main():
 
 def extra_workloads(args, g, torch, np) -> dict:
     """More workloads timed in the same run: the shared-input GPT-J-shaped stack (batch 1, q/k/v
-    and fc_in as one site), the T = 64 batched workload (k = 512, ~20% slow tokens per step) and
+    and fc_in as one site), the GPT-2-shaped (fp16) and OPT-shaped (bf16, ~14% slow tokens)
+    stacks at batch 1, the T = 64 batched workload (k = 512, ~20% slow tokens per step) and
     the decode step (the GSI sites of a GPT-J-shaped model around an unchanged plain attention,
     against the same step with dense sites), each with its own bytes and roofline fraction; the
     operating-point sweep at k = 256 (tokens/s against the fast fraction, next to the vendor dense
@@ -143,6 +145,14 @@ def extra_workloads(args, g, torch, np) -> dict:
     res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
     gc.collect()
     torch.cuda.empty_cache()
+    for cid, key in ((2, "gpt2_stack_fp16_batch1"), (4, "opt_stack_bf16_batch1")):
+        a2 = argparse.Namespace(**vars(args))
+        a2.steps, a2.warmup, a2.reps, a2.no_cpu_baseline = 512, 32, 1, True
+        o2 = batch1(a2, synth.get(cid), g, torch, np, light=True)
+        res[key] = {k: o2[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction")}
+        res[key]["workload"] = o2["config"]["workload"]
+        gc.collect()
+        torch.cuda.empty_cache()
     a9 = argparse.Namespace(**vars(args))
     a9.sweep_ranks = "256"
     o9 = sweep(a9, g, torch, np)
