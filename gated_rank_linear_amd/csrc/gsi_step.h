@@ -15,7 +15,8 @@ int attn_splits(int L, int n_heads);
 // arrival counter per head (zero before the first launch; each launch leaves them zero)
 size_t attn_ws_bytes(int d, int n_heads);
 
-// xa[0:d] = xa[d:2d] = LayerNorm(x) (unit row, float32 statistics, rounded to the dtype)
+// xa[0:d] = xa[d:2d] = LayerNorm(x) (unit row, float32 statistics, rounded to the dtype); d a
+// multiple of 4, at most 16384
 int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta, int d, void* xa, hipStream_t s);
 // attention of the query q = ya[0:d] over cache rows 0 .. pos - 1 and the new k, v = ya[d:2d],
 // ya[2d:3d] (row pos of the caches is written with them); o to xb[0:d]; u = gelu(ya[3d:3d+dff]) to

@@ -59,50 +59,73 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-constexpr int kLnPer = 16;  // row elements per thread of a 1024-thread LayerNorm block (d <= 16384)
-
-// LayerNorm of the row held in v (thread t has elements t + 1024 u), written twice to xa: the
-// stack's two sites read the same input
+// LayerNorm blocks: 1024 threads; thread t holds the groups of 4 consecutive row elements
+// 4096 c + 4 t .. + 3 (c < kLnChunks; d a multiple of 4, d <= 16384), read and written 8 bytes at
+// a time, with gamma and beta loaded together with the row
+constexpr int kLnChunks = 16384 / 4096;
 template <typename T>
-__device__ __forceinline__ void ln_dup_row(const float (&v)[kLnPer], const T* __restrict__ gamma,
-                                           const T* __restrict__ beta, int d, T* __restrict__ xa, float* red) {
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
+  const T a0 = from_f32<T>(v[0]), a1 = from_f32<T>(v[1]), a2 = from_f32<T>(v[2]), a3 = from_f32<T>(v[3]);
+  uint2 w;
+  w.x = (unsigned)a0.b | ((unsigned)a1.b << 16);
+  w.y = (unsigned)a2.b | ((unsigned)a3.b << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+// LayerNorm of the row held in v (groups as above, zero past d), written twice to xa: the stack's
+// two sites read the same input
+template <typename T>
+__device__ __forceinline__ void ln_dup_row(const float (&v)[kLnChunks][4], const float (&gm)[kLnChunks][4],
+                                           const float (&bt)[kLnChunks][4], int d, T* __restrict__ xa,
+                                           float* red) {
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < kLnPer; ++u) s += v[u];
+  for (int c = 0; c < kLnChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += v[c][e];
   const float mean = block_sum<16>(s, red) / (float)d;
   float q = 0.f;
 #pragma unroll
-  for (int u = 0; u < kLnPer; ++u) {
-    const int i = threadIdx.x + 1024 * u;
-    const float dv = i < d ? v[u] - mean : 0.f;
-    q = __builtin_fmaf(dv, dv, q);
+  for (int c = 0; c < kLnChunks; ++c) {
+    if (4096 * c + 4 * (int)threadIdx.x < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dv = v[c][e] - mean;
+        q = __builtin_fmaf(dv, dv, q);
+      }
+    }
   }
   const float var = block_sum<16>(q, red) / (float)d;
   const float rs = 1.0f / sqrtf(var + kLnEps);
 #pragma unroll
-  for (int u = 0; u < kLnPer; ++u) {
-    const int i = threadIdx.x + 1024 * u;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int i = 4096 * c + 4 * (int)threadIdx.x;
     if (i < d) {
-      const T a = from_f32<T>((v[u] - mean) * rs * to_f32(gamma[i]) + to_f32(beta[i]));
-      xa[i] = a;
-      xa[d + i] = a;
+      float a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = (v[c][e] - mean) * rs * gm[c][e] + bt[c][e];
+      store4<T>(xa + i, a);
+      store4<T>(xa + d + i, a);
     }
   }
 }
-
 template <typename T>
 __global__ __launch_bounds__(1024) void ln_dup_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                       const T* __restrict__ beta, int d, T* __restrict__ xa) {
   __shared__ float red[16];
-  float v[kLnPer];
+  float v[kLnChunks][4], gm[kLnChunks][4], bt[kLnChunks][4];
 #pragma unroll
-  for (int u = 0; u < kLnPer; ++u) {
-    const int i = threadIdx.x + 1024 * u;
-    v[u] = i < d ? to_f32(x[i]) : 0.f;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int i = 4096 * c + 4 * (int)threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[c][e] = gm[c][e] = bt[c][e] = 0.f;
+    if (i < d) {
+      load_row<T, 4>(x + i, v[c]);
+      load_row<T, 4>(gamma + i, gm[c]);
+      load_row<T, 4>(beta + i, bt[c]);
+    }
   }
-  ln_dup_row<T>(v, gamma, beta, d, xa, red);
+  ln_dup_row<T>(v, gm, bt, d, xa, red);
 }
-
 // x += yb[0:d] + yb[d:2d] (rounded and stored), then the next block's LayerNorm of the stored row
 // to xa: the same values as the residual kernel followed by ln_dup_kernel, in one launch
 template <typename T>
@@ -110,20 +133,30 @@ __global__ __launch_bounds__(1024) void residual_ln_kernel(T* __restrict__ x, co
                                                            const T* __restrict__ gamma, const T* __restrict__ beta,
                                                            int d, T* __restrict__ xa) {
   __shared__ float red[16];
-  float v[kLnPer];
+  float v[kLnChunks][4], gm[kLnChunks][4], bt[kLnChunks][4];
 #pragma unroll
-  for (int u = 0; u < kLnPer; ++u) {
-    const int i = threadIdx.x + 1024 * u;
-    v[u] = 0.f;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int i = 4096 * c + 4 * (int)threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[c][e] = gm[c][e] = bt[c][e] = 0.f;
     if (i < d) {
-      const T xn = from_f32<T>((to_f32(x[i]) + to_f32(yb[i])) + to_f32(yb[d + i]));
-      x[i] = xn;
-      v[u] = to_f32(xn);
+      float xv[4], y0[4], y1[4];
+      load_row<T, 4>(x + i, xv);
+      load_row<T, 4>(yb + i, y0);
+      load_row<T, 4>(yb + d + i, y1);
+      load_row<T, 4>(gamma + i, gm[c]);
+      load_row<T, 4>(beta + i, bt[c]);
+      float xn[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xn[e] = (xv[e] + y0[e]) + y1[e];
+        v[c][e] = to_f32(from_f32<T>(xn[e]));
+      }
+      store4<T>(x + i, xn);
     }
   }
-  ln_dup_row<T>(v, gamma, beta, d, xa, red);
+  ln_dup_row<T>(v, gm, bt, d, xa, red);
 }
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {  // this wave's vector memory operations, down to N
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
@@ -292,7 +325,7 @@ size_t attn_ws_bytes(int d, int n_heads) {
 }
 
 int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta, int d, void* xa, hipStream_t s) {
-  if (d < 1 || d > 16384) return GSI_ERR_SHAPE;
+  if (d < 4 || d > 16384 || d % 4 != 0) return GSI_ERR_SHAPE;
   if (dtype == GSI_BF16)
     ln_dup_kernel<bf16_t><<<1, 1024, 0, s>>>((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)beta, d,
                                              (bf16_t*)xa);
@@ -339,7 +372,7 @@ int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cach
 
 int launch_residual_ln(int dtype, void* x, const void* yb, const void* gamma, const void* beta, int d, void* xa,
                       hipStream_t s) {
-  if (d < 1 || d > 16384) return GSI_ERR_SHAPE;
+  if (d < 4 || d > 16384 || d % 4 != 0) return GSI_ERR_SHAPE;
   if (dtype == GSI_BF16)
     residual_ln_kernel<bf16_t><<<1, 1024, 0, s>>>((bf16_t*)x, (const bf16_t*)yb, (const bf16_t*)gamma,
                                                   (const bf16_t*)beta, d, (bf16_t*)xa);
