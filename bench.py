@@ -141,7 +141,7 @@ def extra_workloads(args, g, torch, np) -> dict:
     a7.steps, a7.warmup, a7.no_cpu_baseline = 48, 8, True
     o7 = decode_step(a7, g, torch, np)
     res["gptj_decode_step"] = {k: o7[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction",
-                                                   "dense_step", "speedup_vs_dense")}
+                                                   "dense_step", "speedup_vs_dense", "two_site_stack_a")}
     res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
     gc.collect()
     torch.cuda.empty_cache()
@@ -725,10 +725,12 @@ def calibration(args, g, torch, np):
 def decode_step(args, g, torch, np):
     """Batch-1 decode step of a GPT-J-shaped model (28 parallel blocks, d 4096, 16 heads of 256,
     d_ff 16384, k 256, eps 0.10, bf16) on the synthetic step model: per block gsi_block_step
-    (LayerNorm, the [QKV, fc_in] stack, plain attention over a key/value cache that starts with a
-    1024-position prefix, GELU, the [out, fc_out] stack, residual add), token after token, each
-    block's output feeding the next. The same step with both stacks in the dense site mode (y = W x
-    for every site, the same kernels otherwise) is the reference. Tokens/s over --steps tokens
+    (LayerNorm, stack A, plain attention over a key/value cache that starts with a 1024-position
+    prefix, GELU, the [out, fc_out] stack, residual add), token after token, each block's output
+    feeding the next. Stack A is one shared-input site: QKV and fc_in read the same LayerNorm
+    output, so their rows are stacked on one basis (one g, one gate for both). The same step with
+    the sites in the dense site mode (y = W x, the same kernels otherwise) is the reference. The
+    line also gives both for stack A as two sites [QKV, fc_in] ("two_site_stack_a"). Tokens/s over --steps tokens
     (default 48) after --warmup (default 8), one gsi_decode_step call per token followed by a
     synchronisation (decoding is autoregressive: a token's input exists only once the previous
     token is done), HIP events on the stream the library enqueues on; "queued" gives the rate with
@@ -752,11 +754,16 @@ def decode_step(args, g, torch, np):
     blocks = []
     for hb in model["blocks"]:
         layers = {n: g.create_layer(hb[n][0], hb[n][1]) for n in names_a + names_b}
-        blocks.append({"layers": layers, "hb": hb,
-                       "A": g.gsi_stack_create([layers[n] for n in names_a]),
+        # QKV and fc_in share the LayerNorm output's basis: one site with their rows stacked
+        wc = torch.cat([hb["qkv"][0], hb["fc_in"][0]], dim=0).contiguous()
+        layers["qkv_fc_in"] = g.create_layer(wc, hb["qkv"][1])
+        blocks.append({"layers": layers, "hb": hb, "wc": wc,
+                       "A": g.gsi_stack_create([layers["qkv_fc_in"]]),
                        "B": g.gsi_stack_create([layers[n] for n in names_b]),
-                       "Ad": g.gsi_stack_create_modes([layers[n] for n in names_a], [g.GSI_SITE_DENSE] * 2),
-                       "Bd": g.gsi_stack_create_modes([layers[n] for n in names_b], [g.GSI_SITE_DENSE] * 2)})
+                       "Ad": g.gsi_stack_create_modes([layers["qkv_fc_in"]], [g.GSI_SITE_DENSE]),
+                       "Bd": g.gsi_stack_create_modes([layers[n] for n in names_b], [g.GSI_SITE_DENSE] * 2),
+                       "A2": g.gsi_stack_create([layers[n] for n in names_a]),
+                       "A2d": g.gsi_stack_create_modes([layers[n] for n in names_a], [g.GSI_SITE_DENSE] * 2)})
     torch.cuda.synchronize()
     log(f"[step] layers and stacks in {time.time() - t0:.1f}s")
     d, dff, H = cfg.d, cfg.d_ff, cfg.n_heads
@@ -767,7 +774,7 @@ def decode_step(args, g, torch, np):
     yb = torch.zeros(2 * d, dtype=dt, device="cuda")
     n_tok = cfg.n_tokens
     gates = torch.zeros((n_tok, cfg.n_blocks, 4), dtype=torch.uint8, device="cuda")
-    ws = g.new_workspace(g.gsi_block_step_workspace_bytes(blocks[0]["A"], blocks[0]["B"], H))
+    ws = g.new_workspace(max(g.gsi_block_step_workspace_bytes(blocks[0][a], blocks[0]["B"], H) for a in ("A", "A2")))
     K0 = [hb["K"].clone() for hb in model["blocks"]]  # the prefix, restored before each pass
     V0 = [hb["V"].clone() for hb in model["blocks"]]
     stream = torch.cuda.current_stream()
@@ -778,12 +785,14 @@ def decode_step(args, g, torch, np):
     Vs = [hb["V"] for hb in model["blocks"]]
     gates = gates.view(n_tok, cfg.n_blocks * 4)
 
-    def run(dense, sync_each=True):
+    def run(dense, sync_each=True, two_site=False):
         for b, hb in enumerate(model["blocks"]):
             hb["K"].copy_(K0[b])
             hb["V"].copy_(V0[b])
         xs = model["x0"].clone()
         sa, sb = ("Ad", "Bd") if dense else ("A", "B")
+        if two_site:
+            sa = "A2d" if dense else "A2"
         A = [blk[sa] for blk in blocks]
         B = [blk[sb] for blk in blocks]
         h0 = 0.0
@@ -800,30 +809,36 @@ def decode_step(args, g, torch, np):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / 1e3 / n_time, xs, host
 
+    t2_gsi, _, _ = run(False, two_site=True)
+    gt2 = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)
+    t2_dense, _, _ = run(True, two_site=True)
     t_gsi, xs, host_gsi = run(False)
     t_gsi_q, _, _ = run(False, sync_each=False)
     gt = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)  # [QKV, fc_in, out, fc_out]
     t_dense, _, host_dense = run(True)
     t_dense_q, _, _ = run(True, sync_each=False)
     assert g.gsi_workspace_status(ws) == 0
-    # algorithmic bytes of the timed tokens
-    shapes = {"qkv": (3 * d, d), "fc_in": (dff, d), "out": (d, d), "fc_out": (d, dff)}
-    order = ("qkv", "fc_in", "out", "fc_out")
+    # algorithmic bytes of the timed tokens: per site V_k + M (+ W when slow), W for dense sites;
+    # the shared-input site reads V_k once for QKV and fc_in
     k = cfg.k
-    gsi_b, dense_b = 0.0, 0.0
-    for t in range(n_time):
-        pos = cfg.L0 + n_warm + t
-        att = 2.0 * (pos + 1) * d * 2 * cfg.n_blocks
-        for i, n in enumerate(order):
-            do, di = shapes[n]
-            slow = gt[t, :, i].sum()
-            gsi_b += cfg.n_blocks * (di * k + do * k) * 2.0 + slow * do * di * 2.0
-            dense_b += cfg.n_blocks * do * di * 2.0
-        gsi_b += att
-        dense_b += att
-    gsi_b /= n_time
-    dense_b /= n_time
-    fast = 1.0 - gt.mean()
+
+    def step_bytes(sites, gts):
+        gsi_b, dense_b = 0.0, 0.0
+        for t in range(n_time):
+            pos = cfg.L0 + n_warm + t
+            att = 2.0 * (pos + 1) * d * 2 * cfg.n_blocks
+            for col, (do, di) in sites:
+                slow = gts[t, :, col].sum()
+                gsi_b += cfg.n_blocks * (di * k + do * k) * 2.0 + slow * do * di * 2.0
+                dense_b += cfg.n_blocks * do * di * 2.0
+            gsi_b += att
+            dense_b += att
+        return gsi_b / n_time, dense_b / n_time
+
+    gsi_b, dense_b = step_bytes([(0, (3 * d + dff, d)), (2, (d, d)), (3, (d, dff))], gt)
+    gsi2_b, dense2_b = step_bytes([(0, (3 * d, d)), (1, (dff, d)), (2, (d, d)), (3, (d, dff))], gt2)
+    order = ("qkv", "fc_in", "out", "fc_out")
+    fast = 1.0 - gt[:, :, [0, 2, 3]].mean()
     # CPU baseline: the oracle's step on block 0 for as many tokens as about --cpu-seconds allow
     cpu = None
     if not args.no_cpu_baseline:
@@ -858,12 +873,16 @@ def decode_step(args, g, torch, np):
            "dense_step": {"value": round(1.0 / t_dense, 2), "ms_per_step": round(t_dense * 1e3, 4),
                           "achieved_gbps": round(dense_b / t_dense / 1e9, 1), "bytes_per_step": round(dense_b)},
            "speedup_vs_dense": round(t_dense / t_gsi, 3),
+           "two_site_stack_a": {"value": round(1.0 / t2_gsi, 2), "ms_per_step": round(t2_gsi * 1e3, 4),
+                                "achieved_gbps": round(gsi2_b / t2_gsi / 1e9, 1),
+                                "dense_value": round(1.0 / t2_dense, 2), "speedup_vs_dense": round(t2_dense / t2_gsi, 3),
+                                "fast_fraction": round(float(1.0 - gt2.mean()), 5)},
            # the given tokens enqueued without waiting between them (not autoregressive)
            "queued": {"value": round(1.0 / t_gsi_q, 2), "ms_per_step": round(t_gsi_q * 1e3, 4),
                       "dense_value": round(1.0 / t_dense_q, 2)},
            "cpu_baseline": cpu}
     for blk in blocks:
-        for key in ("A", "B", "Ad", "Bd"):
+        for key in ("A", "B", "Ad", "Bd", "A2", "A2d"):
             blk[key].destroy()
     torch.cuda.synchronize()
     return out

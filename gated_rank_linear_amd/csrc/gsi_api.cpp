@@ -532,14 +532,22 @@ int gsi_workspace_status(void* ws, size_t ws_nbytes, int* host_status, void* str
 
 // ---- one decode-step block: GSI sites around an unchanged plain attention ----
 
+// A: [QKV, fc_in] (d -> 3 d, d -> dff), or one shared-input site d -> 3 d + dff (QKV and fc_in
+// stacked: one basis, one g, one gate); B: [out, fc_out] (d -> d, dff -> d)
 static bool block_shapes(const gsi_stack* A, const gsi_stack* B, int n_heads, int* d_out, int* dff_out) {
-  if (A->n_sites != 2 || B->n_sites != 2) return false;
-  const LayerDesc &q = A->h_table[0], &f = A->h_table[1], &o = B->h_table[0], &m = B->h_table[1];
-  const int d = q.d, dff = f.d_out;
-  if (d < 64 || d > 16384 || n_heads < 1 || d % n_heads != 0) return false;
+  if ((A->n_sites != 1 && A->n_sites != 2) || B->n_sites != 2) return false;
+  const LayerDesc &q = A->h_table[0], &o = B->h_table[0], &m = B->h_table[1];
+  const int d = q.d, dff = m.d;
+  if (d < 64 || d > 16384 || n_heads < 1 || d % n_heads != 0 || dff < 1) return false;
   const int dh = d / n_heads;
   if (dh != 64 && dh != 128 && dh != 256) return false;
-  if (q.d_out != 3 * d || f.d != d || o.d != d || o.d_out != d || m.d != dff || m.d_out != d || dff < 1) return false;
+  if (A->n_sites == 2) {
+    const LayerDesc& f = A->h_table[1];
+    if (q.d_out != 3 * d || f.d != d || f.d_out != dff) return false;
+  } else if ((long long)q.d_out != 3LL * d + dff) {
+    return false;
+  }
+  if (o.d != d || o.d_out != d || m.d_out != d) return false;
   *d_out = d;
   *dff_out = dff;
   return true;
@@ -606,7 +614,10 @@ static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const vo
   if (rc != GSI_OK) return rc;
   rc = stack_one_token(A, xa, eps, ya, gates, rho, ws, s);
   if (rc != GSI_OK) return rc;
-  rc = launch_attention_gelu(A->dtype, ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+  // a shared-input stack A decides one gate for QKV and fc_in: the attention launch repeats it
+  const bool shared = A->n_sites == 1;
+  rc = launch_attention_gelu(A->dtype, ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part,
+                             shared ? gates : nullptr, shared ? rho : nullptr, s);
   if (rc != GSI_OK) return rc;
   rc = stack_one_token(B, xb, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, s);
   if (rc != GSI_OK) return rc;

@@ -178,8 +178,15 @@ template <typename T, int EPL>
 __global__ __launch_bounds__(256) void attn_gelu_kernel(const T* __restrict__ ya, T* __restrict__ kc,
                                                         T* __restrict__ vc, int pos, int d, int n_heads, int lc,
                                                         int nsplit, float* __restrict__ part, int* __restrict__ cnt,
-                                                        int dff, T* __restrict__ xb) {
+                                                        int dff, T* __restrict__ xb, uint8_t* __restrict__ gate_dup,
+                                                        float* __restrict__ rho_dup) {
   constexpr int dh = 64 * EPL;
+  // a shared-input site's gate (and ratio), decided by the stack launch before this one, is
+  // reported for both of its maps
+  if (gate_dup && blockIdx.x == 0 && threadIdx.x == 0) {
+    gate_dup[1] = gate_dup[0];
+    if (rho_dup) rho_dup[1] = rho_dup[0];
+  }
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_acc[4][dh];
   __shared__ int s_last;
@@ -339,31 +346,31 @@ int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta,
 
 template <typename T, int EPL>
 static void attention_launch(const void* ya, void* kc, void* vc, int pos, int d, int n_heads, int dff, void* xb,
-                             float* part, hipStream_t s) {
+                             float* part, uint8_t* gate_dup, float* rho_dup, hipStream_t s) {
   const int L = pos + 1;
   const int nsplit = attn_splits(L, n_heads);
   const int lc = (L + nsplit - 1) / nsplit;
   int* cnt = (int*)((char*)part + align256((size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4));
   const unsigned nb = (unsigned)(n_heads * nsplit + (dff + 255) / 256);
   attn_gelu_kernel<T, EPL><<<nb, 256, 0, s>>>((const T*)ya, (T*)kc, (T*)vc, pos, d, n_heads, lc, nsplit, part, cnt,
-                                               dff, (T*)xb);
+                                               dff, (T*)xb, gate_dup, rho_dup);
 }
 
 int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cache, int pos, int d, int n_heads,
-                          int dff, void* xb, float* part, hipStream_t s) {
+                          int dff, void* xb, float* part, uint8_t* gate_dup, float* rho_dup, hipStream_t s) {
   if (n_heads < 1 || d % n_heads != 0 || pos < 0) return GSI_ERR_SHAPE;
   const int dh = d / n_heads;
   const bool bf = dtype == GSI_BF16;
   if (dtype != GSI_BF16 && dtype != GSI_F16) return GSI_ERR_DTYPE;
   if (dh == 64) {
-    if (bf) attention_launch<bf16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
-    else attention_launch<f16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    if (bf) attention_launch<bf16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    else attention_launch<f16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
   } else if (dh == 128) {
-    if (bf) attention_launch<bf16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
-    else attention_launch<f16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    if (bf) attention_launch<bf16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    else attention_launch<f16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
   } else if (dh == 256) {
-    if (bf) attention_launch<bf16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
-    else attention_launch<f16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, s);
+    if (bf) attention_launch<bf16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    else attention_launch<f16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
   } else {
     return GSI_ERR_SHAPE;
   }

@@ -244,9 +244,12 @@ int gsi_calibrate(int n, int d, int k, const float* A, const float* Q0t, int n_i
  *   u = gelu(f), tanh form
  *   y_out = site out(o), y_mlp = site fc_out(u)                stack B: [out, fc_out], input [o | u]
  *   x += y_out + y_mlp
- * A and B are stacks of exactly two sites of one 16-bit dtype with those shapes (A: d -> 3 d and
- * d -> dff; B: d -> d and dff -> d; any site mode), n_heads divides d with d / n_heads in
- * {64, 128, 256}, d <= 16384; otherwise GSI_ERR_SHAPE / GSI_ERR_DTYPE. Each stack runs with gate
+ * A and B are stacks of one 16-bit dtype with those shapes (A: d -> 3 d and d -> dff; B: d -> d
+ * and dff -> d; any site mode), n_heads divides d with d / n_heads in {64, 128, 256},
+ * d <= 16384; otherwise GSI_ERR_SHAPE / GSI_ERR_DTYPE. A may instead be one shared-input site
+ * d -> 3 d + dff: QKV and fc_in read the same a, so one basis serves both and the site forms one
+ * g and decides one gate for both (W rows [q | k | v | f], written to ya as they are); its gate
+ * and ratio are then reported in entries 0 and 1 alike. Each stack runs with gate
  * threshold eps through the batch-1 kernel for one token, as an ordinary launch of its co-resident
  * grid (a cooperative launch would add a queue switch before and after each of the two).
  * Buffers (device, 16-byte aligned, the caller's): gamma, beta [d]; x [d]; k_cache, v_cache

@@ -99,7 +99,9 @@ def _extend(lead: torch.Tensor, n: int, gen) -> torch.Tensor:
 def step_model(cfg: StepConfig, device="cpu") -> dict:
     """The model's weights, bases, LayerNorm parameters, prefilled caches and token embeddings, in
     the storage dtype on `device`. blocks[b] holds "gamma", "beta", "qkv" / "out" / "fc_in" /
-    "fc_out" as (W, V) pairs, and "K" / "V" caches of L0 + n_tokens rows (the first L0 filled)."""
+    "fc_out" as (W, V) pairs, and "K" / "V" caches of L0 + n_tokens rows (the first L0 filled).
+    QKV and fc_in read the same input (the block's LayerNorm output), so they share one basis
+    tensor: the two sites can run as one shared-input site (W stacked, one g, one gate)."""
     dev = torch.device(device)
     ft = torch.float64 if dev.type == "cpu" else torch.float32
     st = TORCH_DTYPE[cfg.dtype]
@@ -138,11 +140,12 @@ def step_model(cfg: StepConfig, device="cpu") -> dict:
         Wo = S @ rn(r, d, scale=0.3 / math.sqrt(d))
         Wm = S @ rn(r, dff, scale=1.0 / math.sqrt(dff))
         rs = lambda a: a.to(st).contiguous()  # row-major, in the storage dtype
+        Va = rs(_extend(B, k, gb))  # the basis of the block's LayerNorm output, read by QKV and fc_in
         blk = {
             "gamma": torch.ones(d, device=dev, dtype=st), "beta": torch.zeros(d, device=dev, dtype=st),
-            "qkv": (rs(torch.cat([Wq, Wk, Wv], dim=0)), rs(_extend(B, k, gb))),
+            "qkv": (rs(torch.cat([Wq, Wk, Wv], dim=0)), Va),
             "out": (rs(Wo), rs(_extend(Tv, k, gb))),
-            "fc_in": (rs(Wf), rs(_extend(B, k, gb))),
+            "fc_in": (rs(Wf), Va),
             "fc_out": (rs(Wm), rs(_extend(Tf, k, gb))),
         }
         K = torch.zeros((cfg.L0 + n, d), device=dev, dtype=st)

@@ -32,17 +32,25 @@ def g():
 
 
 class Model:
-    """The synthetic step model on the GPU: per block two stacks, LayerNorm parameters, caches."""
+    """The synthetic step model on the GPU: per block two stacks, LayerNorm parameters, caches.
+    shared: stack A is one shared-input site (QKV and fc_in rows stacked on their common basis)."""
 
-    def __init__(self, g, cfg):
+    def __init__(self, g, cfg, shared=False):
         self.cfg = cfg
+        self.shared = shared
         self.host = step_model(cfg)
         self.blocks = []
         self.keep = []
         for hb in self.host["blocks"]:
             dev = {n: (hb[n][0].cuda(), hb[n][1].cuda()) for n in SITES_A + SITES_B}
             layers = {n: g.create_layer(*dev[n]) for n in dev}
-            A = g.gsi_stack_create([layers[n] for n in SITES_A])
+            if shared:
+                assert hb["qkv"][1] is hb["fc_in"][1]  # one basis for the block's LayerNorm output
+                Wc = torch.cat([dev["qkv"][0], dev["fc_in"][0]], dim=0).contiguous()
+                layers["qkv_fc_in"] = g.create_layer(Wc, dev["qkv"][1])
+                A = g.gsi_stack_create([layers["qkv_fc_in"]])
+            else:
+                A = g.gsi_stack_create([layers[n] for n in SITES_A])
             B = g.gsi_stack_create([layers[n] for n in SITES_B])
             blk = {"A": A, "B": B, "gamma": hb["gamma"].cuda(), "beta": hb["beta"].cuda(),
                    "K": hb["K"].cuda(), "V": hb["V"].cuda(), "layers": layers, "dev": dev}
@@ -100,6 +108,9 @@ def _teacher_forced(g, model, n_tokens):
             xa, ya, xb, yb = (to_np(v) for v in (model.xa, model.ya, model.xb, model.yb))
             gates = model.gates.cpu().numpy()
             where = f"token {t} block {b}"
+            if model.shared:  # one gate and one ratio, reported for QKV and fc_in alike
+                rho = model.rho.cpu().numpy()
+                assert gates[0] == gates[1] and rho[0] == rho[1], f"{where}: {gates} {rho}"
             # LayerNorm of the stored x, written twice
             assert np.array_equal(xa[:d], xa[d:]), where
             e = rel_l2(xa[:d], ostep.layer_norm(x_before, hb["gamma"], hb["beta"]))
@@ -145,6 +156,57 @@ def test_step_full_width_teacher_forced(g):
     say(f"  {n} site calls, {n_slow} slow")
     assert 0 < n_slow < n
     model.destroy()
+
+
+def test_step_shared_input_teacher_forced(g):
+    """Stack A as one shared-input site (QKV and fc_in stacked, d 4096 -> 28672, one basis, one g,
+    one gate) at GPT-J-shaped widths: the same per-op checks, each map against its own site in the
+    oracle (the same basis and input give the same ratio), and one gate reported for both maps."""
+    cfg = step_config(73)
+    say(f"case: {cfg.name}, stack A as one shared-input site, teacher-forced per op")
+    model = Model(g, cfg, shared=True)
+    n, n_slow = _teacher_forced(g, model, cfg.n_tokens)
+    say(f"  {n} site calls, {n_slow} slow")
+    assert 0 < n_slow < n
+    model.destroy()
+
+
+def test_step_shared_input_chain(g):
+    """Two GPT-2-shaped blocks with a shared-input stack A, six tokens chained through
+    gsi_decode_step: the final rows against the oracle's float64 chain (within 3e-2) and against the
+    two-site stack A's rows (within 3e-2: the same maps, different work splits)."""
+    cfg = step_config(71)
+    say(f"case: {cfg.name}, shared-input stack A, chained")
+    ms, mt = Model(g, cfg, shared=True), Model(g, cfg)
+    nb = cfg.n_blocks
+    Kh = [orc.as_f64(hb["K"]) for hb in ms.host["blocks"]]
+    Vh = [orc.as_f64(hb["V"]) for hb in ms.host["blocks"]]
+    gates_all = torch.zeros((cfg.n_tokens, nb * 4), dtype=torch.uint8, device="cuda")
+    for t in range(cfg.n_tokens):
+        pos = cfg.L0 + t
+        xs = ms.host["x0"][t].cuda().clone()
+        xt = xs.clone()
+        xo = orc.as_f64(ms.host["x0"][t])
+        for m, x, gv in ((ms, xs, gates_all[t]), (mt, xt, None)):
+            bl = m.blocks
+            g.gsi_decode_step([k["A"] for k in bl], [k["B"] for k in bl], [k["gamma"] for k in bl],
+                              [k["beta"] for k in bl], [k["K"] for k in bl], [k["V"] for k in bl], pos,
+                              cfg.n_heads, cfg.eps, x, m.xa, m.ya, m.xb, m.yb,
+                              gv if gv is not None else torch.zeros(nb * 4, dtype=torch.uint8, device="cuda"),
+                              None, m.ws)
+        torch.cuda.synchronize()
+        for b in range(nb):
+            r = ostep.decode_block(xo, ms.host["blocks"][b], Kh[b], Vh[b], pos, cfg.eps, cfg.n_heads)
+            xo = r["x_next"]
+        gv = gates_all[t].cpu().numpy().reshape(nb, 4)
+        assert np.array_equal(gv[:, 0], gv[:, 1]), f"token {t}: {gv}"
+        e = rel_l2(to_np(xs), xo)
+        assert e <= 3e-2, f"token {t}: final row rel L2 {e:.2e} against the oracle"
+        e = rel_l2(to_np(xs), to_np(xt))
+        assert e <= 3e-2, f"token {t}: final row rel L2 {e:.2e} against the two-site stack A"
+    assert g.gsi_workspace_status(ms.ws) == 0
+    ms.destroy()
+    mt.destroy()
 
 
 def test_step_long_cache(g):
