@@ -89,3 +89,30 @@ def test_mutant_rejected(monkeypatch, name, mutant):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin rejects {mutant.__name__}"
+
+
+@pytest.mark.parametrize("eps", [0.05, 0.2, 1.5])
+def test_shared_input_site_equals_its_two_sites(eps):
+    """Two maps of one input on one basis (QKV and fc_in of a parallel block) run as one site with
+    their rows stacked give, in the oracle, the two sites' outputs side by side and the same gate
+    and ratio: the residual norm and the gate depend on the input and the basis only. At eps 1.5
+    every token is fast, at 0.05 most are slow, at 0.2 both occur."""
+    from oracle import gsi_oracle as orc
+    rng = np.random.default_rng(30)
+    d, k, n = 64, 8, 40
+    Q, R = np.linalg.qr(rng.standard_normal((d, k + 24)))
+    V, C = Q[:, :k], Q[:, k:]
+    W1 = rng.standard_normal((3 * 16, d))
+    W2 = rng.standard_normal((24, d))
+    rho = rng.uniform(0.02, 0.4, n)
+    z = rng.standard_normal((n, k))
+    w = rng.standard_normal((n, C.shape[1]))
+    s = rho * np.linalg.norm(z, axis=1) / (np.linalg.norm(w, axis=1) * np.sqrt(1 - rho ** 2))
+    X = z @ V.T + (s[:, None] * w) @ C.T
+    both = orc.forward(np.vstack([W1, W2]), V, X, eps)
+    r1, r2 = orc.forward(W1, V, X, eps), orc.forward(W2, V, X, eps)
+    assert np.array_equal(both["gate"], r1["gate"]) and np.array_equal(both["gate"], r2["gate"])
+    np.testing.assert_allclose(both["rho"], r1["rho"], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(both["y"], np.hstack([r1["y"], r2["y"]]), rtol=1e-12, atol=1e-12)
+    if eps == 0.2:
+        assert 0 < both["gate"].sum() < n
