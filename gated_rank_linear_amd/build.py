@@ -68,5 +68,34 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PHASE_LIB = os.path.join(OUT_DIR, "libgsi_phases.so")
+
+
+def build_phase_timeline() -> str:
+    """A profiling variant of libgsi (_lib/libgsi_phases.so): the same sources with the batch-1
+    kernel's phase stamps compiled in (GSI_PHASE_STAMPS) and gsi_phase_stamps exported. Used by
+    gated_rank_linear_amd.phase_timeline only; libgsi itself never carries the stamps."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(OUT_DIR, "phases_" + os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *HIP_FLAGS, "-DGSI_PHASE_STAMPS", "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,--no-undefined", *objs, "-o", PHASE_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    for o in objs:
+        os.remove(o)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the phase-stamp library failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return PHASE_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--phase-stamps" in sys.argv[1:]:
+        print(build_phase_timeline())
+    else:
+        print(build(verbose=True))

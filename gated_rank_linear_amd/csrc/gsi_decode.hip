@@ -44,6 +44,27 @@
 
 namespace gsi {
 
+// Phase timeline (a build option for profiling; compiled out of libgsi): with GSI_PHASE_STAMPS,
+// the sync wave of blocks 0, 100 and 200 stores a wall-clock stamp at each phase boundary of the
+// 16 site steps q = GSI_PHASE_Q0 .. + 15 of a launch; gsi_phase_stamps copies them out.
+#ifdef GSI_PHASE_STAMPS
+#ifndef GSI_PHASE_Q0
+#define GSI_PHASE_Q0 512
+#endif
+__device__ unsigned long long g_phase_stamps[3][16][11];
+#define GSI_PHASE(i)                                                                                   \
+  do {                                                                                                 \
+    if (c.tid == kDataThreads && c.q >= GSI_PHASE_Q0 && c.q < GSI_PHASE_Q0 + 16) {                     \
+      const int bi_ = c.b == 0 ? 0 : (c.b == 100 ? 1 : (c.b == 200 ? 2 : -1));                          \
+      if (bi_ >= 0) g_phase_stamps[bi_][c.q - GSI_PHASE_Q0][i] = wall_clock64();                       \
+    }                                                                                                  \
+  } while (0)
+#else
+#define GSI_PHASE(i) \
+  do {               \
+  } while (0)
+#endif
+
 constexpr int kSlowBatch = 8;  // W / x chunk pairs per lane in flight on the W x rows
 constexpr unsigned long long kWaitTicks = 200000000ull;  // 2 s at the 100 MHz wall clock
 
@@ -401,6 +422,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   // what the step still needs after g and gn are replaced by the next step's rows
   const int mode = g.mode, nrows = g.nrows, cprd = g.cprd;
   const unsigned long long w_rows = g.w;
+  GSI_PHASE(10);  // step entry
   Cursor cn = cq;
   cn.advance(p.n_sites, p.t_step);
   Cursor c2 = cn;
@@ -444,6 +466,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   }
 
   // ---------------- phase A (data waves): g_j for owned columns and |x|^2 ----------------
+  GSI_PHASE(0);
   if (!is_sync) {
     float acc[kMaxJ];
 #pragma unroll
@@ -501,6 +524,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   }
   lds_barrier();
   // ---------------- E1: post this block's g_j, then all-gather g ----------------
+  GSI_PHASE(1);
   float gj_own[kMaxJ];
   if (is_sync) {
 #pragma unroll
@@ -513,11 +537,13 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     if (lane == 0) *sh.s_nx2 = ((sh.red[0][kMaxJ] + sh.red[1][kMaxJ]) + sh.red[2][kMaxJ]) + sh.red[3][kMaxJ];
   }
   lds_barrier();  // the g words are issued ahead of the copy below
+  GSI_PHASE(2);
   if (!is_sync) {
     if (has_next) fill_region(gn, P, wave, lane, nxt, c.dummy);
   } else {
     float gv[kMaxK / 64];
     const bool ok = gather(p, c.base, p.box_g + (long long)c.rep * kMaxK, g.k, tag_g, lane, gv);
+    GSI_PHASE(3);
     if (!ok && lane == 0) *sh.s_abort = 1;
     float gg = 0.f;
 #pragma unroll
@@ -530,6 +556,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     if (lane == 63) *sh.s_gg = gg;
   }
   lds_barrier();
+  GSI_PHASE(4);
   if (*sh.s_abort) return false;
 
   // ------- phase B (data waves): this block's rows of y = M g; (sync wave) the gate piece -------
@@ -555,11 +582,13 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
   }
   lds_barrier();
   // ---- the sync wave stores this block's rows of y, then posts its E2 word (site done) ----
+  GSI_PHASE(5);
   if (is_sync) {
     for (int r = lane; r < nrows; r += 64) yrow[r] = from_f32<T>(sh.ypart[r]);
     if (lane < kReplicas) st_dev(p.box_p + (long long)lane * kMaxBlocks + b, pack(tag_p, pb));
   }
   lds_barrier();  // the y rows and the E2 word are issued ahead of the loads below
+  GSI_PHASE(6);
   if (!is_sync) {
     // the next input row streams in while E2 resolves
     if (has_next) load_x<XR>(reinterpret_cast<const T*>(p.X) + cn.token(p.t_step) * p.x_ld + gn.x_off, gn.cprd, tid, xw);
@@ -571,6 +600,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     // ---------------- E2: all-gather the pieces, resolve the gate ----------------
     float pv[kMaxBlocks / 64];
     const bool ok = gather(p, c.base, p.box_p + (long long)c.rep * kMaxBlocks, P, tag_p, lane, pv);
+    GSI_PHASE(7);
     if (!ok && lane == 0) *sh.s_abort = 1;
     float ps = 0.f;
 #pragma unroll
@@ -596,6 +626,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     }
   }
   lds_barrier();
+  GSI_PHASE(8);
   if (*sh.s_abort) return false;
 
   // ---------------- slow path: y = W x for the owned rows, then E3 ----------------
@@ -617,6 +648,7 @@ __device__ __forceinline__ bool site_step(const DecodeParams& p, const StepCtx& 
     __syncthreads();
     if (*sh.s_abort) return false;
   }
+  GSI_PHASE(9);
   return true;
 }
 
@@ -782,3 +814,10 @@ int launch_decode_resident(int dtype, const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace gsi
+
+#ifdef GSI_PHASE_STAMPS
+// the phase stamps of the last launch: 3 blocks x 16 site steps x 11 stamps, wall-clock ticks
+extern "C" int gsi_phase_stamps(unsigned long long* out) {
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(gsi::g_phase_stamps), sizeof(gsi::g_phase_stamps)) == hipSuccess ? 0 : -1;
+}
+#endif
