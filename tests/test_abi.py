@@ -28,6 +28,14 @@ def test_every_declared_symbol_is_exported_and_bound():
         assert n in bound, f"{n} has no binding"
 
 
+
+def test_library_carries_no_phase_stamps():
+    # the wall-clock stamps of the batch-1 kernel exist only in the separate stamp build
+    if os.path.basename(g.LIB_PATH) != "libgsi.so":
+        pytest.skip("a non-default library is loaded")
+    with pytest.raises(AttributeError):
+        lib.gsi_phase_stamps
+
 def test_status_strings():
     for code in range(0, -10, -1):
         s = lib.gsi_status_string(code)
