@@ -734,7 +734,8 @@ def decode_step(args, g, torch, np):
     (default 48) after --warmup (default 8), one gsi_decode_step call per token followed by a
     synchronisation (decoding is autoregressive: a token's input exists only once the previous
     token is done), HIP events on the stream the library enqueues on; "queued" gives the rate with
-    the synthetic tokens enqueued back to back.
+    the synthetic tokens enqueued back to back, "graph" the rate of one captured step
+    (gsi_decode_step_devpos) replayed per token.
     Algorithmic bytes per token: per site V_k + M (+ W when slow), W for the dense step, plus the
     attention's key and value rows (2 (pos + 1) d 2 bytes per block)."""
     import dataclasses
@@ -809,6 +810,39 @@ def decode_step(args, g, torch, np):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / 1e3 / n_time, xs, host
 
+    def run_graph(dense):
+        # one step captured in a HIP graph with the position in device memory, replayed per token
+        # (each replay followed by a synchronisation, as in run); token 0 runs the call eagerly
+        for b, hb in enumerate(model["blocks"]):
+            hb["K"].copy_(K0[b])
+            hb["V"].copy_(V0[b])
+        xs = model["x0"].clone()
+        A = [blk["Ad" if dense else "A"] for blk in blocks]
+        B = [blk["Bd" if dense else "B"] for blk in blocks]
+        pos_dev = torch.tensor([cfg.L0], dtype=torch.int32, device="cuda")
+        xg = torch.empty_like(xs[0])
+        gg = torch.zeros(cfg.n_blocks * 4, dtype=torch.uint8, device="cuda")
+        call = lambda: g.gsi_decode_step_devpos(A, B, gam, bet, Ks, Vs, pos_dev, H, cfg.eps, xg, xa, ya, xb, yb, gg,
+                                                None, ws)
+        xg.copy_(xs[0])
+        call()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        w = max(n_warm, 1)
+        for t in range(1, n_tok):
+            if t == w:
+                ev0.record(stream)
+            xg.copy_(xs[t])
+            graph.replay()
+            torch.cuda.synchronize()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        assert int(pos_dev.item()) == cfg.L0 + n_tok
+        del graph
+        return ev0.elapsed_time(ev1) / 1e3 / (n_tok - w)
+
     t2_gsi, _, _ = run(False, two_site=True)
     gt2 = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)
     t2_dense, _, _ = run(True, two_site=True)
@@ -817,6 +851,8 @@ def decode_step(args, g, torch, np):
     gt = gates[n_warm:].view(n_time, cfg.n_blocks, 4).cpu().numpy().astype(np.int64)  # [QKV, fc_in, out, fc_out]
     t_dense, _, host_dense = run(True)
     t_dense_q, _, _ = run(True, sync_each=False)
+    t_gsi_g = run_graph(False)
+    t_dense_g = run_graph(True)
     assert g.gsi_workspace_status(ws) == 0
     # algorithmic bytes of the timed tokens: per site V_k + M (+ W when slow), W for dense sites;
     # the shared-input site reads V_k once for QKV and fc_in
@@ -873,6 +909,10 @@ def decode_step(args, g, torch, np):
            "dense_step": {"value": round(1.0 / t_dense, 2), "ms_per_step": round(t_dense * 1e3, 4),
                           "achieved_gbps": round(dense_b / t_dense / 1e9, 1), "bytes_per_step": round(dense_b)},
            "speedup_vs_dense": round(t_dense / t_gsi, 3),
+           # the same step from a captured graph (gsi_decode_step_devpos), one replay per token
+           "graph": {"value": round(1.0 / t_gsi_g, 2), "ms_per_step": round(t_gsi_g * 1e3, 4),
+                     "achieved_gbps": round(gsi_b / t_gsi_g / 1e9, 1), "dense_value": round(1.0 / t_dense_g, 2),
+                     "speedup_vs_dense": round(t_dense_g / t_gsi_g, 3)},
            "two_site_stack_a": {"value": round(1.0 / t2_gsi, 2), "ms_per_step": round(t2_gsi * 1e3, 4),
                                 "achieved_gbps": round(gsi2_b / t2_gsi / 1e9, 1),
                                 "dense_value": round(1.0 / t2_dense, 2), "speedup_vs_dense": round(t2_dense / t2_gsi, 3),

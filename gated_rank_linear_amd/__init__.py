@@ -5,7 +5,8 @@ package only marshals arguments to it. Importing it without the built library ra
 """
 from ._binding import (GSI_BF16, GSI_F16, GSI_F32, GSI_OK, GSI_SITE_DENSE, GSI_SITE_GATED,  # noqa: F401
                        GSI_SITE_STATIC, LIB_PATH, SIGNATURES, STATUS_NAMES, GsiError, Layer, Stack, create_dense_layer,
-                       create_layer, dtype_code, gsi_block_step, gsi_block_step_workspace_bytes, gsi_calibrate, gsi_decode_step, gsi_calibrate_workspace_bytes,
+                       create_layer, dtype_code, gsi_block_step, gsi_block_step_workspace_bytes, gsi_calibrate, gsi_decode_step, gsi_decode_step_devpos,
+                       gsi_calibrate_workspace_bytes,
                        gsi_device_check,
                        gsi_forward, gsi_layer_aux_bytes, gsi_layer_create, gsi_layer_create_dense,
                        gsi_layer_create_workspace_bytes, gsi_stack_create,

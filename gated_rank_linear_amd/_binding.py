@@ -54,6 +54,9 @@ SIGNATURES = [
     ("gsi_decode_step", _int, [_int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _int, _int, _float, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    ("gsi_decode_step_devpos", _int, [_int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _int, _int,
+                                      _float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 ]
 
 
@@ -275,6 +278,27 @@ def gsi_decode_step(A: list, B: list, gamma: list, beta: list, k_cache: list, v_
                              _ptr(ya), _ptr(xb), _ptr(yb), _ptr(gates), _ptr(rho), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "gsi_decode_step")
+
+
+def gsi_decode_step_devpos(A: list, B: list, gamma: list, beta: list, k_cache: list, v_cache: list,
+                           pos: torch.Tensor, n_heads: int, eps: float, x: torch.Tensor, xa: torch.Tensor,
+                           ya: torch.Tensor, xb: torch.Tensor, yb: torch.Tensor, gates: torch.Tensor,
+                           rho: torch.Tensor | None, ws: torch.Tensor, stream=None) -> None:
+    """gsi_decode_step at the position held by the device int32 tensor `pos` (advanced by one by the
+    step itself), so that a captured graph of one call replays token after token."""
+    n = len(A)
+    if not (len(B) == len(gamma) == len(beta) == len(k_cache) == len(v_cache) == n):
+        raise ValueError("per-block lists differ in length")
+    if pos.dtype != torch.int32 or pos.numel() != 1:
+        raise ValueError("pos must be one int32 element")
+    arr = lambda vals: (_vp * n)(*vals)
+    rc = lib.gsi_decode_step_devpos(n, arr([s.handle for s in A]), arr([s.handle for s in B]),
+                                    arr([_ptr(t) for t in gamma]), arr([_ptr(t) for t in beta]),
+                                    arr([_ptr(t) for t in k_cache]), arr([_ptr(t) for t in v_cache]), _ptr(pos),
+                                    int(k_cache[0].shape[0]), int(n_heads), float(eps), _ptr(x), _ptr(xa), _ptr(ya),
+                                    _ptr(xb), _ptr(yb), _ptr(gates), _ptr(rho), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "gsi_decode_step_devpos")
 
 
 # ------------------------------------------------------------------------------------------------

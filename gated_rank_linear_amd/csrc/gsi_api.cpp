@@ -607,7 +607,8 @@ static int block_check(gsi_stack* A, gsi_stack* B, const void* gamma, const void
 static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const void* beta, void* x, void* k_cache,
                          void* v_cache, int pos, int n_heads, float eps, void* xa, void* ya, void* xb, void* yb,
                          uint8_t* gates, float* rho, void* ws, int d, int dff, hipStream_t s, bool ln_done = false,
-                         const void* next_gamma = nullptr, const void* next_beta = nullptr) {
+                         const void* next_gamma = nullptr, const void* next_beta = nullptr,
+                         const int* pos_dev = nullptr, int cap = 0) {
   const size_t st = align256(std::max(ws_bytes_for(A->k_max, A->d_out_max, 1), ws_bytes_for(B->k_max, B->d_out_max, 1)));
   float* part = (float*)((char*)ws + st);
   int rc = ln_done ? GSI_OK : launch_ln_dup(A->dtype, x, gamma, beta, d, xa, s);
@@ -617,7 +618,7 @@ static int block_enqueue(gsi_stack* A, gsi_stack* B, const void* gamma, const vo
   // a shared-input stack A decides one gate for QKV and fc_in: the attention launch repeats it
   const bool shared = A->n_sites == 1;
   rc = launch_attention_gelu(A->dtype, ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part,
-                             shared ? gates : nullptr, shared ? rho : nullptr, s);
+                             shared ? gates : nullptr, shared ? rho : nullptr, pos_dev, cap, s);
   if (rc != GSI_OK) return rc;
   rc = stack_one_token(B, xb, eps, yb, gates + 2, rho ? rho + 2 : nullptr, ws, s);
   if (rc != GSI_OK) return rc;
@@ -636,10 +637,11 @@ int gsi_block_step(gsi_stack* A, gsi_stack* B, const void* gamma, const void* be
                        dff, (hipStream_t)stream);
 }
 
-int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
-                    const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int n_heads,
-                    float eps, void* x, void* xa, void* ya, void* xb, void* yb, uint8_t* gates, float* rho, void* ws,
-                    size_t ws_bytes, void* stream) {
+// the step at host position pos, or (pos_dev) at the device position *pos_dev, advanced afterwards
+static int decode_step_impl(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                            const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int* pos_dev,
+                            int cap, int n_heads, float eps, void* x, void* xa, void* ya, void* xb, void* yb,
+                            uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream) {
   if (n_blocks < 1) return GSI_ERR_SHAPE;
   if (!A || !B || !gamma || !beta || !k_cache || !v_cache) return GSI_ERR_NULL;
   int d0 = 0, dff0 = 0;
@@ -661,10 +663,29 @@ int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, cons
     const bool more = b + 1 < n_blocks;
     const int rc = block_enqueue(A[b], B[b], gamma[b], beta[b], x, k_cache[b], v_cache[b], pos, n_heads, eps, xa, ya,
                                  xb, yb, gates + 4 * b, rho ? rho + 4 * b : nullptr, ws, d0, dff0, s, b > 0,
-                                 more ? gamma[b + 1] : nullptr, more ? beta[b + 1] : nullptr);
+                                 more ? gamma[b + 1] : nullptr, more ? beta[b + 1] : nullptr, pos_dev, cap);
     if (rc != GSI_OK) return rc;
   }
-  return GSI_OK;
+  return pos_dev ? launch_pos_advance(pos_dev, s) : GSI_OK;
+}
+
+int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                    const void* const* beta, void* const* k_cache, void* const* v_cache, int pos, int n_heads,
+                    float eps, void* x, void* xa, void* ya, void* xb, void* yb, uint8_t* gates, float* rho, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return decode_step_impl(n_blocks, A, B, gamma, beta, k_cache, v_cache, pos, nullptr, 0, n_heads, eps, x, xa, ya, xb,
+                          yb, gates, rho, ws, ws_bytes, stream);
+}
+
+int gsi_decode_step_devpos(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                           const void* const* beta, void* const* k_cache, void* const* v_cache, int* pos,
+                           int cache_rows, int n_heads, float eps, void* x, void* xa, void* ya, void* xb, void* yb,
+                           uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream) {
+  if (!pos) return GSI_ERR_NULL;
+  if (cache_rows < 1 || cache_rows > (1 << 24) || ((uintptr_t)pos & 3)) return GSI_ERR_SHAPE;
+  // the block checks see position 0; the kernels bound the device position by cache_rows
+  return decode_step_impl(n_blocks, A, B, gamma, beta, k_cache, v_cache, 0, pos, cache_rows, n_heads, eps, x, xa, ya,
+                          xb, yb, gates, rho, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -174,13 +174,39 @@ __device__ __forceinline__ void wait_vmcnt() {  // this wave's vector memory ope
 // the head's last chunk to arrive (counter cnt[h], zero between launches) adds the chunks in chunk
 // order, o_h = sum_c e^(m_c - M) sums_c / sum_c e^(m_c - M) l_c, to xb[h dh ..]. Position pos reads
 // the new token's k and v from ya, and the chunk holding it writes them into row pos of the caches.
+// Position chunks of the attention over L positions with n_heads heads: at most
+// split_count_max(n_heads), chunks of at least 16 positions (the same rule on the host and in
+// the kernel).
+__host__ __device__ inline int split_count_max(int n_heads) {
+  const int want = (512 + n_heads - 1) / n_heads;
+  return want < 1 ? 1 : (want > kMaxAttnSplit ? kMaxAttnSplit : want);
+}
+__host__ __device__ inline int split_count(int L, int n_heads) {
+  const int want = split_count_max(n_heads);
+  const int lc0 = (L + want - 1) / want;
+  const int lc = lc0 < 16 ? 16 : lc0;
+  return (L + lc - 1) / lc;
+}
+
+// pos_dev (optional): the position is read from device memory instead (a step replayed from a
+// captured graph); the grid then holds gsplit = split_count_max(n_heads) chunk blocks per head,
+// those past the position's chunk count leave at once, and a position outside [0, cap) runs no
+// attention block (nothing is written to the caches).
 template <typename T, int EPL>
 __global__ __launch_bounds__(256) void attn_gelu_kernel(const T* __restrict__ ya, T* __restrict__ kc,
-                                                        T* __restrict__ vc, int pos, int d, int n_heads, int lc,
-                                                        int nsplit, float* __restrict__ part, int* __restrict__ cnt,
-                                                        int dff, T* __restrict__ xb, uint8_t* __restrict__ gate_dup,
-                                                        float* __restrict__ rho_dup) {
+                                                        T* __restrict__ vc, int pos_arg, int d, int n_heads,
+                                                        int lc_arg, int nsplit_arg, float* __restrict__ part,
+                                                        int* __restrict__ cnt, int dff, T* __restrict__ xb,
+                                                        uint8_t* __restrict__ gate_dup, float* __restrict__ rho_dup,
+                                                        const int* __restrict__ pos_dev, int cap, int gsplit) {
   constexpr int dh = 64 * EPL;
+  int pos = pos_arg, lc = lc_arg, nsplit = nsplit_arg;
+  if (pos_dev) {
+    pos = *pos_dev;
+    const int L = pos + 1;
+    nsplit = split_count(L > 0 ? L : 1, n_heads);
+    lc = (L + nsplit - 1) / nsplit;
+  }
   // a shared-input site's gate (and ratio), decided by the stack launch before this one, is
   // reported for both of its maps
   if (gate_dup && blockIdx.x == 0 && threadIdx.x == 0) {
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_gelu_kernel(const T* __restrict__ ya
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_acc[4][dh];
   __shared__ int s_last;
-  const int na = n_heads * nsplit;
+  const int na = n_heads * gsplit;
   if ((int)blockIdx.x >= na) {
     const int i = ((int)blockIdx.x - na) * 256 + threadIdx.x;
     if (i >= dff) return;
@@ -199,7 +225,8 @@ __global__ __launch_bounds__(256) void attn_gelu_kernel(const T* __restrict__ ya
     xb[d + i] = from_f32<T>(u);
     return;
   }
-  const int h = blockIdx.x / nsplit, c = blockIdx.x % nsplit;
+  const int h = blockIdx.x / gsplit, c = blockIdx.x % gsplit;
+  if (pos_dev && (pos < 0 || pos >= cap || c >= nsplit)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = h * dh + lane * EPL;
   const int j0 = c * lc, j1 = min(pos + 1, j0 + lc);
@@ -320,10 +347,15 @@ __global__ __launch_bounds__(256) void residual_kernel(T* __restrict__ x, const 
 
 }  // namespace
 
-int attn_splits(int L, int n_heads) {
-  const int want = std::max(1, std::min(kMaxAttnSplit, (512 + n_heads - 1) / n_heads));
-  const int lc = std::max(16, (L + want - 1) / want);
-  return (L + lc - 1) / lc;
+int attn_splits(int L, int n_heads) { return split_count(L, n_heads); }
+
+__global__ void pos_advance_kernel(int* pos) {
+  if (threadIdx.x == 0) *pos += 1;
+}
+
+int launch_pos_advance(int* pos, hipStream_t s) {
+  pos_advance_kernel<<<1, 64, 0, s>>>(pos);
+  return hipGetLastError() == hipSuccess ? GSI_OK : GSI_ERR_HIP;
 }
 
 // partial sums, then one arrival counter per head (zero between launches)
@@ -346,31 +378,34 @@ int launch_ln_dup(int dtype, const void* x, const void* gamma, const void* beta,
 
 template <typename T, int EPL>
 static void attention_launch(const void* ya, void* kc, void* vc, int pos, int d, int n_heads, int dff, void* xb,
-                             float* part, uint8_t* gate_dup, float* rho_dup, hipStream_t s) {
+                             float* part, uint8_t* gate_dup, float* rho_dup, const int* pos_dev, int cap,
+                             hipStream_t s) {
   const int L = pos + 1;
   const int nsplit = attn_splits(L, n_heads);
   const int lc = (L + nsplit - 1) / nsplit;
+  const int gsplit = pos_dev ? split_count_max(n_heads) : nsplit;
   int* cnt = (int*)((char*)part + align256((size_t)kMaxAttnSplit * (d + 2 * (size_t)n_heads) * 4));
-  const unsigned nb = (unsigned)(n_heads * nsplit + (dff + 255) / 256);
+  const unsigned nb = (unsigned)(n_heads * gsplit + (dff + 255) / 256);
   attn_gelu_kernel<T, EPL><<<nb, 256, 0, s>>>((const T*)ya, (T*)kc, (T*)vc, pos, d, n_heads, lc, nsplit, part, cnt,
-                                               dff, (T*)xb, gate_dup, rho_dup);
+                                               dff, (T*)xb, gate_dup, rho_dup, pos_dev, cap, gsplit);
 }
 
 int launch_attention_gelu(int dtype, const void* ya, void* k_cache, void* v_cache, int pos, int d, int n_heads,
-                          int dff, void* xb, float* part, uint8_t* gate_dup, float* rho_dup, hipStream_t s) {
+                          int dff, void* xb, float* part, uint8_t* gate_dup, float* rho_dup, const int* pos_dev,
+                          int cap, hipStream_t s) {
   if (n_heads < 1 || d % n_heads != 0 || pos < 0) return GSI_ERR_SHAPE;
   const int dh = d / n_heads;
   const bool bf = dtype == GSI_BF16;
   if (dtype != GSI_BF16 && dtype != GSI_F16) return GSI_ERR_DTYPE;
   if (dh == 64) {
-    if (bf) attention_launch<bf16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
-    else attention_launch<f16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    if (bf) attention_launch<bf16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
+    else attention_launch<f16_t, 1>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
   } else if (dh == 128) {
-    if (bf) attention_launch<bf16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
-    else attention_launch<f16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    if (bf) attention_launch<bf16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
+    else attention_launch<f16_t, 2>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
   } else if (dh == 256) {
-    if (bf) attention_launch<bf16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
-    else attention_launch<f16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, s);
+    if (bf) attention_launch<bf16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
+    else attention_launch<f16_t, 4>(ya, k_cache, v_cache, pos, d, n_heads, dff, xb, part, gate_dup, rho_dup, pos_dev, cap, s);
   } else {
     return GSI_ERR_SHAPE;
   }

@@ -284,6 +284,20 @@ int gsi_decode_step(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, cons
                     float eps, void* x, void* xa, void* ya, void* xb, void* yb, uint8_t* gates, float* rho, void* ws,
                     size_t ws_bytes, void* stream);
 
+/*
+ * gsi_decode_step with the cache position in device memory, so that one captured graph of the call
+ * replays token after token [GSI §3 item 4, §5: every linear map a GSI site, attention unchanged].
+ * `pos` is a device int32 (4-byte aligned), read by the step's kernels when they run; the call's
+ * last launch adds one to it. cache_rows (1 .. 2^24) is the number of rows of every k_cache and
+ * v_cache. A step whose *pos lies outside [0, cache_rows) runs no attention and writes no cache
+ * row (its outputs are then unspecified). Other arguments, checks and launches as gsi_decode_step
+ * (one more launch, the advance); the attention launch always has the grid of the longest cache.
+ */
+int gsi_decode_step_devpos(int n_blocks, gsi_stack* const* A, gsi_stack* const* B, const void* const* gamma,
+                           const void* const* beta, void* const* k_cache, void* const* v_cache, int* pos,
+                           int cache_rows, int n_heads, float eps, void* x, void* xa, void* ya, void* xb, void* yb,
+                           uint8_t* gates, float* rho, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,19 @@ def test_library_carries_no_phase_stamps():
     with pytest.raises(AttributeError):
         lib.gsi_phase_stamps
 
+
+def test_decode_step_devpos_rejects_before_device():
+    """The device-position step checks its pointer and cache length before anything is enqueued."""
+    p = vp(256)
+    arr = (vp * 1)(None)
+    f = ctypes.c_float(0.1)
+    args = lambda pos, rows: (1, arr, arr, arr, arr, arr, arr, pos, rows, 16, f, p, p, p, p, p, p, None, p, 1 << 20, None)
+    assert lib.gsi_decode_step_devpos(*args(None, 8)) == -1            # no position
+    assert lib.gsi_decode_step_devpos(*args(vp(256), 0)) == -2         # empty cache
+    assert lib.gsi_decode_step_devpos(*args(vp(256), (1 << 24) + 1)) == -2
+    assert lib.gsi_decode_step_devpos(*args(vp(258), 8)) == -2         # misaligned int
+    assert lib.gsi_decode_step_devpos(*args(vp(256), 8)) == -1         # null stacks
+
 def test_status_strings():
     for code in range(0, -10, -1):
         s = lib.gsi_status_string(code)

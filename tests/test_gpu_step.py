@@ -295,3 +295,52 @@ def test_decode_step_equals_block_calls(g):
     assert g.gsi_workspace_status(m2.ws) == 0
     m1.destroy()
     m2.destroy()
+
+
+def test_decode_step_graph_replays_equal_eager(g):
+    """One gsi_decode_step_devpos call captured in a HIP graph and replayed token after token (the
+    position advanced on the device) gives, bit for bit, the rows, gates and cache rows of eager
+    gsi_decode_step calls at the same positions; the first token runs the device-position call
+    eagerly. Eager work and a synchronisation separate the replays."""
+    cfg = step_config(71)
+    say(f"case: {cfg.name}, captured step replayed against eager steps")
+    m1, m2 = Model(g, cfg), Model(g, cfg)
+    nb, n = cfg.n_blocks, cfg.n_tokens
+    b1, b2 = m1.blocks, m2.blocks
+    lists = lambda bl: ([k["A"] for k in bl], [k["B"] for k in bl], [k["gamma"] for k in bl],
+                        [k["beta"] for k in bl], [k["K"] for k in bl], [k["V"] for k in bl])
+    pos_dev = torch.tensor([cfg.L0], dtype=torch.int32, device="cuda")
+    xg = torch.zeros_like(m2.host["x0"][0], device="cuda")
+    gates_g = torch.zeros(nb * 4, dtype=torch.uint8, device="cuda")
+    rho_g = torch.zeros(nb * 4, dtype=torch.float32, device="cuda")
+    gates_e = torch.zeros(nb * 4, dtype=torch.uint8, device="cuda")
+    rho_e = torch.zeros(nb * 4, dtype=torch.float32, device="cuda")
+    step2 = lambda: g.gsi_decode_step_devpos(*lists(b2), pos_dev, cfg.n_heads, cfg.eps, xg, m2.xa, m2.ya, m2.xb,
+                                             m2.yb, gates_g, rho_g, m2.ws)
+    graph = None
+    for t in range(n):
+        pos = cfg.L0 + t
+        x1 = m1.host["x0"][t].cuda().clone()
+        g.gsi_decode_step(*lists(b1), pos, cfg.n_heads, cfg.eps, x1, m1.xa, m1.ya, m1.xb, m1.yb, gates_e, rho_e,
+                          m1.ws)
+        xg.copy_(m2.host["x0"][t].cuda())
+        if t == 0:
+            step2()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step2()
+        else:
+            graph.replay()
+        torch.cuda.synchronize()
+        assert int(pos_dev.item()) == pos + 1, f"token {t}: position not advanced"
+        assert torch.equal(x1, xg), f"token {t}: rows differ"
+        assert torch.equal(gates_e, gates_g), f"token {t}: gates differ"
+        assert torch.equal(rho_e, rho_g), f"token {t}: ratios differ"
+        for b in range(nb):
+            assert torch.equal(b1[b]["K"][pos], b2[b]["K"][pos]), f"token {t} block {b}: key row"
+            assert torch.equal(b1[b]["V"][pos], b2[b]["V"][pos]), f"token {t} block {b}: value row"
+    assert g.gsi_workspace_status(m2.ws) == 0
+    del graph
+    m1.destroy()
+    m2.destroy()
