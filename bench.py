@@ -141,7 +141,7 @@ def extra_workloads(args, g, torch, np) -> dict:
     a7.steps, a7.warmup, a7.no_cpu_baseline = 48, 8, True
     o7 = decode_step(a7, g, torch, np)
     res["gptj_decode_step"] = {k: o7[k] for k in ("value", "unit", "ms_per_step", "roofline", "fast_fraction",
-                                                   "dense_step", "speedup_vs_dense", "two_site_stack_a")}
+                                                   "dense_step", "speedup_vs_dense", "two_site_stack_a", "graph")}
     res["gptj_decode_step"]["workload"] = o7["config"]["workload"]
     gc.collect()
     torch.cuda.empty_cache()
